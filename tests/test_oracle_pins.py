@@ -1,0 +1,346 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each pin is an independent computation (pure-Python brute force, a closed
+form, an invariant or a hand-worked fixture under tests/golden/), chosen so
+that a plausible mistake in the oracle (a dropped scale, a wrong GQA map, a
+causal offset off by one, a sum in place of a mean, a transposed operand, a
+wrong tie rule, a wrong ring index) fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from kv_cache_compression_window_amd import synth
+from oracle import kvc_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------
+# brute-force helpers (pure Python, independent of the oracle)
+# ----------------------------------------------------------------------------
+
+def brute_full_causal_attention(Q, K):
+    """Full causal attention of every query position: A[b][h][p][j] (nested lists).
+
+    Q: [B,H,S,D], K: [B,Hkv,S,D]; query head h reads KV head h // (H/Hkv);
+    logits scaled by 1/sqrt(D); position p attends keys 0..p."""
+    B, H, S, D = Q.shape
+    Hkv = K.shape[1]
+    G = H // Hkv
+    A = [[[[0.0] * S for _ in range(S)] for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            for p in range(S):
+                logits = []
+                for j in range(p + 1):
+                    dot = 0.0
+                    for d in range(D):
+                        dot += float(Q[b, h, p, d]) * float(K[b, g, j, d])
+                    logits.append(dot / math.sqrt(D))
+                m = max(logits)
+                ex = [math.exp(x - m) for x in logits]
+                z = sum(ex)
+                for j in range(p + 1):
+                    A[b][h][p][j] = ex[j] / z
+    return A
+
+
+def brute_topk(scores, k, n_tail):
+    """Best subset by exhaustive search: the kept set T of size k - n_tail
+    among the first N - n_tail positions such that every kept position beats
+    every dropped one (larger score, or equal score and lower index)."""
+    N = len(scores)
+    E = N - n_tail
+    found = []
+    for T in itertools.combinations(range(E), k - n_tail):
+        Ts = set(T)
+        ok = all((scores[a] > scores[c]) or (scores[a] == scores[c] and a < c)
+                 for a in Ts for c in range(E) if c not in Ts)
+        if ok:
+            found.append(sorted(T) + list(range(E, N)))
+    assert len(found) == 1, "the tie rule must make the kept set unique"
+    return found[0]
+
+
+# ----------------------------------------------------------------------------
+# O1-O3 window scores
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,H,Hkv,S,D,w", [(1, 4, 2, 9, 3, 3), (2, 2, 1, 7, 4, 2), (1, 4, 4, 6, 2, 4),
+                                           (1, 2, 2, 5, 3, 1)])
+def test_window_scores_equal_slice_of_full_causal_attention(B, H, Hkv, S, D, w):
+    """P2: window rows are rows S-w..S-1 of the full causal attention; GROUP
+    scores are their mean over the group's heads and the window."""
+    rs = np.random.default_rng(1000 + S * 10 + w)
+    Q = rs.standard_normal((B, H, S, D)) * 1.5
+    K = rs.standard_normal((B, Hkv, S, D))
+    A = brute_full_causal_attention(Q, K)
+    G = H // Hkv
+    got = O.window_scores(Q[:, :, S - w:, :], K, reduce=O.REDUCE_GROUP, causal=True)
+    for b in range(B):
+        for g in range(Hkv):
+            for j in range(S):
+                ref = sum(A[b][h][p][j] for h in range(g * G, (g + 1) * G) for p in range(S - w, S)) / (G * w)
+                assert abs(got[b, g, j] - ref) <= 1e-13, (b, g, j)
+
+
+def test_tova_is_head_mean_of_last_row_repeated():
+    """P3: TOVA = mean over all heads of the last attention row, repeated for
+    each KV head (Add TOVA press: attn_weights.mean(1) then repeat)."""
+    B, H, Hkv, S, D = 2, 4, 2, 8, 3
+    rs = np.random.default_rng(7)
+    Q = rs.standard_normal((B, H, S, D))
+    K = rs.standard_normal((B, Hkv, S, D))
+    A = brute_full_causal_attention(Q, K)
+    got = O.window_scores(Q[:, :, -1:, :], K, reduce=O.REDUCE_ALL_HEADS, causal=False)
+    for b in range(B):
+        ref = [sum(A[b][h][S - 1][j] for h in range(H)) / H for j in range(S)]
+        for g in range(Hkv):
+            assert np.allclose(got[b, g], ref, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("reduce", [O.REDUCE_GROUP, O.REDUCE_ALL_HEADS])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_score_rows_sum_to_one(reduce, causal):
+    """P1: every softmax row sums to 1, so every score row sums to 1
+    (with holes, channel pruning and causal masking)."""
+    p = synth.random_problem(11, 2, 8, 2, 37, 16, 5, dtype="bf16", heavy_frac=0.1)
+    valid = synth.random_valid(3, 2, 2, 37, 0.3)
+    valid[:, :, -5:] = 1
+    ch = np.stack([np.stack([np.sort(np.random.default_rng(b * 2 + g).choice(16, 8, replace=False))
+                             for g in range(2)]) for b in range(2)])
+    for v, c in [(None, None), (valid, None), (None, ch), (valid, ch)]:
+        s = O.window_scores(p.q64(), p.k64(), valid=v, chan_keep=c, reduce=reduce, causal=causal)
+        assert np.allclose(s.sum(axis=-1), 1.0, rtol=0, atol=1e-12)
+        if v is not None:
+            if reduce == O.REDUCE_GROUP:
+                assert np.all(s[v == 0] == 0.0)
+            else:  # a hole gets mass only from other KV heads' valid slots
+                hole_everywhere = (v == 0).all(axis=1)
+                assert np.all(s[:, 0, :][hole_everywhere] == 0.0)
+                assert np.all(s == s[:, :1, :])
+
+
+def test_zero_query_and_equal_keys_are_uniform():
+    """P4: q = 0 or all keys equal gives P = 1/(allowed count)."""
+    p = synth.random_problem(12, 1, 4, 2, 20, 8, 1, dtype="f32")
+    q0 = np.zeros_like(p.q64())
+    s = O.window_scores(q0, p.k64(), reduce=O.REDUCE_GROUP, causal=False)
+    assert np.allclose(s, 1.0 / 20, rtol=0, atol=1e-15)
+    k_eq = np.repeat(p.k64()[:, :, :1, :], 20, axis=2)
+    valid = synth.random_valid(4, 1, 2, 20, 0.25)
+    s = O.window_scores(p.q64(), k_eq, valid=valid, reduce=O.REDUCE_GROUP, causal=False)
+    for g in range(2):
+        n = valid[0, g].sum()
+        assert np.allclose(s[0, g][valid[0, g] == 1], 1.0 / n, rtol=0, atol=1e-15)
+    # uniform scores: the kept set is the lowest k indices (closed form of the tie rule)
+    idx = O.topk_select(s[0, :1, :] * 0 + 0.05, 7)
+    assert idx.tolist() == [list(range(7))]
+
+
+def test_group_of_one_is_per_head_row():
+    """P4: with G = 1 and w = 1 the GROUP score of KV head g is head g's row."""
+    B, H, S, D = 1, 3, 6, 4
+    rs = np.random.default_rng(9)
+    Q = rs.standard_normal((B, H, S, D))
+    K = rs.standard_normal((B, H, S, D))
+    A = brute_full_causal_attention(Q, K)
+    got = O.window_scores(Q[:, :, -1:, :], K, reduce=O.REDUCE_GROUP, causal=False)
+    for h in range(H):
+        assert np.allclose(got[0, h], A[0][h][S - 1], rtol=0, atol=1e-14)
+
+
+def test_golden_window_scores():
+    for c in _golden("window_scores_closed_form.json")["cases"]:
+        q = np.array(c["q"], dtype=np.float64) * c["q_scale"]
+        k = np.array(c["k"], dtype=np.float64)
+        red = O.REDUCE_GROUP if c["reduce"] == "group" else O.REDUCE_ALL_HEADS
+        s = O.window_scores(q, k, reduce=red, causal=c["causal"])
+        assert np.allclose(s, np.array(c["scores"]), rtol=0, atol=1e-12), c["name"]
+
+
+def test_channel_pruned_logits_equal_zeroed_keys():
+    """Zeroing the pruned key channels gives the same scores as masking them
+    out of the dot product (Add ThinK_Press: option 3a, zero in the key cache)."""
+    p = synth.random_problem(13, 1, 4, 2, 30, 8, 3, dtype="f32")
+    ch = np.array([[[0, 2, 5, 7], [1, 2, 3, 6]]])
+    kz = p.k64().copy()
+    for g in range(2):
+        drop = [d for d in range(8) if d not in ch[0, g]]
+        kz[0, g][:, drop] = 0.0
+    a = O.window_scores(p.q64(), p.k64(), chan_keep=ch)
+    b = O.window_scores(p.q64(), kz)
+    assert np.allclose(a, b, rtol=1e-14, atol=0)
+
+
+# ----------------------------------------------------------------------------
+# O4 top-k
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(40))
+def test_topk_matches_exhaustive_subset_search(seed):
+    """P10: the oracle's selection is the unique subset with the stated
+    ordering property (brute force over all subsets, n <= 9, many ties)."""
+    rs = np.random.default_rng(seed)
+    n = int(rs.integers(1, 10))
+    n_tail = int(rs.integers(0, n + 1))
+    k = int(rs.integers(n_tail, n + 1))
+    levels = int(rs.integers(1, 5))
+    scores = rs.integers(0, levels, size=n).astype(np.float64) / levels
+    if seed % 5 == 0:
+        scores[rs.integers(0, n)] = -np.inf
+    got = O.topk_select(scores[None, :], k, n_tail)[0].tolist()
+    assert got == brute_topk(list(scores), k, n_tail)
+
+
+def test_golden_topk():
+    for c in _golden("topk_ties.json")["cases"]:
+        got = O.topk_select(np.array(c["scores"]), c["k"], c["n_tail"])
+        assert got.tolist() == c["idx"], c["why"]
+
+
+def test_snapkv_keeps_window():
+    """P5: SnapKV keeps every window position; |kept| = k; ascending."""
+    p = synth.snapkv(0, S=300, w=16, H=8, Hkv=2, D=16)
+    s, idx = O.snapkv(p.q64(), p.k64(), keep=40)
+    assert idx.shape == (1, 2, 40)
+    for g in range(2):
+        assert set(range(300 - 16, 300)) <= set(idx[0, g].tolist())
+        assert np.all(np.diff(idx[0, g]) > 0)
+
+
+# ----------------------------------------------------------------------------
+# O6 ThinK
+# ----------------------------------------------------------------------------
+
+def test_think_factorised_equals_materialised_channel_attn():
+    """P9: sum_{i,j} (q_i,d * k_j,d)^2 (the materialised channel_attn of
+    Add ThinK_Press, brute force) equals the factorised oracle."""
+    B, H, Hkv, w, S, D = 2, 4, 2, 3, 5, 6
+    rs = np.random.default_rng(21)
+    q = rs.standard_normal((B, H, w, D))
+    k = rs.standard_normal((B, Hkv, S, D))
+    G = H // Hkv
+    ref = np.zeros((B, Hkv, D))
+    for b in range(B):
+        for h in range(H):
+            for d in range(D):
+                acc = 0.0
+                for i in range(w):
+                    for j in range(S):
+                        acc += (q[b, h, i, d] * k[b, h // G, j, d]) ** 2
+                ref[b, h // G, d] += acc
+    got = O.channel_scores(q, k)
+    assert np.allclose(got, ref, rtol=1e-12, atol=0)
+
+
+def test_golden_think():
+    c = _golden("think_channel_closed_form.json")
+    q = np.array(c["q"], dtype=np.float64)
+    k = np.array(c["k"], dtype=np.float64)
+    cs = O.channel_scores(q, k)
+    assert np.allclose(cs, np.array(c["channel_scores"]), rtol=0, atol=1e-12)
+    assert O.select_channels(cs, c["d_keep"]).tolist() == c["kept_channels"]
+
+
+# ----------------------------------------------------------------------------
+# O8 gather
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gather_matches_row_copy_loops(dtype):
+    """P11: gather is a bit copy of the kept rows, pruned key channels +0."""
+    p = synth.random_problem(31, 2, 4, 2, 17, 8, 1, dtype=dtype)
+    rs = np.random.default_rng(3)
+    idx = np.stack([np.stack([np.sort(rs.choice(17, 6, replace=False)) for _ in range(2)]) for _ in range(2)])
+    ch = np.stack([np.stack([np.sort(rs.choice(8, 3, replace=False)) for _ in range(2)]) for _ in range(2)])
+    ko, vo = O.gather_compact(p.k, p.v, idx, chan_keep=ch)
+    for b in range(2):
+        for g in range(2):
+            for r in range(6):
+                for d in range(8):
+                    want_k = p.k[b, g, idx[b, g, r], d] if d in ch[b, g] else 0
+                    assert ko[b, g, r, d].tobytes() == np.array(want_k, dtype=p.k.dtype).tobytes()
+                    assert vo[b, g, r, d].tobytes() == p.v[b, g, idx[b, g, r], d].tobytes()
+
+
+# ----------------------------------------------------------------------------
+# O5 Scissorhands
+# ----------------------------------------------------------------------------
+
+def test_golden_scissorhands_steps():
+    c = _golden("scissorhands_steps.json")
+    cache = O.ScissorhandsCache(1, 1, 4, c["history"])
+    for t, attn in enumerate(c["attn"]):
+        low = cache.update_attn_history(np.array(attn, dtype=np.float64)[None, None, :])
+        assert low[0, 0].astype(int).tolist() == c["low"][t]
+        assert cache.low_counts()[0, 0].tolist() == c["counts"][t]
+        ev = cache.evict(c["n_evict"]) if (t + 1) % c["evict_every"] == 0 else None
+        assert (None if ev is None else ev[0, 0].tolist()) == c["evicted"][t]
+        assert cache.valid[0, 0].astype(int).tolist() == c["valid_after"][t]
+
+
+@pytest.mark.parametrize("hist", [1, 3, 7])
+def test_scissorhands_ring_equals_windowed_sum(hist):
+    """P6/P7: the circular history count equals the sum of the full
+    [steps x slots] low matrix over the last min(t+1, hist) steps, and stays
+    within [0, min(t+1, hist)]."""
+    B, Hkv, C, steps = 2, 2, 11, 25
+    rs = np.random.default_rng(hist)
+    cache = O.ScissorhandsCache(B, Hkv, C, hist)
+    lows = []
+    for t in range(steps):
+        attn = rs.dirichlet(np.ones(C) * 0.7, size=(B, Hkv))
+        attn = np.where(cache.valid, attn, 0.0)
+        lows.append(cache.update_attn_history(attn).astype(np.int64))
+        # brute force: recompute the low test from its definition
+        for b in range(B):
+            for g in range(Hkv):
+                n = int(cache.valid[b, g].sum())
+                for c in range(C):
+                    want = bool(cache.valid[b, g, c]) and attn[b, g, c] < 1.0 / n
+                    assert bool(lows[-1][b, g, c]) == want
+        window = np.stack(lows[max(0, t + 1 - hist):t + 1]).sum(axis=0)
+        counts = cache.low_counts()
+        assert np.array_equal(counts, window)
+        assert counts.min() >= 0 and counts.max() <= min(t + 1, hist)
+        if t % 6 == 5:
+            cache.evict(1)
+
+
+def test_scissorhands_equal_keys_never_low_and_dominant_key():
+    """P8: all keys equal -> every probability is exactly 1/S_t, never low;
+    one dominant key -> every other valid slot is low at every step, so its
+    count is min(t+1, history), and eviction takes the lowest indices."""
+    B, H, Hkv, C, D, hist = 1, 2, 1, 70, 4, 5
+    k_eq = np.ones((B, Hkv, C, D))
+    cache = O.ScissorhandsCache(B, Hkv, C, hist)
+    rs = np.random.default_rng(5)
+    for t in range(8):
+        q = rs.standard_normal((B, H, 1, D))
+        _, low, _ = O.scissorhands_step(cache, q, k_eq, t, evict_every=100, n_evict=3)
+        assert not low.any()
+    k_dom = np.zeros((B, Hkv, C, D))
+    k_dom[0, 0, 65] = [40.0, 0, 0, 0]
+    q = np.zeros((B, H, 1, D))
+    q[..., 0] = 1.0
+    cache = O.ScissorhandsCache(B, Hkv, C, hist)
+    for t in range(8):
+        _, low, ev = O.scissorhands_step(cache, q, k_dom, t, evict_every=4, n_evict=3)
+        assert not low[0, 0, 65]
+        counts = cache.low_counts()[0, 0]
+        v = cache.valid[0, 0]
+        if ev is not None:
+            assert ev[0, 0].tolist() == [3 * (t // 4), 3 * (t // 4) + 1, 3 * (t // 4) + 2]
+        assert np.all(counts[v & (np.arange(C) != 65)] == min(t + 1, hist))
