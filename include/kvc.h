@@ -1,0 +1,211 @@
+/*
+ * kvc.h — KV-cache scoring and pruning for one transformer layer on MI355X (gfx950).
+ *
+ * The library scores a layer's KV cache from attention statistics of an
+ * observation window of queries and prunes it.  It covers TOVA, SnapKV,
+ * Scissorhands and ThinK.  Each of them feeds a per-KV-head top-k and the
+ * compaction of K/V into the smaller cache.  Sources (web pages):
+ *   [TOVA]  "Add TOVA press", NVIDIA kvpress pull request 12 (review thread).
+ *   [COLD]  "Implement Scissorhands KV-cache compression & SnapKV prompt
+ *           compression", AnswerDotAI cold-compress pull request 11
+ *           (cache.py review hunks and the PR description).
+ *   [THINK] "Add ThinK_Press", NVIDIA kvpress pull request 18 (review thread).
+ *
+ * Conventions for every call:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or keeps a pointer after the call returns.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the default stream).
+ *     There is no host synchronisation inside the library.  A fault on the device
+ *     surfaces at the caller's next synchronisation.
+ *   - Arguments are validated before anything is enqueued.  On any error nothing
+ *     is enqueued and an error status is returned.  KVC_ERR_HIP reports a
+ *     failed launch (hipGetLastError after the launch).
+ *   - Tensors are dense, row-major and contiguous in the listed shape.  q, k, v
+ *     and the compacted outputs must be 16-byte aligned.
+ *   - dtype KVC_BF16 means bfloat16 storage and KVC_F32 float32 storage.
+ *     Arithmetic is float32: bf16 x bf16 products are exact in fp32 and are
+ *     accumulated in fp32.  Scores are float32; indices are int32.
+ *   - head_dim D must be 64 or 128 (KVC_ERR_UNSUPPORTED otherwise).
+ *   - Query head h reads KV head h / (H / Hkv) (the repeat_interleave order of
+ *     [COLD]'s GQA hunk).  Window row i (0 <= i < w) is query position S-w+i.
+ *   - Calls that take a workspace `ws` use it like this.  With ws == NULL,
+ *     the call writes the required byte count to *ws_bytes, returns KVC_OK and
+ *     enqueues nothing.  Otherwise *ws_bytes is the size of ws, and
+ *     KVC_ERR_WORKSPACE is returned if it is too small.  Workspace contents
+ *     need no initialisation and are scratch after the call.
+ *   - Calls are reentrant and the library has no global mutable state.  Two
+ *     calls that share a workspace or an output must be ordered by the caller,
+ *     for example by using one stream.
+ *   - NaN inputs give unspecified (but in-bounds) results.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  KVC_ERR_SHAPE = 2,       /* sizes out of range or inconsistent              */
+  KVC_ERR_DTYPE = 3,       /* unknown dtype / reduce mode                      */
+  KVC_ERR_ALIGN = 4,       /* q, k, v or a compacted output not 16-B aligned  */
+  KVC_ERR_WORKSPACE = 5,   /* *ws_bytes smaller than the required workspace   */
+  KVC_ERR_UNSUPPORTED = 6, /* a valid but unsupported size (e.g. D not 64/128) */
+  KVC_ERR_HIP = 7          /* a kernel launch failed                           */
+} kvc_status;
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+typedef enum {
+  /* Mean over the G query heads of each GQA group and the w window rows:
+   * SnapKV's window scoring and Scissorhands' attention callback ([COLD]:
+   * "Mean pool over the grouped queries"). */
+  KVC_REDUCE_GROUP = 0,
+  /* Mean over all H query heads and the w window rows, the same row written
+   * for every KV head ([TOVA]: attn_weights.mean(1) followed by a repeat
+   * over num_key_value_heads). */
+  KVC_REDUCE_ALL_HEADS = 1
+} kvc_reduce;
+
+typedef struct {
+  int32_t B;   /* batch                                    */
+  int32_t H;   /* query heads (multiple of Hkv)            */
+  int32_t Hkv; /* KV heads                                 */
+  int32_t S;   /* cache positions (keys)                   */
+  int32_t D;   /* head_dim: 64 or 128                      */
+  int32_t w;   /* observation-window rows, 1 <= w <= S     */
+} kvc_shape;
+
+/*
+ * kvc_window_scores — observation-window attention scores per KV head.
+ *
+ * Defines ([TOVA] SimJeg's reply: only the last window_size rows of the
+ * attention, shape [batch, heads, window_size, seq_len], are computed):
+ *   l[b,h,i,j] = sum_{d in keep(b,g)} q[b,h,i,d] * k[b,g,j,d] / sqrt(D),   g = h / (H/Hkv)
+ *   allowed(b,g,i,j) = valid[b,g,j] != 0  and  (!causal or j <= S-w+i)
+ *   P[b,h,i,j] = exp(l - logsumexp over allowed j of l) on allowed entries, else 0
+ *   GROUP:     scores[b,g,j] = 1/(G*w) * sum_{h in group g} sum_i P[b,h,i,j]
+ *   ALL_HEADS: scores[b,g,j] = 1/(H*w) * sum_h sum_i P[b,h,i,j]   (same for every g)
+ * A row with no allowed key contributes P = 0.
+ *
+ * Arguments:
+ *   sh        shape (B, H, Hkv, S, D, w).  Needs H % Hkv == 0 and G*w <= 1024.
+ *   dt        storage type of q_win and k.
+ *   q_win     [B, H, w, D] window queries (already position-encoded by the caller).
+ *   k         [B, Hkv, S, D] cache keys.
+ *   valid     [B, Hkv, S] uint8 (0 = hole, excluded) or NULL (all valid).
+ *   chan_idx  [B, Hkv, d_keep] int32 kept key channels, or NULL (all D channels).
+ *             Entries must be distinct and in [0, D).  Pruned channels count as zero
+ *             keys ([THINK] option 3a: zeros in the key cache).
+ *   d_keep    number of kept channels (ignored when chan_idx is NULL), 1..D.
+ *   reduce    KVC_REDUCE_GROUP or KVC_REDUCE_ALL_HEADS.
+ *   causal    nonzero: window row i attends keys j <= S-w+i (no effect when w == 1).
+ *   scores    out [B, Hkv, S] float32.
+ *   ws, ws_bytes  workspace (see the conventions above).
+ */
+kvc_status kvc_window_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
+                             const uint8_t* valid, const int32_t* chan_idx, int32_t d_keep,
+                             kvc_reduce reduce, int32_t causal, float* scores, void* ws,
+                             size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * kvc_scissor_update — Scissorhands low-attention history (record and evict).
+ *
+ * [COLD] cache.py hunks: a slot has low attention when its probability is below
+ * uniform attention 1/keys.  The indicator goes into the circular history slot
+ * (counter % history_window_size), which overwrites the oldest entry.  [COLD] PR
+ * description: every m steps, per head, evict the tokens with the highest
+ * fraction of unimportant attentions.  Bulk eviction leaves empty slots.
+ *
+ * State (caller-owned device buffers, which persist across steps):
+ *   valid  [B, Hkv, C] uint8, 1 = occupied slot, 0 = hole.
+ *   hist   [hist_len][B*Hkv][ceil(C/32)] uint32 bit-planes.  Bit (c % 32) of word
+ *          c/32 in plane p holds the indicator recorded at the last step t with
+ *          t % hist_len == p.  Zero it before step 0.
+ *   counts [B, Hkv, C] uint16, the number of set bits of slot c over the planes.
+ *          Zero it before step 0.
+ *
+ * When probs != NULL (record step `step`, counted from 0):
+ *   S_t = number of valid slots of (b, g);
+ *   low = valid[c] and probs[c] < 1/S_t (compared exactly: probs is widened to double);
+ *   plane = step % hist_len: counts += low - old bit;  bit <- low.
+ *   If frac_out != NULL, it then writes
+ *   frac_out[b,g,c] = counts / min(step+1, hist_len) at valid slots and -inf at holes.
+ * When evict_idx != NULL (after the record, if both are given):
+ *   valid[b, g, evict_idx[b,g,e]] = 0 for e < n_evict.  The indices must be in
+ *   [0, C) (e.g. kvc_topk_select over frac_out with k = n_evict).
+ *
+ *   probs     [B, Hkv, C] float32 group-mean probabilities of this step (the
+ *             kvc_window_scores output with w = 1, KVC_REDUCE_GROUP and valid), or NULL.
+ *   hist_len  1..65535 (400 in [COLD]).  step >= 0.
+ */
+kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_len, int64_t step,
+                              const float* probs, uint8_t* valid, uint32_t* hist, uint16_t* counts,
+                              float* frac_out, const int32_t* evict_idx, int32_t n_evict,
+                              hipStream_t stream);
+
+/*
+ * kvc_channel_scores — ThinK per-channel key importance.
+ *
+ * [THINK] yuhuixu1993's factorised score (equal to the squared, summed
+ * channel_attn of shape (bsz, num_heads, head_dim, window_size, seq_len)):
+ *   chan_scores[b,g,d] = ( sum_{h in group g} sum_{i<w} q[b,h,i,d]^2 ) * ( sum_{j<S} k[b,g,j,d]^2 )
+ * Sums run over positions: window rows for q and all S keys for k.  Pruning zeroes
+ * the channels with the smallest scores (kvc_topk_select over rows (b,g) with
+ * n = D, then chan_idx for kvc_window_scores / kvc_gather_compact).
+ *   chan_scores  out [B, Hkv, D] float32.  Sums are deterministic (fixed order).
+ */
+kvc_status kvc_channel_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
+                              float* chan_scores, void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * kvc_topk_select — per-row top-k with a forced tail, in ascending index order.
+ *
+ * Row r of `scores` has n entries.  Its last n_tail positions are always kept
+ * ([COLD] PR description: SnapKV keeps every observation-window token and
+ * compresses the prefix).  The first n - n_tail positions compete for
+ * k - n_tail slots.  A larger score wins; among equal scores the lower index
+ * wins (-0.0 counts as +0.0).  idx[r, :] lists the kept positions in
+ * ascending order, so the tail comes last.  The kept set is unique.  The same
+ * call picks Scissorhands evictions (largest low-attention fraction) and
+ * ThinK channels.
+ *   scores [rows, n] float32;  idx out [rows, k] int32;  0 <= n_tail <= k <= n.
+ */
+kvc_status kvc_topk_select(const float* scores, int32_t rows, int32_t n, int32_t k, int32_t n_tail,
+                           int32_t* idx, void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * kvc_gather_compact — compacted cache from the kept positions.
+ *
+ *   k_out[b,g,r,:] = k[b,g,idx[b,g,r],:], with the channels not listed in
+ *                    chan_idx[b,g,:] written as +0.0 ([THINK] option 3a: zeros
+ *                    in the key cache);
+ *   v_out[b,g,r,:] = v[b,g,idx[b,g,r],:].
+ * This is a bit copy (kept channels are bit-identical).
+ *   k, v        [B, Hkv, S, D] (sh->w is ignored); v may be NULL (then v_out is unused).
+ *   idx         [B, Hkv, n_keep] int32 in [0, S).
+ *   chan_idx    [B, Hkv, d_keep] int32 or NULL (keep every channel).
+ *   k_out, v_out  [B, Hkv, n_keep, D] (must not overlap k or v).
+ */
+kvc_status kvc_gather_compact(const kvc_shape* sh, kvc_dtype dt, const void* k, const void* v,
+                              const int32_t* idx, int32_t n_keep, const int32_t* chan_idx,
+                              int32_t d_keep, void* k_out, void* v_out, hipStream_t stream);
+
+/* Text for a status code (static storage). */
+const char* kvc_status_string(kvc_status s);
+
+/* KVC_ABI_VERSION of the built library. */
+int32_t kvc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H */

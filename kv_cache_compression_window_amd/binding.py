@@ -1,0 +1,214 @@
+"""Thin Python binding of libkvc (ctypes).  Argument marshalling only.
+
+Every function has the name of the C entry point it calls and takes torch
+tensors that already live on the GPU.  torch supplies device memory (outputs and
+workspaces allocated here when the caller passes none) and the stream (the
+current torch stream unless one is given).  No computation happens in Python,
+and there is no fallback: when ``libkvc.so`` is missing, importing this module
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvc.so")
+
+KVC_F32, KVC_BF16 = 0, 1
+KVC_REDUCE_GROUP, KVC_REDUCE_ALL_HEADS = 0, 1
+
+STATUS_NAMES = {0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_ALIGN",
+                5: "KVC_ERR_WORKSPACE", 6: "KVC_ERR_UNSUPPORTED", 7: "KVC_ERR_HIP"}
+
+# every symbol include/kvc.h declares
+EXPORTS = ["kvc_window_scores", "kvc_scissor_update", "kvc_channel_scores", "kvc_topk_select",
+           "kvc_gather_compact", "kvc_status_string", "kvc_abi_version"]
+
+
+class KvcShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("w", ctypes.c_int32)]
+
+
+class KvcError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)} ({text})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m kv_cache_compression_window_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, SZP = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)
+    SH = ctypes.POINTER(KvcShape)
+    sig = {
+        "kvc_window_scores": [SH, I32, P, P, P, P, I32, I32, I32, P, P, SZP, P],
+        "kvc_scissor_update": [I32, I32, I32, I32, I64, P, P, P, P, P, P, I32, P],
+        "kvc_channel_scores": [SH, I32, P, P, P, P, SZP, P],
+        "kvc_topk_select": [P, I32, I32, I32, I32, P, P, SZP, P],
+        "kvc_gather_compact": [SH, I32, P, P, P, I32, P, I32, P, P, P],
+        "kvc_status_string": [I32],
+        "kvc_abi_version": [],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_char_p if name == "kvc_status_string" else ctypes.c_int32
+    return lib
+
+
+LIB = _load()
+
+
+def abi_version() -> int:
+    return LIB.kvc_abi_version()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise KvcError(fn, status, LIB.kvc_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KVC_BF16
+    if t.dtype == torch.float32:
+        return KVC_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dim: int):
+    if t.dim() != dim or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {dim}-d CUDA tensor, got {tuple(t.shape)}")
+
+
+def _shape(q: torch.Tensor, k: torch.Tensor) -> KvcShape:
+    B, H, w, D = q.shape
+    _, Hkv, S, _ = k.shape
+    return KvcShape(B, H, Hkv, S, D, w)
+
+
+def _workspace(nbytes: int, device, ws):
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def window_scores_ws_bytes(B, H, Hkv, S, D, w) -> int:
+    sh = KvcShape(B, H, Hkv, S, D, w)
+    n = ctypes.c_size_t(0)
+    _check("kvc_window_scores", LIB.kvc_window_scores(ctypes.byref(sh), KVC_BF16, None, None, None, None, 0, 0, 0,
+                                                      None, None, ctypes.byref(n), None))
+    return n.value
+
+
+def kvc_window_scores(q, k, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, causal=True, scores=None, ws=None,
+                      stream=None):
+    """scores [B,Hkv,S] float32 of the window rows q [B,H,w,D] against k [B,Hkv,S,D]."""
+    _need(q, "q_win", 4)
+    _need(k, "k", 4)
+    sh = _shape(q, k)
+    if valid is not None:
+        _need(valid, "valid", 3)
+        assert valid.dtype == torch.uint8
+    d_keep = 0
+    if chan_idx is not None:
+        _need(chan_idx, "chan_idx", 3)
+        assert chan_idx.dtype == torch.int32
+        d_keep = chan_idx.shape[2]
+    if scores is None:
+        scores = torch.empty((sh.B, sh.Hkv, sh.S), dtype=torch.float32, device=k.device)
+    n = ctypes.c_size_t(0)
+    _check("kvc_window_scores", LIB.kvc_window_scores(ctypes.byref(sh), _dtype_code(k), None, None, None, None,
+                                                      d_keep, reduce, int(causal), None, None, ctypes.byref(n),
+                                                      None))
+    ws = _workspace(n.value, k.device, ws)
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check("kvc_window_scores", LIB.kvc_window_scores(ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid),
+                                                      _ptr(chan_idx), d_keep, reduce, int(causal), _ptr(scores),
+                                                      _ptr(ws), ctypes.byref(n), _stream(stream)))
+    return scores
+
+
+def kvc_scissor_update(step, valid, hist, counts, probs=None, frac_out=None, evict_idx=None, stream=None):
+    """Record step `step` (probs given) and/or evict (evict_idx given).  valid [B,Hkv,C]
+    uint8, hist [hist_len, B*Hkv, ceil(C/32)] int32 bit-planes, counts [B,Hkv,C] int16
+    (read as uint16)."""
+    _need(valid, "valid", 3)
+    B, Hkv, C = valid.shape
+    hist_len = hist.shape[0]
+    n_evict = 0 if evict_idx is None else evict_idx.shape[2]
+    _check("kvc_scissor_update", LIB.kvc_scissor_update(B, Hkv, C, hist_len, int(step), _ptr(probs), _ptr(valid),
+                                                        _ptr(hist), _ptr(counts), _ptr(frac_out), _ptr(evict_idx),
+                                                        n_evict, _stream(stream)))
+
+
+def channel_scores_ws_bytes(B, H, Hkv, S, D, w) -> int:
+    sh = KvcShape(B, H, Hkv, S, D, w)
+    n = ctypes.c_size_t(0)
+    _check("kvc_channel_scores", LIB.kvc_channel_scores(ctypes.byref(sh), KVC_BF16, None, None, None, None,
+                                                        ctypes.byref(n), None))
+    return n.value
+
+
+def kvc_channel_scores(q, k, out=None, ws=None, stream=None):
+    """ThinK channel scores [B,Hkv,D] float32."""
+    _need(q, "q_win", 4)
+    _need(k, "k", 4)
+    sh = _shape(q, k)
+    if out is None:
+        out = torch.empty((sh.B, sh.Hkv, sh.D), dtype=torch.float32, device=k.device)
+    n = ctypes.c_size_t(0)
+    _check("kvc_channel_scores", LIB.kvc_channel_scores(ctypes.byref(sh), _dtype_code(k), None, None, None, None,
+                                                        ctypes.byref(n), None))
+    ws = _workspace(n.value, k.device, ws)
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check("kvc_channel_scores", LIB.kvc_channel_scores(ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(out),
+                                                        _ptr(ws), ctypes.byref(n), _stream(stream)))
+    return out
+
+
+def kvc_topk_select(scores, k, n_tail=0, idx=None, ws=None, stream=None):
+    """idx [..., k] int32 (ascending) of each row of scores [..., n]."""
+    if not scores.is_contiguous() or scores.dtype != torch.float32 or not scores.is_cuda:
+        raise ValueError("scores must be a contiguous float32 CUDA tensor")
+    n = scores.shape[-1]
+    rows = scores.numel() // n
+    if idx is None:
+        idx = torch.empty((*scores.shape[:-1], k), dtype=torch.int32, device=scores.device)
+    nb = ctypes.c_size_t(0)
+    _check("kvc_topk_select", LIB.kvc_topk_select(None, rows, n, k, n_tail, None, None, ctypes.byref(nb), None))
+    ws = _workspace(nb.value, scores.device, ws)
+    nb = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check("kvc_topk_select", LIB.kvc_topk_select(_ptr(scores), rows, n, k, n_tail, _ptr(idx), _ptr(ws),
+                                                  ctypes.byref(nb), _stream(stream)))
+    return idx
+
+
+def kvc_gather_compact(k, v, idx, chan_idx=None, k_out=None, v_out=None, stream=None):
+    """Compacted (k_out, v_out) [B,Hkv,n_keep,D] of the rows idx [B,Hkv,n_keep]."""
+    _need(k, "k", 4)
+    B, Hkv, S, D = k.shape
+    n_keep = idx.shape[2]
+    sh = KvcShape(B, Hkv, Hkv, S, D, 1)
+    d_keep = 0 if chan_idx is None else chan_idx.shape[2]
+    if k_out is None:
+        k_out = torch.empty((B, Hkv, n_keep, D), dtype=k.dtype, device=k.device)
+    if v is not None and v_out is None:
+        v_out = torch.empty((B, Hkv, n_keep, D), dtype=v.dtype, device=v.device)
+    _check("kvc_gather_compact", LIB.kvc_gather_compact(ctypes.byref(sh), _dtype_code(k), _ptr(k), _ptr(v), _ptr(idx),
+                                                        n_keep, _ptr(chan_idx), d_keep, _ptr(k_out), _ptr(v_out),
+                                                        _stream(stream)))
+    return k_out, v_out

@@ -1,0 +1,97 @@
+// Gather-compact of the kept K/V rows (gfx950).
+//
+// k_out[b,g,r,:] = k[b,g,idx[b,g,r],:] with the unkept key channels written as
+// +0.0, and v_out likewise without channel pruning.  Source: "Add ThinK_Press"
+// (kvpress PR 18), option 3a: put zeros in the key cache.
+//
+// One thread moves one 16-byte unit of one row of K and the same unit of V.
+// Consecutive threads cover consecutive units of a row, so every kept row is
+// read as whole 128-byte lines and the output is written densely.  Output
+// stores are non-temporal: the compacted cache is not read again by this layer.
+#include "kvc_device.h"
+#include "kvc_launch.h"
+
+namespace kvc {
+
+namespace {
+
+constexpr int NTH = 256;
+
+template <int ESZ, int D>
+__global__ __launch_bounds__(NTH) void gather_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
+                                                     const int32_t* __restrict__ idx, int S, int n_keep,
+                                                     const int32_t* __restrict__ chan_idx, int d_keep,
+                                                     uint4* __restrict__ k_out, uint4* __restrict__ v_out,
+                                                     int Hkv) {
+  constexpr int UPR = D * ESZ / 16;  // 16-byte units per row
+  constexpr int EPU = 16 / ESZ;      // elements per unit
+  __shared__ uint32_t keep[D / 32];
+  const size_t bg = (size_t)blockIdx.z * Hkv + blockIdx.y;
+  const int tid = threadIdx.x;
+  if (chan_idx) {
+    if (tid < D / 32) keep[tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < d_keep; i += NTH) {
+      const int ch = chan_idx[bg * d_keep + i];
+      if (ch >= 0 && ch < D) atomicOr(&keep[ch >> 5], 1u << (ch & 31));
+    }
+    __syncthreads();
+  }
+  const long long u = (long long)blockIdx.x * NTH + tid;
+  const int r = (int)(u / UPR);
+  const int cu = (int)(u % UPR);
+  if (r >= n_keep) return;
+  // indices are caller data: clamp so that a bad index cannot read out of bounds
+  const int src = min(max(idx[bg * n_keep + r], 0), S - 1);
+  const size_t in_off = (bg * S + src) * UPR + cu;
+  const size_t out_off = (bg * n_keep + r) * UPR + cu;
+  uint4 kv = k[in_off];
+  if (chan_idx) {
+    uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) {
+      const int d = cu * EPU + e;
+      if (!((keep[d >> 5] >> (d & 31)) & 1u)) {
+        if constexpr (ESZ == 4) {
+          w[e] = 0u;
+        } else {
+          w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        }
+      }
+    }
+    kv = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  __builtin_nontemporal_store(kv.x, &k_out[out_off].x);
+  __builtin_nontemporal_store(kv.y, &k_out[out_off].y);
+  __builtin_nontemporal_store(kv.z, &k_out[out_off].z);
+  __builtin_nontemporal_store(kv.w, &k_out[out_off].w);
+  if (v) {
+    const uint4 vv = v[in_off];
+    __builtin_nontemporal_store(vv.x, &v_out[out_off].x);
+    __builtin_nontemporal_store(vv.y, &v_out[out_off].y);
+    __builtin_nontemporal_store(vv.z, &v_out[out_off].z);
+    __builtin_nontemporal_store(vv.w, &v_out[out_off].w);
+  }
+}
+
+template <int ESZ, int D>
+void run(const GatherArgs& a, hipStream_t st) {
+  constexpr int UPR = D * ESZ / 16;
+  const long long units = (long long)a.n_keep * UPR;
+  const dim3 grid((unsigned)((units + NTH - 1) / NTH), a.Hkv, a.B);
+  gather_kernel<ESZ, D><<<grid, NTH, 0, st>>>(
+      static_cast<const uint4*>(a.k), static_cast<const uint4*>(a.v), a.idx, a.S, a.n_keep, a.chan_idx, a.d_keep,
+      static_cast<uint4*>(a.k_out), static_cast<uint4*>(a.v_out), a.Hkv);
+}
+
+}  // namespace
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st) {
+  if (a.bf16 && a.D == 128) run<2, 128>(a, st);
+  else if (a.bf16) run<2, 64>(a, st);
+  else if (a.D == 128) run<4, 128>(a, st);
+  else run<4, 64>(a, st);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

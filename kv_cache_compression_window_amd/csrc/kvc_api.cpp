@@ -1,0 +1,189 @@
+// C-ABI entry points of libkvc: argument validation, workspace sizing and dispatch.
+// Validation runs before any HIP call, so every error path can be exercised on a
+// machine without a GPU.
+#include "../../include/kvc.h"
+
+#include "kvc_launch.h"
+#include "kvc_plan.h"
+
+namespace {
+
+inline bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+inline bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
+
+inline kvc_status hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
+
+// Shape checks shared by the calls that take a kvc_shape.
+kvc_status check_shape(const kvc_shape* sh, bool need_window) {
+  if (sh->B < 1 || sh->H < 1 || sh->Hkv < 1 || sh->S < 1) return KVC_ERR_SHAPE;
+  if (sh->H % sh->Hkv != 0) return KVC_ERR_SHAPE;
+  if (sh->B > 65535 || sh->Hkv > 65535) return KVC_ERR_SHAPE;  // grid y/z limits
+  if (need_window && (sh->w < 1 || sh->w > sh->S)) return KVC_ERR_SHAPE;
+  if (sh->D != 64 && sh->D != 128) return KVC_ERR_UNSUPPORTED;
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvc_status_string(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_NULL: return "a required pointer is NULL";
+    case KVC_ERR_SHAPE: return "sizes out of range or inconsistent";
+    case KVC_ERR_DTYPE: return "unknown dtype or reduce mode";
+    case KVC_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case KVC_ERR_WORKSPACE: return "workspace too small";
+    case KVC_ERR_UNSUPPORTED: return "unsupported size";
+    case KVC_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+kvc_status kvc_window_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
+                             const uint8_t* valid, const int32_t* chan_idx, int32_t d_keep, kvc_reduce reduce,
+                             int32_t causal, float* scores, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  if (!sh || !ws_bytes) return KVC_ERR_NULL;
+  if (dt != KVC_F32 && dt != KVC_BF16) return KVC_ERR_DTYPE;
+  if (reduce != KVC_REDUCE_GROUP && reduce != KVC_REDUCE_ALL_HEADS) return KVC_ERR_DTYPE;
+  kvc_status st = check_shape(sh, true);
+  if (st != KVC_OK) return st;
+  if (chan_idx && (d_keep < 1 || d_keep > sh->D)) return KVC_ERR_SHAPE;
+  kvc::WsPlan plan;
+  if (!kvc::ws_make_plan(sh->B, sh->H, sh->Hkv, sh->S, sh->w, &plan)) return KVC_ERR_UNSUPPORTED;
+  if (!ws) {
+    *ws_bytes = plan.bytes;
+    return KVC_OK;
+  }
+  if (*ws_bytes < plan.bytes) return KVC_ERR_WORKSPACE;
+  if (!q_win || !k || !scores) return KVC_ERR_NULL;
+  if (misaligned16(q_win) || misaligned16(k) || misaligned4(scores) || misaligned16(ws)) return KVC_ERR_ALIGN;
+  kvc::WsArgs a;
+  a.bf16 = dt == KVC_BF16;
+  a.B = sh->B;
+  a.H = sh->H;
+  a.Hkv = sh->Hkv;
+  a.S = sh->S;
+  a.D = sh->D;
+  a.w = sh->w;
+  a.q = q_win;
+  a.k = k;
+  a.valid = valid;
+  a.chan_idx = chan_idx;
+  a.d_keep = chan_idx ? d_keep : 0;
+  a.reduce = reduce == KVC_REDUCE_ALL_HEADS;
+  a.causal = causal != 0;
+  a.scores = scores;
+  a.ws = ws;
+  return hip_status(kvc::launch_window_scores(a, plan, stream));
+}
+
+kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_len, int64_t step,
+                              const float* probs, uint8_t* valid, uint32_t* hist, uint16_t* counts,
+                              float* frac_out, const int32_t* evict_idx, int32_t n_evict, hipStream_t stream) {
+  if (B < 1 || Hkv < 1 || C < 1 || hist_len < 1 || hist_len > 65535 || step < 0) return KVC_ERR_SHAPE;
+  if ((int64_t)B * Hkv > 0x7fffffffLL) return KVC_ERR_SHAPE;
+  if (n_evict < 0 || n_evict > C) return KVC_ERR_SHAPE;
+  if (!valid) return KVC_ERR_NULL;
+  if (probs && (!hist || !counts)) return KVC_ERR_NULL;
+  if (probs && (misaligned4(probs) || misaligned4(hist) || (frac_out && misaligned4(frac_out)) ||
+                (reinterpret_cast<uintptr_t>(counts) & 1u)))
+    return KVC_ERR_ALIGN;
+  kvc::ScissorArgs a;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.C = C;
+  a.hist_len = hist_len;
+  a.step = step;
+  a.probs = probs;
+  a.valid = valid;
+  a.hist = hist;
+  a.counts = counts;
+  a.frac_out = probs ? frac_out : nullptr;
+  a.evict_idx = evict_idx;
+  a.n_evict = evict_idx ? n_evict : 0;
+  if (!a.probs && !a.evict_idx) return KVC_OK;
+  return hip_status(kvc::launch_scissor(a, stream));
+}
+
+kvc_status kvc_channel_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
+                              float* chan_scores, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  if (!sh || !ws_bytes) return KVC_ERR_NULL;
+  if (dt != KVC_F32 && dt != KVC_BF16) return KVC_ERR_DTYPE;
+  kvc_status st = check_shape(sh, true);
+  if (st != KVC_OK) return st;
+  kvc::CsPlan plan;
+  kvc::cs_make_plan(sh->B, sh->Hkv, sh->S, sh->D, &plan);
+  if (!ws) {
+    *ws_bytes = plan.bytes;
+    return KVC_OK;
+  }
+  if (*ws_bytes < plan.bytes) return KVC_ERR_WORKSPACE;
+  if (!q_win || !k || !chan_scores) return KVC_ERR_NULL;
+  if (misaligned16(q_win) || misaligned16(k) || misaligned4(chan_scores) || misaligned4(ws)) return KVC_ERR_ALIGN;
+  kvc::CsArgs a;
+  a.bf16 = dt == KVC_BF16;
+  a.B = sh->B;
+  a.H = sh->H;
+  a.Hkv = sh->Hkv;
+  a.S = sh->S;
+  a.D = sh->D;
+  a.w = sh->w;
+  a.q = q_win;
+  a.k = k;
+  a.out = chan_scores;
+  a.ws = ws;
+  return hip_status(kvc::launch_channel_scores(a, plan, stream));
+}
+
+kvc_status kvc_topk_select(const float* scores, int32_t rows, int32_t n, int32_t k, int32_t n_tail, int32_t* idx,
+                           void* ws, size_t* ws_bytes, hipStream_t stream) {
+  if (!ws_bytes) return KVC_ERR_NULL;
+  if (rows < 0 || n < 1 || n_tail < 0 || n_tail > k || k > n) return KVC_ERR_SHAPE;
+  if (!ws) {
+    *ws_bytes = kvc::topk_ws_bytes(rows, n);
+    return KVC_OK;
+  }
+  if (*ws_bytes < kvc::topk_ws_bytes(rows, n)) return KVC_ERR_WORKSPACE;
+  if (rows == 0 || k == 0) return KVC_OK;
+  if (!scores || !idx) return KVC_ERR_NULL;
+  if (misaligned4(scores) || misaligned4(idx)) return KVC_ERR_ALIGN;
+  return hip_status(kvc::launch_topk(scores, rows, n, k, n_tail, idx, stream));
+}
+
+kvc_status kvc_gather_compact(const kvc_shape* sh, kvc_dtype dt, const void* k, const void* v, const int32_t* idx,
+                              int32_t n_keep, const int32_t* chan_idx, int32_t d_keep, void* k_out, void* v_out,
+                              hipStream_t stream) {
+  if (!sh) return KVC_ERR_NULL;
+  if (dt != KVC_F32 && dt != KVC_BF16) return KVC_ERR_DTYPE;
+  kvc_status st = check_shape(sh, false);
+  if (st != KVC_OK) return st;
+  if (n_keep < 0 || n_keep > sh->S) return KVC_ERR_SHAPE;
+  if (chan_idx && (d_keep < 1 || d_keep > sh->D)) return KVC_ERR_SHAPE;
+  if (n_keep == 0) return KVC_OK;
+  if (!k || !idx || !k_out) return KVC_ERR_NULL;
+  if (v && !v_out) return KVC_ERR_NULL;
+  if (misaligned16(k) || misaligned16(k_out) || (v && (misaligned16(v) || misaligned16(v_out))) ||
+      misaligned4(idx))
+    return KVC_ERR_ALIGN;
+  kvc::GatherArgs a;
+  a.bf16 = dt == KVC_BF16;
+  a.B = sh->B;
+  a.Hkv = sh->Hkv;
+  a.S = sh->S;
+  a.D = sh->D;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.n_keep = n_keep;
+  a.chan_idx = chan_idx;
+  a.d_keep = chan_idx ? d_keep : 0;
+  a.k_out = k_out;
+  a.v_out = v ? v_out : nullptr;
+  return hip_status(kvc::launch_gather(a, stream));
+}
+
+}  // extern "C"

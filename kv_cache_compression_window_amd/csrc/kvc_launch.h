@@ -1,0 +1,66 @@
+// Launchers of the gfx950 kernels (host functions defined in the .hip files).
+// Arguments have been validated by the C-ABI layer before these are called.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "kvc_plan.h"
+
+namespace kvc {
+
+struct WsArgs {
+  int bf16;  // 1: bfloat16 storage, 0: float32
+  int B, H, Hkv, S, D, w;
+  const void* q;
+  const void* k;
+  const uint8_t* valid;
+  const int32_t* chan_idx;
+  int d_keep;
+  int reduce;  // 0 group, 1 all heads
+  int causal;
+  float* scores;
+  void* ws;
+};
+hipError_t launch_window_scores(const WsArgs& a, const WsPlan& plan, hipStream_t st);
+
+struct CsArgs {
+  int bf16;
+  int B, H, Hkv, S, D, w;
+  const void* q;
+  const void* k;
+  float* out;
+  void* ws;
+};
+hipError_t launch_channel_scores(const CsArgs& a, const CsPlan& plan, hipStream_t st);
+
+hipError_t launch_topk(const float* scores, int rows, int n, int k, int n_tail, int32_t* idx,
+                       hipStream_t st);
+
+struct GatherArgs {
+  int bf16;
+  int B, Hkv, S, D;
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  int n_keep;
+  const int32_t* chan_idx;
+  int d_keep;
+  void* k_out;
+  void* v_out;
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
+
+struct ScissorArgs {
+  int B, Hkv, C, hist_len;
+  int64_t step;
+  const float* probs;
+  uint8_t* valid;
+  uint32_t* hist;
+  uint16_t* counts;
+  float* frac_out;
+  const int32_t* evict_idx;
+  int n_evict;
+};
+hipError_t launch_scissor(const ScissorArgs& a, hipStream_t st);
+
+}  // namespace kvc

@@ -1,0 +1,92 @@
+// Host-side launch planning shared by the C-ABI entry points and the launchers.
+// Plain C++ (no device code): sizes, tilings and workspace layouts.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvc {
+
+constexpr int kTileKeys = 64;  // keys per LDS tile in the window-score kernels
+
+// How kvc_window_scores runs a given shape.
+//  * two-pass path (rows per KV head R > 16): pass 1 computes per-row (max, sum
+//    of exp2) over a chunk of keys, a merge kernel combines the chunks into a
+//    per-row log-normaliser, pass 2 recomputes the logits and sums the
+//    normalised probabilities over the group's rows;
+//  * stored-logits path (R <= 16): pass 1 also writes the scaled logits of the
+//    real rows, and a light kernel normalises and reduces them, so the keys are
+//    read from HBM once.
+struct WsPlan {
+  bool store;       // stored-logits path
+  int NW, RB;       // waves per workgroup, 32-row blocks per wave
+  int R, Rpad;      // rows per KV head (G*w) and padded rows (NW*RB*32)
+  int CH, nchunks;  // keys per chunk (multiple of kTileKeys) and chunks per (b,g)
+  int Spad;         // row stride of the stored logits (multiple of kTileKeys)
+  size_t off_part, off_lse, off_logits, bytes;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, WsPlan* p) {
+  const int G = H / Hkv;
+  const long long R = (long long)G * w;
+  if (R > 512) return false;
+  p->R = (int)R;
+  p->store = R <= 16;
+  const int nrb = (int)((R + 31) / 32);
+  if (nrb <= 1) { p->NW = 1; p->RB = 1; }
+  else if (nrb == 2) { p->NW = 2; p->RB = 1; }
+  else if (nrb <= 4) { p->NW = 4; p->RB = 1; }
+  else if (nrb <= 8) { p->NW = 4; p->RB = 2; }
+  else { p->NW = 4; p->RB = 4; }
+  p->Rpad = p->NW * p->RB * 32;
+  const long long bg = (long long)B * Hkv;
+  const long long target = p->store ? 4096 : 1024;  // workgroups to aim for
+  long long nch = (target + bg - 1) / bg;
+  const long long max_ch = (S + kTileKeys - 1) / kTileKeys;
+  if (nch > max_ch) nch = max_ch;
+  if (nch < 1) nch = 1;
+  long long per = (S + nch - 1) / nch;
+  per = (per + kTileKeys - 1) / kTileKeys * kTileKeys;
+  p->CH = (int)per;
+  p->nchunks = (int)((S + per - 1) / per);
+  p->Spad = (int)((S + kTileKeys - 1) / kTileKeys * kTileKeys);
+  size_t off = 0;
+  p->off_part = off;
+  off += align256((size_t)bg * p->Rpad * p->nchunks * 2 * sizeof(float));
+  p->off_lse = off;
+  off += align256((size_t)bg * p->Rpad * sizeof(float));
+  p->off_logits = off;
+  if (p->store) off += align256((size_t)bg * p->R * p->Spad * sizeof(float));
+  p->bytes = off;
+  return true;
+}
+
+// kvc_channel_scores: keys per chunk of the partial sums of k^2.
+struct CsPlan {
+  int CH, nchunks;
+  size_t bytes;
+};
+
+inline void cs_make_plan(int B, int Hkv, int S, int D, CsPlan* p) {
+  const long long bg = (long long)B * Hkv;
+  long long nch = (2048 + bg - 1) / bg;
+  const long long max_ch = (S + 63) / 64;
+  if (nch > max_ch) nch = max_ch;
+  if (nch < 1) nch = 1;
+  long long per = (S + nch - 1) / nch;
+  per = (per + 63) / 64 * 64;
+  p->CH = (int)per;
+  p->nchunks = (int)((S + per - 1) / per);
+  p->bytes = align256((size_t)bg * p->nchunks * D * sizeof(float));
+}
+
+// kvc_topk_select needs no workspace beyond a small fixed area (kept so the
+// signature can grow a multi-workgroup select without an ABI change).
+inline size_t topk_ws_bytes(int rows, int n) {
+  (void)rows;
+  (void)n;
+  return 256;
+}
+
+}  // namespace kvc

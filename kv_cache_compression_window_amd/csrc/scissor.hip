@@ -1,0 +1,94 @@
+// Scissorhands low-attention history: record one decode step, bulk eviction (gfx950).
+//
+// Source: "Implement Scissorhands KV-cache compression & SnapKV prompt
+// compression" (cold-compress PR 11).  The cache.py hunks mark a slot low when
+// its attention is below uniform attention 1/keys.  The circular slot
+// counter % history_window_size holds the newest indicator.  The PR description
+// evicts per head the tokens with the highest fraction of unimportant
+// attentions, and bulk eviction leaves holes.
+//
+// The history is kept as bit-planes (one plane per circular slot, one bit per
+// cache slot) plus a running count per slot.  A step reads and writes one plane
+// and the counts instead of a [slots x history] integer tensor.
+#include "kvc_device.h"
+#include "kvc_launch.h"
+
+namespace kvc {
+
+namespace {
+
+constexpr int NTH = 256;
+
+__global__ __launch_bounds__(NTH) void scissor_record_kernel(int C, int W, int BHkv, int plane, int n_obs,
+                                                              const float* __restrict__ probs,
+                                                              const uint8_t* __restrict__ valid,
+                                                              uint32_t* __restrict__ hist,
+                                                              uint16_t* __restrict__ counts,
+                                                              float* __restrict__ frac_out) {
+  __shared__ int red[NTH / 64];
+  const size_t bg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint8_t* vrow = valid + bg * C;
+
+  // S_t: number of valid slots of this (b, g)
+  int cnt = 0;
+  for (int c = tid; c < C; c += NTH) cnt += vrow[c] != 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  if (lane == 0) red[wave] = cnt;
+  __syncthreads();
+  int S_t = 0;
+#pragma unroll
+  for (int wv = 0; wv < NTH / 64; ++wv) S_t += red[wv];
+  const double uniform = S_t > 0 ? 1.0 / (double)S_t : 0.0;
+  const float inv_obs = 1.0f / (float)n_obs;
+
+  uint32_t* prow = hist + ((size_t)plane * BHkv + bg) * W;
+  for (int c0 = 0; c0 < C; c0 += NTH) {
+    const int c = c0 + tid;  // c0 is a multiple of 64, so a wave covers whole words
+    const bool in = c < C;
+    const bool v = in && vrow[c] != 0;
+    const bool low = v && ((double)probs[bg * C + c] < uniform);
+    const unsigned long long bits = __ballot(low);
+    uint32_t old_bit = 0u;
+    if (in) old_bit = (prow[c >> 5] >> (c & 31)) & 1u;
+    if (in) {
+      const int cnew = (int)counts[bg * C + c] + (int)low - (int)old_bit;
+      counts[bg * C + c] = (uint16_t)cnew;
+      if (frac_out) frac_out[bg * C + c] = v ? (float)cnew * inv_obs : kNegInf;
+    }
+    // all lanes have read the old word before it is overwritten (ballot above
+    // and the wave's single instruction stream order the reads first)
+    __builtin_amdgcn_wave_barrier();
+    if (in && (lane == 0 || lane == 32)) {
+      const uint32_t word = (lane == 0) ? (uint32_t)bits : (uint32_t)(bits >> 32);
+      prow[c >> 5] = word;
+    }
+  }
+}
+
+__global__ void scissor_evict_kernel(int C, int n_evict, const int32_t* __restrict__ evict_idx,
+                                     uint8_t* __restrict__ valid) {
+  const size_t bg = blockIdx.x;
+  for (int e = threadIdx.x; e < n_evict; e += blockDim.x) {
+    const int c = evict_idx[bg * n_evict + e];
+    if (c >= 0 && c < C) valid[bg * C + c] = 0;  // out-of-range indices are ignored
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scissor(const ScissorArgs& a, hipStream_t st) {
+  const int BHkv = a.B * a.Hkv;
+  const int W = (a.C + 31) / 32;
+  if (a.probs) {
+    const int plane = (int)(a.step % a.hist_len);
+    const int64_t obs = a.step + 1 < a.hist_len ? a.step + 1 : a.hist_len;
+    scissor_record_kernel<<<BHkv, NTH, 0, st>>>(a.C, W, BHkv, plane, (int)obs, a.probs, a.valid, a.hist,
+                                                a.counts, a.frac_out);
+  }
+  if (a.evict_idx && a.n_evict > 0) scissor_evict_kernel<<<BHkv, 256, 0, st>>>(a.C, a.n_evict, a.evict_idx, a.valid);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

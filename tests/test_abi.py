@@ -1,0 +1,140 @@
+"""libkvc loads, exports what include/kvc.h declares, and validates on the host.
+
+No test here launches a kernel: every call returns from validation or from a
+workspace query before touching the GPU, so this file runs on a CPU-only machine.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+LIB_PATH = os.path.join(ROOT, "kv_cache_compression_window_amd", "libkvc.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        from kv_cache_compression_window_amd.build import build
+        build(verbose=False)
+    from kv_cache_compression_window_amd import binding
+    return binding
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert set(names) == set(lib.EXPORTS)
+    raw = ctypes.CDLL(LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.abi_version() == 1
+    for code in range(8):
+        s = lib.LIB.kvc_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.LIB.kvc_status_string(99).decode() == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x100000)      # 16-byte aligned, never dereferenced
+ODD = ctypes.c_void_p(0x100008)       # 8-byte aligned only
+
+
+def ws_call(lib, sh, dt=1, q=FAKE, k=FAKE, valid=None, chan=None, d_keep=0, reduce=0, causal=1, scores=FAKE,
+            ws=FAKE, nbytes=1 << 40):
+    n = ctypes.c_size_t(nbytes)
+    return lib.LIB.kvc_window_scores(ctypes.byref(sh) if sh is not None else None, dt, q, k, valid, chan, d_keep,
+                                     reduce, causal, scores, ws, ctypes.byref(n), None)
+
+
+def test_window_scores_validation(lib):
+    S = lib.KvcShape
+    ok = S(1, 32, 8, 4096, 128, 64)
+    assert ws_call(lib, None) == 1
+    assert ws_call(lib, ok, dt=5) == 3
+    assert ws_call(lib, ok, reduce=2) == 3
+    assert ws_call(lib, S(1, 30, 8, 4096, 128, 64)) == 2       # H % Hkv
+    assert ws_call(lib, S(0, 32, 8, 4096, 128, 64)) == 2       # B
+    assert ws_call(lib, S(1, 32, 8, 4096, 128, 0)) == 2        # w
+    assert ws_call(lib, S(1, 32, 8, 63, 128, 64)) == 2         # w > S
+    assert ws_call(lib, S(1, 32, 8, 4096, 96, 64)) == 6        # D
+    assert ws_call(lib, S(1, 64, 8, 4096, 128, 128)) == 6      # G*w > 512
+    assert ws_call(lib, ok, chan=FAKE, d_keep=0) == 2
+    assert ws_call(lib, ok, chan=FAKE, d_keep=129) == 2
+    assert ws_call(lib, ok, q=None) == 1
+    assert ws_call(lib, ok, scores=None) == 1
+    assert ws_call(lib, ok, q=ODD) == 4
+    assert ws_call(lib, ok, k=ODD) == 4
+    assert ws_call(lib, ok, nbytes=16) == 5
+    # workspace query launches nothing and returns the size
+    n = ctypes.c_size_t(0)
+    assert lib.LIB.kvc_window_scores(ctypes.byref(ok), 1, None, None, None, None, 0, 0, 1, None, None,
+                                     ctypes.byref(n), None) == 0
+    assert n.value > 0
+    assert lib.window_scores_ws_bytes(1, 32, 8, 32768, 128, 64) > 0
+
+
+def test_window_scores_workspace_grows_with_rows(lib):
+    small = lib.window_scores_ws_bytes(1, 4, 2, 512, 64, 1)     # stored-logits path
+    big = lib.window_scores_ws_bytes(1, 32, 8, 32768, 128, 64)  # two-pass path
+    assert small >= 2 * 2 * 512 * 4  # the stored logits: 2 KV heads x 2 rows x 512 keys
+    assert big >= 8 * 256 * 4         # one normaliser per row
+
+
+def test_scissor_validation(lib):
+    f = lib.LIB.kvc_scissor_update
+    assert f(0, 8, 4096, 400, 0, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 2
+    assert f(8, 8, 4096, 0, 0, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 2
+    assert f(8, 8, 4096, 70000, 0, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 2
+    assert f(8, 8, 4096, 400, -1, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 2
+    assert f(8, 8, 4096, 400, 0, FAKE, None, FAKE, FAKE, None, None, 0, None) == 1
+    assert f(8, 8, 4096, 400, 0, FAKE, FAKE, None, FAKE, None, None, 0, None) == 1
+    assert f(8, 8, 4096, 400, 0, FAKE, FAKE, FAKE, None, None, None, 0, None) == 1
+    assert f(8, 8, 4096, 400, 0, None, FAKE, None, None, None, FAKE, 4097, None) == 2
+    assert f(8, 8, 4096, 400, 0, ctypes.c_void_p(0x100002), FAKE, FAKE, FAKE, None, None, 0, None) == 4
+    # nothing to do is not an error
+    assert f(8, 8, 4096, 400, 0, None, FAKE, None, None, None, None, 0, None) == 0
+
+
+def test_topk_validation(lib):
+    f = lib.LIB.kvc_topk_select
+    n = ctypes.c_size_t(1 << 20)
+    assert f(FAKE, 8, 100, 10, 0, FAKE, FAKE, None, None) == 1
+    assert f(FAKE, 8, 100, 101, 0, FAKE, FAKE, ctypes.byref(n), None) == 2
+    assert f(FAKE, 8, 100, 10, 11, FAKE, FAKE, ctypes.byref(n), None) == 2
+    assert f(FAKE, 8, 0, 0, 0, FAKE, FAKE, ctypes.byref(n), None) == 2
+    assert f(None, 8, 100, 10, 0, FAKE, FAKE, ctypes.byref(n), None) == 1
+    assert f(ctypes.c_void_p(0x100002), 8, 100, 10, 0, FAKE, FAKE, ctypes.byref(n), None) == 4
+    small = ctypes.c_size_t(0)
+    assert f(FAKE, 8, 100, 10, 0, FAKE, FAKE, ctypes.byref(small), None) == 5
+    q = ctypes.c_size_t(0)
+    assert f(None, 8, 100, 10, 0, None, None, ctypes.byref(q), None) == 0 and q.value > 0
+    assert f(FAKE, 0, 100, 10, 0, FAKE, FAKE, ctypes.byref(n), None) == 0  # no rows: no-op
+
+
+def test_gather_and_channel_validation(lib):
+    S = lib.KvcShape
+    sh = S(1, 8, 8, 4096, 128, 1)
+    g = lib.LIB.kvc_gather_compact
+    assert g(None, 1, FAKE, FAKE, FAKE, 10, None, 0, FAKE, FAKE, None) == 1
+    assert g(ctypes.byref(sh), 2, FAKE, FAKE, FAKE, 10, None, 0, FAKE, FAKE, None) == 3
+    assert g(ctypes.byref(sh), 1, FAKE, FAKE, FAKE, 4097, None, 0, FAKE, FAKE, None) == 2
+    assert g(ctypes.byref(sh), 1, FAKE, FAKE, FAKE, 10, FAKE, 0, FAKE, FAKE, None) == 2
+    assert g(ctypes.byref(sh), 1, None, FAKE, FAKE, 10, None, 0, FAKE, FAKE, None) == 1
+    assert g(ctypes.byref(sh), 1, FAKE, FAKE, FAKE, 10, None, 0, FAKE, None, None) == 1
+    assert g(ctypes.byref(sh), 1, FAKE, FAKE, FAKE, 10, None, 0, ODD, FAKE, None) == 4
+    assert g(ctypes.byref(sh), 1, FAKE, FAKE, FAKE, 0, None, 0, FAKE, FAKE, None) == 0
+    c = lib.LIB.kvc_channel_scores
+    n = ctypes.c_size_t(1 << 40)
+    assert c(ctypes.byref(S(1, 32, 8, 4096, 100, 64)), 1, FAKE, FAKE, FAKE, FAKE, ctypes.byref(n), None) == 6
+    assert c(ctypes.byref(S(1, 32, 8, 4096, 128, 64)), 1, None, FAKE, FAKE, FAKE, ctypes.byref(n), None) == 1
+    assert lib.channel_scores_ws_bytes(1, 32, 8, 131072, 128, 64) > 0

@@ -1,0 +1,219 @@
+"""GPU parity of every C-ABI call against the fp64 oracle (small shapes).
+
+The shapes span every kernel variant: the stored-logits path (G*w <= 16), the
+two-pass path with 1, 2 and 4 waves and 1, 2 and 4 row blocks per wave, several
+key tiles and chunks with ragged ends, D = 64 and 128, fp32 and bf16, holes,
+channel masks, causal windows and both reductions.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_window_amd import synth
+from oracle import kvc_oracle as O
+from tests.gpu_util import check_gather, check_kept, check_scores, dev, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def lib():
+    from kv_cache_compression_window_amd import binding
+    return binding
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# (name, B, H, Hkv, S, D, w, dtype, reduce, causal, holes, d_keep, q_scale)
+CASES = [
+    ("tova_tiny_f32", 1, 4, 2, 512, 64, 1, "f32", 1, 0, 0.0, 0, 1.0),
+    ("store_group_holes", 2, 32, 8, 2049, 128, 1, "bf16", 0, 0, 0.2, 0, 1.0),
+    ("store_allheads_b3", 3, 32, 8, 1111, 128, 1, "bf16", 1, 0, 0.0, 0, 1.0),
+    ("store_w4_causal", 1, 8, 2, 100, 128, 4, "bf16", 0, 1, 0.0, 0, 2.0),
+    ("store_s1", 1, 4, 2, 1, 64, 1, "bf16", 0, 1, 0.0, 0, 1.0),
+    ("store_f32_d128_chan", 2, 4, 1, 333, 128, 2, "f32", 0, 1, 0.1, 40, 1.0),
+    ("two_pass_r32_d64", 1, 4, 1, 300, 64, 8, "bf16", 0, 1, 0.0, 0, 1.0),
+    ("two_pass_r64", 1, 8, 2, 777, 128, 16, "bf16", 0, 1, 0.0, 0, 1.0),
+    ("two_pass_r96_f32", 1, 4, 2, 500, 128, 48, "f32", 0, 1, 0.0, 0, 1.0),
+    ("two_pass_r256_snapkv", 1, 32, 8, 1000, 128, 64, "bf16", 0, 1, 0.0, 0, 1.0),
+    ("two_pass_r256_allheads", 2, 32, 8, 700, 128, 64, "bf16", 1, 1, 0.0, 0, 1.0),
+    ("two_pass_r256_chan", 1, 32, 8, 700, 128, 64, "bf16", 0, 1, 0.0, 64, 1.0),
+    ("two_pass_r256_holes", 1, 32, 8, 650, 128, 64, "bf16", 0, 0, 0.3, 0, 3.0),
+    ("two_pass_r512", 1, 64, 8, 513, 128, 64, "bf16", 0, 1, 0.0, 0, 1.0),
+    ("two_pass_s_eq_w", 1, 8, 2, 40, 64, 40, "bf16", 0, 1, 0.0, 0, 1.0),
+    ("two_pass_g1", 1, 4, 4, 260, 128, 32, "bf16", 0, 1, 0.0, 0, 1.0),
+]
+
+
+def _make(case, seed):
+    name, B, H, Hkv, S, D, w, dt, reduce, causal, holes, d_keep, qs = case
+    p = synth.random_problem(seed, B, H, Hkv, S, D, w, dtype=dt, heavy_frac=0.02, q_scale=qs)
+    valid = synth.random_valid(seed, B, Hkv, S, holes) if holes > 0 else None
+    if valid is not None and B * Hkv > 1:
+        valid[0, 0, :] = 0  # one (b, g) with no valid key at all
+    chan = None
+    if d_keep:
+        rs = np.random.default_rng(seed)
+        chan = np.stack([np.stack([np.sort(rs.choice(D, d_keep, replace=False)) for _ in range(Hkv)])
+                         for _ in range(B)]).astype(np.int32)
+    return p, valid, chan
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_window_scores(case):
+    name, B, H, Hkv, S, D, w, dt, reduce, causal, holes, d_keep, qs = case
+    say(f"window_scores {name}")
+    p, valid, chan = _make(case, 100 + CASES.index(case))
+    ref = O.window_scores(p.q64(), p.k64(), valid=valid, chan_keep=chan, reduce=reduce, causal=causal)
+    L = lib()
+    s = L.kvc_window_scores(dev(p.q, dt), dev(p.k, dt), valid=None if valid is None else dev(valid),
+                            chan_idx=None if chan is None else dev(chan), reduce=reduce, causal=bool(causal))
+    torch.cuda.synchronize()
+    check_scores(s.cpu().numpy(), ref, name)
+    # determinism: a second call gives the same bits
+    s2 = L.kvc_window_scores(dev(p.q, dt), dev(p.k, dt), valid=None if valid is None else dev(valid),
+                             chan_idx=None if chan is None else dev(chan), reduce=reduce, causal=bool(causal))
+    assert torch.equal(s, s2)
+
+
+@pytest.mark.parametrize("rows,n,k,n_tail,levels", [
+    (8, 32768, 4096, 64, 0), (3, 1000, 10, 0, 0), (5, 777, 300, 20, 4), (2, 200000, 5000, 64, 0),
+    (64, 4096, 64, 0, 401), (7, 129, 64, 0, 3), (1, 50, 50, 5, 0), (4, 60, 5, 5, 0), (3, 64, 1, 0, 2),
+    (2, 40000, 39000, 0, 0), (1, 1, 1, 0, 0), (6, 5000, 0, 0, 0)])
+def test_topk(rows, n, k, n_tail, levels):
+    say(f"topk rows={rows} n={n} k={k} tail={n_tail} levels={levels}")
+    s = synth.random_scores(rows * 7 + n, rows, n, levels)
+    if levels == 401:  # Scissorhands fractions: count / 400 with holes at -inf
+        s = np.floor(s * 400).astype(np.float32) / np.float32(400)
+        s[:, ::7] = -np.inf
+    idx = lib().kvc_topk_select(dev(s), k, n_tail)
+    torch.cuda.synchronize()
+    ig = idx.cpu().numpy().astype(np.int64)
+    if k == 0:
+        return
+    assert np.array_equal(ig, O.topk_select(s.astype(np.float64), k, n_tail))
+
+
+@pytest.mark.parametrize("dt,D,chan", [("bf16", 128, True), ("bf16", 64, False), ("f32", 128, True),
+                                       ("f32", 64, False)])
+def test_gather(dt, D, chan):
+    say(f"gather {dt} D={D} chan={chan}")
+    B, Hkv, S, n_keep = 2, 3, 517, 129
+    p = synth.random_problem(7, B, Hkv, Hkv, S, D, 1, dtype=dt)
+    rs = np.random.default_rng(1)
+    idx = np.stack([np.stack([np.sort(rs.choice(S, n_keep, replace=False)) for _ in range(Hkv)])
+                    for _ in range(B)]).astype(np.int32)
+    ch = None
+    if chan:
+        ch = np.stack([np.stack([np.sort(rs.choice(D, D // 2, replace=False)) for _ in range(Hkv)])
+                       for _ in range(B)]).astype(np.int32)
+    ko, vo = lib().kvc_gather_compact(dev(p.k, dt), dev(p.v, dt), dev(idx), chan_idx=None if ch is None else dev(ch))
+    torch.cuda.synchronize()
+    check_gather(ko, vo, p.k, p.v, idx, ch)
+    # K only
+    ko2, vo2 = lib().kvc_gather_compact(dev(p.k, dt), None, dev(idx), chan_idx=None if ch is None else dev(ch))
+    assert vo2 is None and torch.equal(ko.view(torch.uint8), ko2.view(torch.uint8))
+
+
+@pytest.mark.parametrize("dt,D,S,w,G", [("bf16", 128, 3001, 64, 4), ("f32", 64, 130, 3, 2), ("bf16", 64, 1, 1, 1)])
+def test_channel_scores(dt, D, S, w, G):
+    say(f"channel_scores {dt} D={D} S={S}")
+    B, Hkv = 2, 2
+    p = synth.random_problem(9, B, G * Hkv, Hkv, S, D, w, dtype=dt)
+    ref = O.channel_scores(p.q64(), p.k64())
+    cs = lib().kvc_channel_scores(dev(p.q, dt), dev(p.k, dt))
+    torch.cuda.synchronize()
+    check_scores(cs.cpu().numpy(), ref, "channel scores")
+    cs2 = lib().kvc_channel_scores(dev(p.q, dt), dev(p.k, dt))
+    assert torch.equal(cs, cs2)
+
+
+def unpack_planes(hist: np.ndarray, bg: int, C: int) -> np.ndarray:
+    """[C, hist_len] 0/1 matrix of the bit-planes of row bg."""
+    words = hist[:, bg, :].astype(np.uint32)  # [hist_len, W]
+    bits = np.unpackbits(words.view(np.uint8).reshape(words.shape[0], -1), bitorder="little", axis=1)
+    return bits[:, :C].T.astype(np.int8)
+
+
+def test_scissorhands_lockstep_small():
+    """Teacher-forced lockstep: after every step the oracle adopts the GPU's state
+    and checks the step's low bits (except within 1e-5 of the threshold), counts,
+    fractions and evictions."""
+    say("scissorhands lockstep small")
+    B, H, Hkv, C, D, hist_len, every, n_ev, steps = 2, 8, 2, 300, 128, 7, 5, 9, 23
+    L = lib()
+    k = synth.random_problem(3, B, Hkv, Hkv, C, D, 1, dtype="bf16", heavy_frac=0.05)
+    kd = dev(k.k, "bf16")
+    k64 = k.k64()
+    valid = torch.ones((B, Hkv, C), dtype=torch.uint8, device="cuda")
+    W = (C + 31) // 32
+    hist = torch.zeros((hist_len, B * Hkv, W), dtype=torch.int32, device="cuda")
+    counts = torch.zeros((B, Hkv, C), dtype=torch.int16, device="cuda")
+    frac = torch.empty((B, Hkv, C), dtype=torch.float32, device="cuda")
+    for t in range(steps):
+        q = synth.random_problem(1000 + t, B, H, Hkv, 1, D, 1, dtype="bf16", with_v=False).q
+        v_before = valid.cpu().numpy().copy()
+        hist_before = hist.cpu().numpy().copy()
+        probs = L.kvc_window_scores(dev(q, "bf16"), kd, valid=valid, reduce=0, causal=False)
+        evict = (t + 1) % every == 0
+        L.kvc_scissor_update(t, valid, hist, counts, probs=probs, frac_out=frac if evict else None)
+        idx = None
+        if evict:
+            idx = L.kvc_topk_select(frac, n_ev)
+            L.kvc_scissor_update(t, valid, hist, counts, evict_idx=idx)
+        torch.cuda.synchronize()
+        pg = probs.cpu().numpy()
+        hist_now = hist.cpu().numpy()
+        cnt = counts.cpu().numpy().view(np.uint16).astype(np.int64)
+        ref_p = O.window_scores(O_bf16(q), k64, valid=v_before, reduce=0, causal=False)
+        check_scores(pg, ref_p, f"step {t} probs")
+        for b in range(B):
+            for g in range(Hkv):
+                bg = b * Hkv + g
+                cache = O.ScissorhandsCache(1, 1, C, hist_len)
+                cache.valid[0, 0] = v_before[b, g].astype(bool)
+                cache.attn_history[0, 0] = unpack_planes(hist_before, bg, C)
+                cache.attn_counter = t
+                low = cache.update_attn_history(ref_p[b, g][None, None])[0, 0]
+                got = unpack_planes(hist_now, bg, C)[:, t % hist_len].astype(bool)
+                n_valid = v_before[b, g].sum()
+                near = np.abs(ref_p[b, g] * n_valid - 1.0) <= 1e-5
+                assert np.array_equal(got[~near], low[~near]), f"step {t} bg {bg} low bits"
+                # the GPU's counts are the popcount of its own planes
+                assert np.array_equal(cnt[b, g], unpack_planes(hist_now, bg, C).sum(axis=1))
+                if evict:
+                    cache.attn_history[0, 0] = unpack_planes(hist_now, bg, C)
+                    fr = cache.low_fraction()[0, 0]
+                    fg = frac.cpu().numpy()[b, g]
+                    assert np.array_equal(np.isinf(fg), np.isinf(fr))
+                    fin = np.isfinite(fr)
+                    assert np.allclose(fg[fin], fr[fin], rtol=1e-6, atol=0)
+                    want = O.topk_select(fr[None], n_ev)[0]
+                    assert np.array_equal(idx.cpu().numpy()[b, g], want), f"step {t} evictions"
+                    v_exp = v_before[b, g].copy()
+                    v_exp[want] = 0
+                    assert np.array_equal(valid.cpu().numpy()[b, g], v_exp)
+
+
+def O_bf16(bits):
+    return synth.stored_to_f64(bits, "bf16")
+
+
+def test_snapkv_path_small_end_to_end():
+    """window scores -> top-k with the window forced -> gather, one small layer."""
+    say("snapkv end-to-end small")
+    p = synth.snapkv(0, S=1500, w=64, H=32, Hkv=8, D=128)
+    L = lib()
+    q, k, v = dev(p.q, "bf16"), dev(p.k, "bf16"), dev(p.v, "bf16")
+    s = L.kvc_window_scores(q, k, reduce=0, causal=True)
+    idx = L.kvc_topk_select(s, 256, n_tail=64)
+    ko, vo = L.kvc_gather_compact(k, v, idx)
+    torch.cuda.synchronize()
+    ref_s, _ = O.snapkv(p.q64(), p.k64(), 256)
+    check_scores(s.cpu().numpy(), ref_s)
+    check_kept(idx.cpu().numpy(), s.cpu().numpy(), ref_s, 256, 64)
+    check_gather(ko, vo, p.k, p.v, idx.cpu().numpy())
