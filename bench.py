@@ -1,0 +1,234 @@
+"""Throughput of the KV-cache scoring-and-pruning path on one MI355X.
+
+Workload: SnapKV prefill on a Llama-3-8B-shaped layer (batch 1, 32 query heads,
+8 KV heads, head_dim 128, S = 32768 cached positions, a 64-query observation
+window that is always kept, 4096 positions kept per KV head), bf16 N(0,1) Q/K/V
+with 1% of the prefix keys scaled by 4.  One step runs the whole path on each of
+8 distinct layers: window scores -> top-k with the window forced -> gather of
+the kept K/V.  The layers together (1.07 GB of K/V) exceed the 256 MB Infinity
+Cache, so every layer's keys come from HBM.
+
+Prints one JSON line.  value = KV tokens scored and pruned per second per layer
+(B * S * layers * steps / elapsed).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV tokens scored+pruned/s per layer (32k ctx, GQA 32/8) + % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_window_scores_snapkv_32k.json")
+SCORE_SOURCES = ["window_scores.hip", "kvc_device.h", "kvc_plan.h"]
+
+
+def score_kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        with open(os.path.join(ROOT, "kv_cache_compression_window_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--streams", type=int, default=2, help="layers are spread round-robin over this many streams")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work budget of the oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is data-parallel per "
+              f"(batch, KV head) and is not sharded here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_compression_window_amd import binding as L
+    from kv_cache_compression_window_amd import configs, synth
+
+    cfg = configs.SNAPKV_32K
+    B, H, Hkv, S, D, w, keep = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.w, cfg.keep
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t0 = time.time()
+    layers = []
+    for layer in range(args.layers):
+        p = synth.snapkv(layer)
+        layers.append(dict(q=up(p.q), k=up(p.k), v=up(p.v)))
+        if layer == 0:
+            host0 = p
+    gen_s = time.time() - t0
+    print(f"[bench] generated {args.layers} layers in {gen_s:.1f}s", file=sys.stderr, flush=True)
+
+    streams = [torch.cuda.Stream(device=dev) for _ in range(args.streams)]
+    ws_bytes = L.window_scores_ws_bytes(B, H, Hkv, S, D, w)
+    for i, ly in enumerate(layers):
+        ly["stream"] = streams[i % len(streams)]
+        ly["scores"] = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
+        ly["idx"] = torch.empty((B, Hkv, keep), dtype=torch.int32, device=dev)
+        ly["k_out"] = torch.empty((B, Hkv, keep, D), dtype=torch.bfloat16, device=dev)
+        ly["v_out"] = torch.empty((B, Hkv, keep, D), dtype=torch.bfloat16, device=dev)
+        ly["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        ly["tk_ws"] = torch.empty(256, dtype=torch.uint8, device=dev)
+
+        st = ly["stream"]
+        ly["score_call"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st,
+                                                reduce=L.KVC_REDUCE_GROUP, causal=True)
+        ly["topk_call"] = L.bind_topk_select(ly["scores"], keep, w, ly["idx"], ly["tk_ws"], st)
+        ly["gather_call"] = L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st)
+
+    def run_layer(ly, ev=None):
+        st = ly["stream"]
+        if ev is not None:
+            ev[0].record(st)
+        ly["score_call"]()
+        if ev is not None:
+            ev[1].record(st)
+        ly["topk_call"]()
+        ly["gather_call"]()
+
+    def step(evs=None):
+        # the streams start after everything queued on the default stream
+        cur = torch.cuda.current_stream(dev)
+        for st in streams:
+            st.wait_stream(cur)
+        for i, ly in enumerate(layers):
+            run_layer(ly, None if evs is None else evs[i])
+        for st in streams:
+            cur.wait_stream(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps between a synchronisation on each side; the score
+    # call of every layer is bracketed by HIP events on its own stream
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in layers] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    elapsed_ms = start.elapsed_time(end)
+    score_us = float(np.mean([a.elapsed_time(b) for row in evs for (a, b) in row])) * 1e3
+
+    tokens = B * S * args.layers * args.steps
+    value = tokens / (elapsed_ms * 1e-3)
+    t_layer_us = elapsed_ms * 1e3 / (args.layers * args.steps)
+    # algorithmic bytes per layer: K read once, Q read, scores written and read
+    # by the top-k, indices written and read, kept K and V read and written
+    k_bytes = B * Hkv * S * D * 2
+    q_bytes = B * H * w * D * 2
+    s_bytes = B * Hkv * S * 4
+    i_bytes = B * Hkv * keep * 4
+    g_bytes = 2 * 2 * B * Hkv * keep * D * 2
+    layer_bytes = k_bytes + q_bytes + 2 * s_bytes + 2 * i_bytes + g_bytes
+    hbm_frac = layer_bytes / (HBM_PEAK_GBS * 1e9) / (t_layer_us * 1e-6)
+
+    # dominant step: the window scores (pass 1, merge, pass 2)
+    score_bytes = k_bytes + q_bytes + s_bytes
+    achieved = score_bytes / (score_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_hash") == score_kernel_hash():
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "kvc_window_scores (pass 1 + merge + pass 2)", "avg_us": round(score_us, 2),
+                "algorithmic_bytes": score_bytes}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host0, keep, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep,
+                   "layers_per_step": args.layers, "streams": args.streams, "us_per_layer": round(t_layer_us, 3),
+                   "algorithmic_bytes_per_layer": layer_bytes, "hbm_roofline_frac": round(hbm_frac, 4),
+                   "wall_s": round(wall, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(p, keep, budget_s):
+    """The fp64 oracle (unchanged) on whole KV heads of one layer of the same
+    workload, until about budget_s seconds of CPU work; tokens/s per layer."""
+    from oracle import kvc_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q64, k64 = p.q64(), p.k64()
+    G = p.H // p.Hkv
+    done_heads = 0
+    t0 = time.perf_counter()
+    while True:
+        g = done_heads % p.Hkv
+        qg = q64[:, g * G:(g + 1) * G]
+        kg = k64[:, g:g + 1]
+        s, idx = O.snapkv(qg, kg, keep)
+        O.gather_compact(p.k[:, g:g + 1], p.v[:, g:g + 1], idx)
+        done_heads += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    # one KV head is 1/Hkv of a layer's work on all S positions
+    tokens = p.B * p.S * done_heads / p.Hkv
+    return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done_heads} KV heads (of {p.Hkv} per layer) of layer 0, S={p.S}, fp64 numpy oracle, "
+                      f"{el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

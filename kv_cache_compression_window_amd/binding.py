@@ -212,3 +212,55 @@ def kvc_gather_compact(k, v, idx, chan_idx=None, k_out=None, v_out=None, stream=
                                                         n_keep, _ptr(chan_idx), d_keep, _ptr(k_out), _ptr(v_out),
                                                         _stream(stream)))
     return k_out, v_out
+
+
+# ----------------------------------------------------------------------------
+# Pre-bound calls: marshal the arguments once and return a function that makes
+# the C call with them (one foreign call per use).  For loops that launch the
+# same call on the same buffers many times.
+# ----------------------------------------------------------------------------
+
+def _bound(fn_name, args):
+    f = getattr(LIB, fn_name)
+
+    def call():
+        st = f(*args)
+        if st != 0:
+            _check(fn_name, st)
+
+    return call
+
+
+def bind_window_scores(q, k, scores, ws, stream, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, causal=True):
+    _need(q, "q_win", 4)
+    _need(k, "k", 4)
+    sh = _shape(q, k)
+    d_keep = 0 if chan_idx is None else chan_idx.shape[2]
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    args = (ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid), _ptr(chan_idx), d_keep, reduce,
+            int(causal), _ptr(scores), _ptr(ws), ctypes.byref(n), ctypes.c_void_p(stream.cuda_stream))
+    call = _bound("kvc_window_scores", args)
+    call.keep_alive = (sh, n, q, k, valid, chan_idx, scores, ws)
+    return call
+
+
+def bind_topk_select(scores, k, n_tail, idx, ws, stream):
+    n = scores.shape[-1]
+    rows = scores.numel() // n
+    nb = ctypes.c_size_t(ws.numel() * ws.element_size())
+    args = (_ptr(scores), rows, n, k, n_tail, _ptr(idx), _ptr(ws), ctypes.byref(nb),
+            ctypes.c_void_p(stream.cuda_stream))
+    call = _bound("kvc_topk_select", args)
+    call.keep_alive = (nb, scores, idx, ws)
+    return call
+
+
+def bind_gather_compact(k, v, idx, k_out, v_out, stream, chan_idx=None):
+    B, Hkv, S, D = k.shape
+    sh = KvcShape(B, Hkv, Hkv, S, D, 1)
+    d_keep = 0 if chan_idx is None else chan_idx.shape[2]
+    args = (ctypes.byref(sh), _dtype_code(k), _ptr(k), _ptr(v), _ptr(idx), idx.shape[2], _ptr(chan_idx), d_keep,
+            _ptr(k_out), _ptr(v_out), ctypes.c_void_p(stream.cuda_stream))
+    call = _bound("kvc_gather_compact", args)
+    call.keep_alive = (sh, k, v, idx, chan_idx, k_out, v_out)
+    return call

@@ -6,7 +6,9 @@
 
 namespace kvc {
 
-constexpr int kTileKeys = 64;  // keys per LDS tile in the window-score kernels
+// Key granularity of the window-score chunks: the two-pass kernels use 128-key
+// tiles, the stored-logits kernel 64-key tiles; chunks are multiples of both.
+constexpr int kTileKeys = 128;
 
 // How kvc_window_scores runs a given shape.
 //  * two-pass path (rows per KV head R > 16): pass 1 computes per-row (max, sum
@@ -18,8 +20,9 @@ constexpr int kTileKeys = 64;  // keys per LDS tile in the window-score kernels
 //    read from HBM once.
 struct WsPlan {
   bool store;       // stored-logits path
-  int NW, RB;       // waves per workgroup, 32-row blocks per wave
-  int R, Rpad;      // rows per KV head (G*w) and padded rows (NW*RB*32)
+  int NW;           // waves per workgroup: one wave per 32 query rows
+  int R, Rpad;      // rows per KV head (G*w) and padded rows (nrch * NW * 32)
+  int nrch;         // row chunks of NW*32 rows (several only when R > 256)
   int CH, nchunks;  // keys per chunk (multiple of kTileKeys) and chunks per (b,g)
   int Spad;         // row stride of the stored logits (multiple of kTileKeys)
   size_t off_part, off_lse, off_logits, bytes;
@@ -27,21 +30,24 @@ struct WsPlan {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kMaxRows = 1024;  // G*w limit per KV head
+
 inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, WsPlan* p) {
   const int G = H / Hkv;
   const long long R = (long long)G * w;
-  if (R > 512) return false;
+  if (R > kMaxRows) return false;
   p->R = (int)R;
   p->store = R <= 16;
+  // one wave per 32 query rows, up to 8 waves; beyond 256 rows the rows are
+  // processed in chunks of 256 by successive launches
   const int nrb = (int)((R + 31) / 32);
-  if (nrb <= 1) { p->NW = 1; p->RB = 1; }
-  else if (nrb == 2) { p->NW = 2; p->RB = 1; }
-  else if (nrb <= 4) { p->NW = 4; p->RB = 1; }
-  else if (nrb <= 8) { p->NW = 4; p->RB = 2; }
-  else { p->NW = 4; p->RB = 4; }
-  p->Rpad = p->NW * p->RB * 32;
+  p->NW = nrb <= 1 ? 1 : nrb == 2 ? 2 : nrb <= 4 ? 4 : 8;
+  p->nrch = (nrb + p->NW - 1) / p->NW;
+  p->Rpad = p->nrch * p->NW * 32;
   const long long bg = (long long)B * Hkv;
-  const long long target = p->store ? 4096 : 1024;  // workgroups to aim for
+  // workgroups to aim for: about eight waves per CU on the two-pass path, many
+  // one-wave workgroups on the (HBM-bound) stored-logits path
+  const long long target = p->store ? 4096 : 256LL * 8 / p->NW;
   long long nch = (target + bg - 1) / bg;
   const long long max_ch = (S + kTileKeys - 1) / kTileKeys;
   if (nch > max_ch) nch = max_ch;

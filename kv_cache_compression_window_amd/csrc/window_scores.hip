@@ -13,18 +13,27 @@
 // i < w.  They are contiguous in q_win, so row r = (h - g*G)*w + i is at
 // q_win + ((b*Hkv + g)*R + r)*D.
 //
-// Kernels:
-//   pass 1  MFMA A = key block (32 keys), B = query block (32 rows); each lane
-//           holds 16 keys of one query row, so the per-row running max and
-//           sum of exp2 stay in the lane.  It writes (max, sum) per row and chunk.
-//           The stored-logits variant also writes the scaled logits.
+// Two passes over the keys, each a 32x32x16 bf16 (or 32x32x2 fp32) MFMA
+// contraction of 32-row query blocks with 32-key blocks:
+//   stats   MFMA A = key block, B = query block.  Each lane holds 16 keys of one
+//           query row, so the row's running max and sum of exp2 stay in the lane.
+//           Writes (max, sum) per row and key chunk; the stored-logits variant
+//           also writes the scaled logits.
 //   merge   combines the chunk partials into a base-2 log-normaliser per row.
-//   pass 2  MFMA A = query block, B = key block; each lane holds 16 rows of one
-//           key, so the column sums of exp2(l*c - lse2) stay in the lane.  The
-//           waves' sums are added in a fixed order in LDS and written as scores.
+//   scores  MFMA A = query block, B = key block.  Each lane holds 16 rows of one
+//           key, so the column sums of exp2(l*c - lse2) stay in the lane; the
+//           partial sums of the waves are added in a fixed order in LDS.
 //   from_logits  (stored-logits path) normalises the stored logits and sums them.
 //   all_heads    (TOVA) sums the group sums over the KV heads and repeats them.
-// All sums are in a fixed order, so the results are deterministic.
+// All sums run in a fixed order, so the results are deterministic.
+//
+// Multi-wave workgroups (one wave per 32 query rows, up to 256 rows per launch)
+// run a continuous stream of 32-key blocks: while the exp work of block b runs
+// on the VALU, the MFMAs of block b+1 run on the matrix cores and the K
+// fragments of block b+2 are read from LDS.  K tiles pass through a three-tile
+// LDS ring (the next tile is already resident when a tile ends) fed by one tile
+// of staging registers.  One-wave workgroups (at most 32 rows) keep a simple
+// two-stage loop: they serve the HBM-bound decode shapes.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
@@ -32,34 +41,31 @@ namespace kvc {
 
 namespace {
 
-constexpr int TK = kTileKeys;  // keys per tile
-constexpr int KB = TK / 32;    // 32-key blocks per tile
-
-enum { MODE_STATS = 0, MODE_STATS_STORE = 1, MODE_SCORES = 2 };
-
 struct WsParams {
   const void* q;
   const void* k;
   const uint8_t* valid;
   const int32_t* chan_idx;
-  int Hkv, S, w, R, Rpad, d_keep, causal, CH, nchunks, Spad;
-  float c;            // log2(e) / sqrt(D)
-  float out_scale;    // pass 2: 1/(G*w) for GROUP, 1 for ALL_HEADS (normalised later)
-  float2* part;       // [B*Hkv*Rpad*nchunks] (max, sum of exp2) in base-2 units
-  float* lse;         // [B*Hkv*Rpad] base-2 log-normaliser (+inf for empty/padded rows)
-  float* logits;      // [B*Hkv*R*Spad] scaled logits (stored-logits path)
-  float* scores;      // [B*Hkv*S]
+  int Hkv, S, w, R, Rpad, d_keep, causal, CH, nchunks, Spad, rows_total;
+  int row0;        // first row of the current row chunk
+  int accumulate;  // scores pass: add to the scores already written
+  float c;         // log2(e) / sqrt(D)
+  float out_scale; // scores: 1/(G*w) for GROUP, 1 for ALL_HEADS (normalised later)
+  float2* part;    // [nchunks][B*Hkv*Rpad] (max, sum of exp2) in base-2 units
+  float* lse;      // [B*Hkv*Rpad] base-2 log-normaliser (+inf for empty or padded rows)
+  float* logits;   // [B*Hkv*R*Spad] scaled logits (stored-logits path)
+  float* scores;   // [B*Hkv*S]
 };
 
 template <typename T, int D>
 struct TileGeom {
   static constexpr int E = sizeof(T);
-  static constexpr int HALF = D / 2;               // channels per lane half
+  static constexpr int HALF = D / 2;                 // channels per lane half
   static constexpr int NSTEP = HALF / Mfma<T>::KPL;  // MFMA steps per block
-  static constexpr int ROWB = D * E;               // bytes per key row
-  static constexpr int LSTRIDE = ROWB + 16;        // padded LDS row stride
-  static constexpr int UPR = ROWB / 16;            // 16-byte units per row
-  static constexpr int FRAGU = HALF * E / 16;      // 16-byte units per lane fragment
+  static constexpr int ROWB = D * E;                 // bytes per key row
+  static constexpr int LSTRIDE = ROWB + 16;          // padded LDS row stride
+  static constexpr int UPR = ROWB / 16;              // 16-byte units per row
+  static constexpr int FRAGU = HALF * E / 16;        // 16-byte units per lane fragment
 };
 
 template <typename T, int D>
@@ -68,99 +74,25 @@ union Frag {
   typename Mfma<T>::op_t o[TileGeom<T, D>::NSTEP];
 };
 
-template <typename T, int D, int NW, int RB, int MODE>
-__global__ __launch_bounds__(NW * 64) void ws_pass_kernel(WsParams p) {
-  using M = Mfma<T>;
+// Keys per LDS tile of the stream kernels: 128 when a key row is at most 256
+// bytes and eight waves share the tile, else 64 (the ring of three tiles must
+// fit in LDS).
+template <typename T, int D, int NW>
+struct StreamTK {
+  static constexpr int value = (NW >= 8 && D * (int)sizeof(T) <= 256) ? 128 : 64;
+};
+
+// K tile staging: contiguous global rows -> registers -> padded LDS rows.
+template <typename T, int D, int NT, int TK>
+struct Stager {
   using G_ = TileGeom<T, D>;
-  constexpr int NT = NW * 64;
-  constexpr int UPT = TK * G_::UPR / NT;
+  static constexpr int UPT = TK * G_::UPR / NT;
   static_assert((TK * G_::UPR) % NT == 0, "tile units must split evenly");
-  constexpr bool STATS = MODE != MODE_SCORES;
-
-  __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TK * G_::LSTRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_valid[2][TK];
-  __shared__ float lds_red[2][NW][TK];
-  __shared__ uint32_t lds_keep[D / 32];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int half = lane >> 5;
-  const int col = lane & 31;
-  const int chunk = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const size_t bg = (size_t)b * p.Hkv + g;
-  const int key0 = chunk * p.CH;
-  const int key1 = min(p.S, key0 + p.CH);
-  const int ntiles = (key1 - key0 + TK - 1) / TK;
-  const bool has_valid = p.valid != nullptr;
-
-  // ---- kept key channels (ThinK) as a bit mask --------------------------------
-  if (p.chan_idx) {
-    if (tid < D / 32) lds_keep[tid] = 0u;
-    __syncthreads();
-    for (int i = tid; i < p.d_keep; i += NT) {
-      const int ch = p.chan_idx[bg * p.d_keep + i];
-      if (ch >= 0 && ch < D) atomicOr(&lds_keep[ch >> 5], 1u << (ch & 31));
-    }
-    __syncthreads();
-  }
-
-  // ---- query fragments of this wave's row blocks (kept in registers) ----------
-  Frag<T, D> qf[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = (wave * RB + rb) * 32 + col;
-    if (r < p.R) {
-      const uint4* src = reinterpret_cast<const uint4*>(
-          reinterpret_cast<const unsigned char*>(p.q) + ((bg * p.R + r) * D + half * G_::HALF) * G_::E);
-#pragma unroll
-      for (int u = 0; u < G_::FRAGU; ++u) qf[rb].u[u] = src[u];
-      if (p.chan_idx) {
-#pragma unroll
-        for (int s = 0; s < G_::NSTEP; ++s) {
-#pragma unroll
-          for (int e = 0; e < M::KPL; ++e) {
-            const int d = half * G_::HALF + s * M::KPL + e;
-            if (!((lds_keep[d >> 5] >> (d & 31)) & 1u)) {
-              if constexpr (M::KPL == 1) qf[rb].o[s] = 0.0f;
-              else qf[rb].o[s][e] = (__bf16)0.0f;
-            }
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < G_::FRAGU; ++u) qf[rb].u[u] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-
-  // ---- per-lane state ----------------------------------------------------------
-  float m_run[RB], z_run[RB];  // pass 1: running max (base-2 units) and sum of exp2
-  int win_row[RB];             // pass 1: window row of this lane's query row
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = kNegInf;
-    z_run[rb] = 0.0f;
-    const int r = (wave * RB + rb) * 32 + col;
-    win_row[rb] = (r < p.R) ? (r % p.w) : 0;
-  }
-  float nb[RB][16];  // pass 2: minus the log-normaliser of each accumulator row
-  if constexpr (!STATS) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        nb[rb][v] = -p.lse[bg * p.Rpad + (wave * RB + rb) * 32 + acc_row(v, lane)];
-  }
-
-  // ---- tile loader: contiguous global rows -> padded LDS rows -------------------
+  static_assert(TK <= NT, "one validity byte per thread");
   uint4 pre[UPT];
-  uint8_t pre_valid = 0;
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
-  auto load_tile = [&](int t) {
-    const int base = key0 + t * TK;
+  uint8_t pre_valid;
+
+  __device__ inline void load(const unsigned char* kbase, const uint8_t* vrow, int base, int key1, int tid) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * NT;
@@ -171,191 +103,492 @@ __global__ __launch_bounds__(NW * 64) void ws_pass_kernel(WsParams p) {
       else
         pre[i] = make_uint4(0u, 0u, 0u, 0u);
     }
-    if (has_valid && tid < TK) {
-      const int key = base + tid;
-      pre_valid = (key < key1) ? p.valid[bg * p.S + key] : (uint8_t)0;
-    }
-  };
-  auto store_tile = [&](int buf) {
+    if (vrow && tid < TK) pre_valid = (base + tid < key1) ? vrow[base + tid] : (uint8_t)0;
+  }
+  __device__ inline void store(unsigned char* lds_k, uint8_t* lds_v, int tid, bool has_valid) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * NT;
       const int row = u / G_::UPR, cu = u % G_::UPR;
-      *reinterpret_cast<uint4*>(&lds_k[buf][row * G_::LSTRIDE + cu * 16]) = pre[i];
+      *reinterpret_cast<uint4*>(lds_k + row * G_::LSTRIDE + cu * 16) = pre[i];
     }
-    if (has_valid && tid < TK) lds_valid[buf][tid] = pre_valid;
-  };
-
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+    if (has_valid && tid < TK) lds_v[tid] = pre_valid;
   }
-  __syncthreads();
+};
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int base = key0 + t * TK;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    // Masking is needed only on tiles with holes, a ragged end, or keys past the
-    // causal limit of the first window row (S - w).
-    const bool need_mask = has_valid || (base + TK > p.S) || (p.causal && p.w > 1 && base + TK - 1 > p.S - p.w);
+template <typename T, int D>
+__device__ inline void read_frag(Frag<T, D>& f, const unsigned char* tile, int key_in_tile, int half) {
+  using G_ = TileGeom<T, D>;
+  const uint4* src = reinterpret_cast<const uint4*>(tile + key_in_tile * G_::LSTRIDE + half * G_::HALF * G_::E);
+#pragma unroll
+  for (int u = 0; u < G_::FRAGU; ++u) f.u[u] = src[u];
+}
 
-    if constexpr (STATS) {
-      f32x16_t acc[KB][RB];
+template <typename T, int D>
+__device__ inline f32x16_t mma_block(const Frag<T, D>& a, const Frag<T, D>& b) {
+  f32x16_t acc = {};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        Frag<T, D> kf;
-        const unsigned char* rowp = &lds_k[buf][(kb * 32 + col) * G_::LSTRIDE + half * G_::HALF * G_::E];
+  for (int s = 0; s < TileGeom<T, D>::NSTEP; ++s) acc = Mfma<T>::run(a.o[s], b.o[s], acc);
+  return acc;
+}
+
+// Query fragment of one row (zero for padded rows); channels not in the keep
+// mask are zeroed.
+template <typename T, int D>
+__device__ inline void load_query(Frag<T, D>& qf, const WsParams& p, size_t bg, int r, int half,
+                                  const uint32_t* keep) {
+  using M = Mfma<T>;
+  using G_ = TileGeom<T, D>;
+  if (r < p.R) {
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(p.q) +
+                                                      ((bg * p.R + r) * D + half * G_::HALF) * G_::E);
 #pragma unroll
-        for (int u = 0; u < G_::FRAGU; ++u) kf.u[u] = reinterpret_cast<const uint4*>(rowp)[u];
+    for (int u = 0; u < G_::FRAGU; ++u) qf.u[u] = src[u];
+    if (keep) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          f32x16_t a = {};
+      for (int s = 0; s < G_::NSTEP; ++s) {
 #pragma unroll
-          for (int s = 0; s < G_::NSTEP; ++s) a = M::run(kf.o[s], qf[rb].o[s], a);
-          acc[kb][rb] = a;
-        }
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (need_mask) {
-          // Branch-free: the keys of accumulator registers 4*v4 .. 4*v4+3 are four
-          // consecutive keys, so their validity bytes come in one 32-bit LDS word.
-          const int lim = min(p.S - 1, p.causal ? (p.S - p.w + win_row[rb]) : (p.S - 1));
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-              const int kk0 = kb * 32 + 8 * v4 + 4 * half;
-              const uint32_t vw =
-                  has_valid ? *reinterpret_cast<const uint32_t*>(&lds_valid[buf][kk0]) : 0x01010101u;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const bool ok = (base + kk0 + e <= lim) & (((vw >> (8 * e)) & 0xFFu) != 0u);
-                acc[kb][rb][4 * v4 + e] = ok ? acc[kb][rb][4 * v4 + e] : kNegInf;
-              }
-            }
-        }
-        if constexpr (MODE == MODE_STATS_STORE) {
-          const int r = (wave * RB + rb) * 32 + col;
-          if (r < p.R) {
-            float* dst = p.logits + (bg * p.R + r) * (size_t)p.Spad + base;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-              for (int v4 = 0; v4 < 4; ++v4) {
-                float4 o;
-                o.x = acc[kb][rb][4 * v4 + 0] * p.c;
-                o.y = acc[kb][rb][4 * v4 + 1] * p.c;
-                o.z = acc[kb][rb][4 * v4 + 2] * p.c;
-                o.w = acc[kb][rb][4 * v4 + 3] * p.c;
-                *reinterpret_cast<float4*>(dst + kb * 32 + 8 * v4 + 4 * half) = o;
-              }
+        for (int e = 0; e < M::KPL; ++e) {
+          const int d = half * G_::HALF + s * M::KPL + e;
+          if (!((keep[d >> 5] >> (d & 31)) & 1u)) {
+            if constexpr (M::KPL == 1) qf.o[s] = 0.0f;
+            else qf.o[s][e] = (__bf16)0.0f;
           }
         }
-        float tmax = kNegInf;
+      }
+    }
+  } else {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+    for (int u = 0; u < G_::FRAGU; ++u) qf.u[u] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Bit mask of the kept key channels of (b, g) (ThinK), built in LDS.
+template <int D, int NT>
+__device__ inline const uint32_t* build_keep(uint32_t* lds_keep, const WsParams& p, size_t bg, int tid) {
+  if (!p.chan_idx) return nullptr;
+  if (tid < D / 32) lds_keep[tid] = 0u;
+  __syncthreads();
+  for (int i = tid; i < p.d_keep; i += NT) {
+    const int ch = p.chan_idx[bg * p.d_keep + i];
+    if (ch >= 0 && ch < D) atomicOr(&lds_keep[ch >> 5], 1u << (ch & 31));
+  }
+  __syncthreads();
+  return lds_keep;
+}
+
+// Minus the log-normalisers of the 16 rows held by a lane's accumulator
+// registers (scores pass layout: rows are the accumulator rows).
+__device__ inline void load_neg_lse(float (&nb)[16], const WsParams& p, size_t bg, int rowblk, int half) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, acc[kb][rb][v]);
-        const float mn = fmaxf(m_run[rb], tmax * p.c);
-        if (mn != kNegInf) {
-          float zs[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int v4 = 0; v4 < 4; ++v4) {
+    const float4 l4 = *reinterpret_cast<const float4*>(p.lse + bg * p.Rpad + rowblk + 8 * v4 + 4 * half);
+    nb[4 * v4 + 0] = -l4.x;
+    nb[4 * v4 + 1] = -l4.y;
+    nb[4 * v4 + 2] = -l4.z;
+    nb[4 * v4 + 3] = -l4.w;
+  }
+}
+
+// Fold the 16 logits of one (query row, 16 keys) lane slice into the lane's
+// running (max, sum exp2).  Keys failing the mask must already be -inf.
+__device__ inline void fold_stats(const f32x16_t& a, float c, float& m_run, float& z_run) {
+  float tmax = fmaxf(a[0], a[1]);
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
+  for (int v = 2; v < 16; v += 2) tmax = fmaxf(fmaxf(tmax, a[v]), a[v + 1]);
+  const float mn = fmaxf(m_run, tmax * c);
+  const float nmn = -mn;
+  float zs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int v = 0; v < 16; ++v) zs[v & 3] += fast_exp2(fmaf(acc[kb][rb][v], p.c, -mn));
-          z_run[rb] = z_run[rb] * fast_exp2(m_run[rb] - mn) + ((zs[0] + zs[1]) + (zs[2] + zs[3]));
-          m_run[rb] = mn;
+  for (int v = 0; v < 16; ++v) zs[v & 3] += fast_exp2(fmaf(a[v], c, nmn));
+  const float znew = z_run * fast_exp2(m_run - mn) + ((zs[0] + zs[1]) + (zs[2] + zs[3]));
+  const bool live = mn != kNegInf;  // a slice with every key masked changes nothing
+  z_run = live ? znew : z_run;
+  m_run = live ? mn : m_run;
+}
+
+// Mask the stats-layout slice: keys above `lim` or holes become -inf.  The keys
+// of registers 4*v4 .. 4*v4+3 are consecutive, so their validity bytes come in one
+// 32-bit LDS word.
+__device__ inline void mask_stats(f32x16_t& a, int key_base, int lim, const uint8_t* lv, bool has_valid, int half) {
+#pragma unroll
+  for (int v4 = 0; v4 < 4; ++v4) {
+    const int kk0 = 8 * v4 + 4 * half;
+    const uint32_t vw = has_valid ? *reinterpret_cast<const uint32_t*>(lv + kk0) : 0x01010101u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = (key_base + kk0 + e <= lim) & (((vw >> (8 * e)) & 0xFFu) != 0u);
+      a[4 * v4 + e] = ok ? a[4 * v4 + e] : kNegInf;
+    }
+  }
+}
+
+template <int NMFMA, int NVALU>
+__device__ inline void interleave_hint() {
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);
+  }
+}
+
+template <bool B>
+using bool_t = std::integral_constant<bool, B>;
+
+// ---------------------------------------------------------------------------
+// Stream kernels (NW = 2, 4, 8 waves; one 32-row block per wave)
+// ---------------------------------------------------------------------------
+
+// The shared skeleton: prologue, tile loop with the three-tile LDS ring, and
+// the block stream.  `mfma(kf)` runs the contraction of one block, `epi(acc, t,
+// kb, masked)` its VALU work, `post(t)` runs after the barrier ending tile t.
+template <typename T, int D, int NW, typename Mma, typename Epi, typename Post>
+__device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* vrow, int key0, int key1,
+                                     int ntiles, bool has_valid, int tid, int col, int half, int S, int w,
+                                     int causal, unsigned char (*lds_k)[StreamTK<T, D, NW>::value * TileGeom<T, D>::LSTRIDE],
+                                     uint8_t (*lds_v)[StreamTK<T, D, NW>::value], Mma mfma, Epi epi, Post post) {
+  constexpr int NT = NW * 64;
+  constexpr int TK = StreamTK<T, D, NW>::value;
+  constexpr int KB = TK / 32;
+  static_assert(KB % 2 == 0, "fragment double buffer alternates within a tile");
+  using G_ = TileGeom<T, D>;
+
+  Stager<T, D, NT, TK> stg;
+  if (ntiles > 0) {
+    stg.load(kbase, vrow, key0, key1, tid);
+    stg.store(lds_k[0], lds_v[0], tid, has_valid);
+  }
+  if (ntiles > 1) {
+    stg.load(kbase, vrow, key0 + TK, key1, tid);
+    stg.store(lds_k[1], lds_v[1], tid, has_valid);
+  }
+  if (ntiles > 2) stg.load(kbase, vrow, key0 + 2 * TK, key1, tid);
+  __syncthreads();
+  if (ntiles <= 0) return;
+
+  Frag<T, D> kf[2];
+  read_frag<T, D>(kf[0], lds_k[0], col, half);
+  read_frag<T, D>(kf[1], lds_k[0], 32 + col, half);
+  f32x16_t acc = mfma(kf[0]);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int base = key0 + t * TK;
+    const bool masked = has_valid || (base + TK > S) || (causal && base + TK - 1 > S - w);
+    const unsigned char* next_tile = lds_k[(t + 1) % 3];
+    const unsigned char* this_tile = lds_k[t % 3];
+
+    auto run = [&](auto masked_tag, auto last_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      constexpr bool LAST = decltype(last_tag)::value;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int cur = kb & 1;
+        // K fragment of block kb+2 (possibly in the next tile) into the buffer
+        // the MFMAs of block kb have consumed
+        if (!LAST || kb + 2 < KB) {
+          const unsigned char* src = (kb + 2 < KB) ? this_tile : next_tile;
+          read_frag<T, D>(kf[cur], src, ((kb + 2) % KB) * 32 + col, half);
         }
+        f32x16_t nxt;
+        if (!LAST || kb + 1 < KB) nxt = mfma(kf[cur ^ 1]);
+        epi(acc, t, kb, MASKED);
+        if constexpr (!MASKED) interleave_hint<G_::NSTEP, 6>();
+        __builtin_amdgcn_sched_barrier(0);
+        if (!LAST || kb + 1 < KB) acc = nxt;
+      }
+    };
+    if (t + 1 < ntiles) {
+      if (masked) run(bool_t<true>(), bool_t<false>());
+      else run(bool_t<false>(), bool_t<false>());
+    } else {
+      if (masked) run(bool_t<true>(), bool_t<true>());
+      else run(bool_t<false>(), bool_t<true>());
+    }
+
+    if (t + 2 < ntiles) stg.store(lds_k[(t + 2) % 3], lds_v[(t + 2) % 3], tid, has_valid);
+    __syncthreads();
+    post(t);
+    if (t + 3 < ntiles) stg.load(kbase, vrow, base + 3 * TK, key1, tid);
+  }
+}
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
+  using G_ = TileGeom<T, D>;
+  constexpr int NT = NW * 64;
+  constexpr int TK = StreamTK<T, D, NW>::value;
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k[3][TK * G_::LSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_valid[3][TK];
+  __shared__ uint32_t lds_keep[D / 32];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int chunk = blockIdx.x;
+  const size_t bg = (size_t)blockIdx.z * p.Hkv + blockIdx.y;
+  const int key0 = chunk * p.CH;
+  const int key1 = min(p.S, key0 + p.CH);
+  const int ntiles = (key1 - key0 + TK - 1) / TK;
+  const bool has_valid = p.valid != nullptr;
+  const uint8_t* vrow = has_valid ? p.valid + bg * p.S : nullptr;
+
+  const uint32_t* keep = build_keep<D, NT>(lds_keep, p, bg, tid);
+  const int r = p.row0 + wave * 32 + col;  // this lane's query row
+  Frag<T, D> qf;
+  load_query<T, D>(qf, p, bg, r, half, keep);
+  int lim = p.S - 1;
+  if (p.causal && r < p.R) lim = min(p.S - 1, p.S - p.w + r % p.w);
+  float m_run = kNegInf, z_run = 0.0f;
+
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
+  auto mfma = [&](const Frag<T, D>& kf) { return mma_block<T, D>(kf, qf); };
+  auto epi = [&](f32x16_t& a, int t, int kb, bool masked) {
+    if (masked) mask_stats(a, key0 + t * TK + kb * 32, lim, &lds_valid[t % 3][kb * 32], has_valid, half);
+    fold_stats(a, p.c, m_run, z_run);
+  };
+  stream_blocks<T, D, NW>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal, lds_k,
+                          lds_valid, mfma, epi, [](int) {});
+
+  const float m2 = __shfl_xor(m_run, 32);
+  const float z2 = __shfl_xor(z_run, 32);
+  lse2_merge(m_run, z_run, m2, z2);
+  if (half == 0) p.part[(size_t)chunk * p.rows_total + bg * p.Rpad + r] = make_float2(m_run, z_run);
+}
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
+  using G_ = TileGeom<T, D>;
+  constexpr int NT = NW * 64;
+  constexpr int TK = StreamTK<T, D, NW>::value;
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k[3][TK * G_::LSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_valid[3][TK];
+  __shared__ float lds_red[3][2 * NW][TK];
+  __shared__ uint32_t lds_keep[D / 32];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int chunk = blockIdx.x;
+  const size_t bg = (size_t)blockIdx.z * p.Hkv + blockIdx.y;
+  const int key0 = chunk * p.CH;
+  const int key1 = min(p.S, key0 + p.CH);
+  const int ntiles = (key1 - key0 + TK - 1) / TK;
+  const bool has_valid = p.valid != nullptr;
+  const uint8_t* vrow = has_valid ? p.valid + bg * p.S : nullptr;
+
+  const uint32_t* keep = build_keep<D, NT>(lds_keep, p, bg, tid);
+  const int rowblk = p.row0 + wave * 32;
+  Frag<T, D> qf;
+  load_query<T, D>(qf, p, bg, rowblk + col, half, keep);
+  float nb[16];
+  load_neg_lse(nb, p, bg, rowblk, half);
+
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
+  auto mfma = [&](const Frag<T, D>& kf) { return mma_block<T, D>(qf, kf); };
+  auto epi = [&](f32x16_t& a, int t, int kb, bool masked) {
+    float cs[4] = {0.f, 0.f, 0.f, 0.f};
+    if (masked) {
+      const int key = key0 + t * TK + kb * 32 + col;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = rowblk + acc_row(v, lane);
+        const int i = (r < p.R) ? (r % p.w) : 0;
+        const float e = fast_exp2(fmaf(a[v], p.c, nb[v]));
+        cs[v & 3] += (!p.causal || key <= p.S - p.w + i) ? e : 0.0f;
       }
     } else {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        Frag<T, D> kf;
-        const unsigned char* rowp = &lds_k[buf][(kb * 32 + col) * G_::LSTRIDE + half * G_::HALF * G_::E];
+      for (int v = 0; v < 16; ++v) cs[v & 3] += fast_exp2(fmaf(a[v], p.c, nb[v]));
+    }
+    // both lane halves publish their partial (16 of the 32 rows each)
+    lds_red[t % 3][2 * wave + half][kb * 32 + col] = (cs[0] + cs[1]) + (cs[2] + cs[3]);
+  };
+  // after the barrier ending tile t: add the partials of every wave and lane half
+  // in a fixed order; holes score 0
+  auto post = [&](int t) {
+    if (tid < TK) {
+      const int key = key0 + t * TK + tid;
+      if (key < key1) {
+        float s = 0.0f;
 #pragma unroll
-        for (int u = 0; u < G_::FRAGU; ++u) kf.u[u] = reinterpret_cast<const uint4*>(rowp)[u];
-        float cs[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < 2 * NW; ++h) s += lds_red[t % 3][h][tid];
+        if (has_valid && !lds_valid[t % 3][tid]) s = 0.0f;
+        s *= p.out_scale;
+        float* dst = p.scores + bg * p.S + key;
+        *dst = p.accumulate ? *dst + s : s;
+      }
+    }
+  };
+  stream_blocks<T, D, NW>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal, lds_k,
+                          lds_valid, mfma, epi, post);
+}
+
+// ---------------------------------------------------------------------------
+// One-wave kernels (at most 32 rows): two-stage staging, block by block
+// ---------------------------------------------------------------------------
+constexpr int kWaveTK = 64;
+
+template <typename T, int D, bool STORE>
+__global__ __launch_bounds__(64) void ws_stats_wave_kernel(WsParams p) {
+  using G_ = TileGeom<T, D>;
+  constexpr int TK = kWaveTK, KB = TK / 32;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TK * G_::LSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_valid[2][TK];
+  __shared__ uint32_t lds_keep[D / 32];
+
+  const int tid = threadIdx.x, lane = tid, half = lane >> 5, col = lane & 31;
+  const int chunk = blockIdx.x;
+  const size_t bg = (size_t)blockIdx.z * p.Hkv + blockIdx.y;
+  const int key0 = chunk * p.CH;
+  const int key1 = min(p.S, key0 + p.CH);
+  const int ntiles = (key1 - key0 + TK - 1) / TK;
+  const bool has_valid = p.valid != nullptr;
+  const uint8_t* vrow = has_valid ? p.valid + bg * p.S : nullptr;
+
+  const uint32_t* keep = build_keep<D, 64>(lds_keep, p, bg, tid);
+  const int r = col;
+  Frag<T, D> qf;
+  load_query<T, D>(qf, p, bg, r, half, keep);
+  int lim = p.S - 1;
+  if (p.causal && r < p.R) lim = min(p.S - 1, p.S - p.w + r % p.w);
+  float m_run = kNegInf, z_run = 0.0f;
+
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
+  Stager<T, D, 64, TK> stg;
+  if (ntiles > 0) {
+    stg.load(kbase, vrow, key0, key1, tid);
+    stg.store(lds_k[0], lds_valid[0], tid, has_valid);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int base = key0 + t * TK;
+    if (t + 1 < ntiles) stg.load(kbase, vrow, base + TK, key1, tid);
+    const bool masked = has_valid || (base + TK > p.S) || (p.causal && base + TK - 1 > p.S - p.w);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          f32x16_t a = {};
+    for (int kb = 0; kb < KB; ++kb) {
+      Frag<T, D> kf;
+      read_frag<T, D>(kf, lds_k[buf], kb * 32 + col, half);
+      f32x16_t a = mma_block<T, D>(kf, qf);
+      if (masked) mask_stats(a, base + kb * 32, lim, &lds_valid[buf][kb * 32], has_valid, half);
+      if constexpr (STORE) {
+        if (r < p.R) {
+          float* dst = p.logits + (bg * p.R + r) * (size_t)p.Spad + base + kb * 32 + 4 * half;
 #pragma unroll
-          for (int s = 0; s < G_::NSTEP; ++s) a = M::run(qf[rb].o[s], kf.o[s], a);
-          if (need_mask && p.causal && p.w > 1) {
-            const int key = base + kb * 32 + col;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int r = (wave * RB + rb) * 32 + acc_row(v, lane);
-              const int i = (r < p.R) ? (r % p.w) : 0;
-              float e = fast_exp2(fmaf(a[v], p.c, nb[rb][v]));
-              cs[v & 3] += (key <= p.S - p.w + i) ? e : 0.0f;
-            }
-          } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) cs[v & 3] += fast_exp2(fmaf(a[v], p.c, nb[rb][v]));
+          for (int v4 = 0; v4 < 4; ++v4) {
+            float4 o;
+            o.x = a[4 * v4 + 0] * p.c;
+            o.y = a[4 * v4 + 1] * p.c;
+            o.z = a[4 * v4 + 2] * p.c;
+            o.w = a[4 * v4 + 3] * p.c;
+            *reinterpret_cast<float4*>(dst + 8 * v4) = o;
           }
         }
-        float csum = (cs[0] + cs[1]) + (cs[2] + cs[3]);
-        csum += __shfl_xor(csum, 32);
-        if (has_valid && !lds_valid[buf][kb * 32 + col]) csum = 0.0f;
-        if (half == 0) lds_red[buf][wave][kb * 32 + col] = csum;
       }
+      fold_stats(a, p.c, m_run, z_run);
     }
-
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    if (t + 1 < ntiles) stg.store(lds_k[buf ^ 1], lds_valid[buf ^ 1], tid, has_valid);
     __syncthreads();
-
-    if constexpr (!STATS) {
-      if (tid < TK) {
-        const int key = base + tid;
-        if (key < key1) {
-          float s = 0.0f;
-#pragma unroll
-          for (int wv = 0; wv < NW; ++wv) s += lds_red[buf][wv][tid];
-          p.scores[bg * p.S + key] = s * p.out_scale;
-        }
-      }
-    }
   }
+  const float m2 = __shfl_xor(m_run, 32);
+  const float z2 = __shfl_xor(z_run, 32);
+  lse2_merge(m_run, z_run, m2, z2);
+  if (half == 0) p.part[(size_t)chunk * p.rows_total + bg * p.Rpad + r] = make_float2(m_run, z_run);
+}
 
-  if constexpr (STATS) {
+template <typename T, int D>
+__global__ __launch_bounds__(64) void ws_scores_wave_kernel(WsParams p) {
+  using G_ = TileGeom<T, D>;
+  constexpr int TK = kWaveTK, KB = TK / 32;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TK * G_::LSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_valid[2][TK];
+  __shared__ float lds_red[2][2][TK];
+  __shared__ uint32_t lds_keep[D / 32];
+
+  const int tid = threadIdx.x, lane = tid, half = lane >> 5, col = lane & 31;
+  const int chunk = blockIdx.x;
+  const size_t bg = (size_t)blockIdx.z * p.Hkv + blockIdx.y;
+  const int key0 = chunk * p.CH;
+  const int key1 = min(p.S, key0 + p.CH);
+  const int ntiles = (key1 - key0 + TK - 1) / TK;
+  const bool has_valid = p.valid != nullptr;
+  const uint8_t* vrow = has_valid ? p.valid + bg * p.S : nullptr;
+
+  const uint32_t* keep = build_keep<D, 64>(lds_keep, p, bg, tid);
+  Frag<T, D> qf;
+  load_query<T, D>(qf, p, bg, col, half, keep);
+  float nb[16];
+  load_neg_lse(nb, p, bg, 0, half);
+
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
+  Stager<T, D, 64, TK> stg;
+  if (ntiles > 0) {
+    stg.load(kbase, vrow, key0, key1, tid);
+    stg.store(lds_k[0], lds_valid[0], tid, has_valid);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int base = key0 + t * TK;
+    if (t + 1 < ntiles) stg.load(kbase, vrow, base + TK, key1, tid);
+    const bool causal_tile = p.causal && base + TK - 1 > p.S - p.w;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float m2 = __shfl_xor(m_run[rb], 32);
-      const float z2 = __shfl_xor(z_run[rb], 32);
-      lse2_merge(m_run[rb], z_run[rb], m2, z2);
-      if (half == 0) {
-        const int r = (wave * RB + rb) * 32 + col;
-        p.part[(bg * p.Rpad + r) * p.nchunks + chunk] = make_float2(m_run[rb], z_run[rb]);
+    for (int kb = 0; kb < KB; ++kb) {
+      Frag<T, D> kf;
+      read_frag<T, D>(kf, lds_k[buf], kb * 32 + col, half);
+      f32x16_t a = mma_block<T, D>(qf, kf);
+      float cs[4] = {0.f, 0.f, 0.f, 0.f};
+      const int key = base + kb * 32 + col;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float e = fast_exp2(fmaf(a[v], p.c, nb[v]));
+        const int rr = acc_row(v, lane);
+        cs[v & 3] += (!causal_tile || rr >= p.R || key <= p.S - p.w + rr % p.w) ? e : 0.0f;
+      }
+      lds_red[buf][half][kb * 32 + col] = (cs[0] + cs[1]) + (cs[2] + cs[3]);
+    }
+    if (t + 1 < ntiles) stg.store(lds_k[buf ^ 1], lds_valid[buf ^ 1], tid, has_valid);
+    __syncthreads();
+    {
+      const int key = base + tid;
+      if (key < key1) {
+        float s = lds_red[buf][0][tid] + lds_red[buf][1][tid];
+        if (has_valid && !lds_valid[buf][tid]) s = 0.0f;
+        p.scores[bg * p.S + key] = s * p.out_scale;
       }
     }
   }
 }
 
-// Per row: combine the chunk partials into lse2 = max + log2(sum).  Rows past R
-// (padding) and rows with no allowed key get +inf, so their probabilities are 0.
-__global__ void ws_merge_kernel(const float2* __restrict__ part, float* __restrict__ lse, int total,
-                                int Rpad, int R, int nchunks) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int r = idx % Rpad;
-  if (r >= R) {
-    lse[idx] = kPosInf;
-    return;
-  }
+// Per row: combine the chunk partials into lse2 = max + log2(sum).  Sixteen
+// lanes share a row (each takes every 16th chunk) and combine by a fixed
+// butterfly.  Rows past R (padding) and rows with no allowed key get +inf, so
+// their probabilities are 0.
+__global__ __launch_bounds__(256) void ws_merge_kernel(const float2* __restrict__ part, float* __restrict__ lse,
+                                                       int rows_total, int Rpad, int R, int nchunks) {
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
   float m = kNegInf, z = 0.0f;
-  for (int c = 0; c < nchunks; ++c) {
-    const float2 pc = part[(size_t)idx * nchunks + c];
-    lse2_merge(m, z, pc.x, pc.y);
+  if (row < rows_total) {
+    for (int c = sub; c < nchunks; c += 16) {
+      const float2 pc = part[(size_t)c * rows_total + row];
+      lse2_merge(m, z, pc.x, pc.y);
+    }
   }
-  lse[idx] = (m == kNegInf || !(z > 0.0f)) ? kPosInf : m + log2f(z);
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const float z2 = __shfl_xor(z, o);
+    lse2_merge(m, z, m2, z2);
+  }
+  if (row < rows_total && sub == 0) {
+    const int r = row % Rpad;
+    lse[row] = (r >= R || m == kNegInf || !(z > 0.0f)) ? kPosInf : m + log2f(z);
+  }
 }
 
 // Stored-logits path: s[b,g,j] = scale * sum over the rows of exp2(logit - lse2).
 __global__ void ws_from_logits_kernel(const float* __restrict__ logits, const float* __restrict__ lse,
-                                      float* __restrict__ scores, int Hkv, int S, int Spad, int R,
-                                      int Rpad, int all_heads, float scale) {
+                                      float* __restrict__ scores, int Hkv, int S, int Spad, int R, int Rpad,
+                                      int all_heads, float scale) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= S) return;
   const int b = blockIdx.z;
@@ -389,37 +622,27 @@ __global__ void ws_all_heads_kernel(float* __restrict__ scores, int Hkv, int S, 
   for (int g = 0; g < Hkv; ++g) scores[(b * Hkv + g) * S + j] = s;
 }
 
-template <typename T, int D, int NW, int RB>
-void launch_passes(const WsParams& p, const WsPlan& plan, dim3 grid, hipStream_t st) {
-  if (plan.store) {
-    if constexpr (NW == 1 && RB == 1) ws_pass_kernel<T, D, 1, 1, MODE_STATS_STORE><<<grid, 64, 0, st>>>(p);
-  } else {
-    ws_pass_kernel<T, D, NW, RB, MODE_STATS><<<grid, NW * 64, 0, st>>>(p);
-  }
-}
-
-template <typename T, int D, int NW, int RB>
-void launch_scores(const WsParams& p, dim3 grid, hipStream_t st) {
-  ws_pass_kernel<T, D, NW, RB, MODE_SCORES><<<grid, NW * 64, 0, st>>>(p);
-}
-
 template <typename T, int D>
-void dispatch(const WsParams& p, const WsPlan& plan, dim3 grid, hipStream_t st, bool scores_pass) {
-  const int key = plan.NW * 10 + plan.RB;
-#define KVC_WS_CASE(NW_, RB_)                                         \
-  case NW_ * 10 + RB_:                                                \
-    if (scores_pass) launch_scores<T, D, NW_, RB_>(p, grid, st);      \
-    else launch_passes<T, D, NW_, RB_>(p, plan, grid, st);            \
-    break;
-  switch (key) {
-    KVC_WS_CASE(1, 1)
-    KVC_WS_CASE(2, 1)
-    KVC_WS_CASE(4, 1)
-    KVC_WS_CASE(4, 2)
-    KVC_WS_CASE(4, 4)
-    default: break;
+void launch_pass(const WsParams& p, const WsPlan& plan, dim3 grid, hipStream_t st, bool scores_pass) {
+  switch (plan.NW) {
+    case 1:
+      if (scores_pass) ws_scores_wave_kernel<T, D><<<grid, 64, 0, st>>>(p);
+      else if (plan.store) ws_stats_wave_kernel<T, D, true><<<grid, 64, 0, st>>>(p);
+      else ws_stats_wave_kernel<T, D, false><<<grid, 64, 0, st>>>(p);
+      break;
+    case 2:
+      if (scores_pass) ws_scores_stream_kernel<T, D, 2><<<grid, 128, 0, st>>>(p);
+      else ws_stats_stream_kernel<T, D, 2><<<grid, 128, 0, st>>>(p);
+      break;
+    case 4:
+      if (scores_pass) ws_scores_stream_kernel<T, D, 4><<<grid, 256, 0, st>>>(p);
+      else ws_stats_stream_kernel<T, D, 4><<<grid, 256, 0, st>>>(p);
+      break;
+    default:
+      if (scores_pass) ws_scores_stream_kernel<T, D, 8><<<grid, 512, 0, st>>>(p);
+      else ws_stats_stream_kernel<T, D, 8><<<grid, 512, 0, st>>>(p);
+      break;
   }
-#undef KVC_WS_CASE
 }
 
 }  // namespace
@@ -440,6 +663,9 @@ hipError_t launch_window_scores(const WsArgs& a, const WsPlan& plan, hipStream_t
   p.CH = plan.CH;
   p.nchunks = plan.nchunks;
   p.Spad = plan.Spad;
+  p.rows_total = a.B * a.Hkv * plan.Rpad;
+  p.row0 = 0;
+  p.accumulate = 0;
   p.c = kLog2e / sqrtf((float)a.D);
   const int G = a.H / a.Hkv;
   p.out_scale = a.reduce ? 1.0f : 1.0f / (float)(G * a.w);
@@ -452,22 +678,30 @@ hipError_t launch_window_scores(const WsArgs& a, const WsPlan& plan, hipStream_t
   const dim3 grid(plan.nchunks, a.Hkv, a.B);
   const bool bf = a.bf16 != 0;
   auto run = [&](bool scores_pass) {
-    if (bf && a.D == 128) dispatch<__bf16, 128>(p, plan, grid, st, scores_pass);
-    else if (bf && a.D == 64) dispatch<__bf16, 64>(p, plan, grid, st, scores_pass);
-    else if (!bf && a.D == 128) dispatch<float, 128>(p, plan, grid, st, scores_pass);
-    else dispatch<float, 64>(p, plan, grid, st, scores_pass);
+    if (bf && a.D == 128) launch_pass<__bf16, 128>(p, plan, grid, st, scores_pass);
+    else if (bf && a.D == 64) launch_pass<__bf16, 64>(p, plan, grid, st, scores_pass);
+    else if (!bf && a.D == 128) launch_pass<float, 128>(p, plan, grid, st, scores_pass);
+    else launch_pass<float, 64>(p, plan, grid, st, scores_pass);
   };
+  const int rows_per_launch = plan.NW * 32;
 
-  run(false);  // pass 1
-  const int total = a.B * a.Hkv * plan.Rpad;
-  ws_merge_kernel<<<(total + 255) / 256, 256, 0, st>>>(p.part, p.lse, total, plan.Rpad, plan.R, plan.nchunks);
+  for (int c = 0; c < plan.nrch; ++c) {  // row statistics (and stored logits)
+    p.row0 = c * rows_per_launch;
+    run(false);
+  }
+  ws_merge_kernel<<<(p.rows_total + 15) / 16, 256, 0, st>>>(p.part, p.lse, p.rows_total, plan.Rpad, plan.R,
+                                                            plan.nchunks);
   const float scale_all = 1.0f / (float)(a.H * a.w);
   if (plan.store) {
     const dim3 g2((a.S + 255) / 256, a.reduce ? 1 : a.Hkv, a.B);
-    ws_from_logits_kernel<<<g2, 256, 0, st>>>(p.logits, p.lse, p.scores, a.Hkv, a.S, plan.Spad, plan.R,
-                                              plan.Rpad, a.reduce, a.reduce ? scale_all : p.out_scale);
+    ws_from_logits_kernel<<<g2, 256, 0, st>>>(p.logits, p.lse, p.scores, a.Hkv, a.S, plan.Spad, plan.R, plan.Rpad,
+                                              a.reduce, a.reduce ? scale_all : p.out_scale);
   } else {
-    run(true);  // pass 2
+    for (int c = 0; c < plan.nrch; ++c) {  // scores, row chunk by row chunk
+      p.row0 = c * rows_per_launch;
+      p.accumulate = c > 0;
+      run(true);
+    }
     if (a.reduce) {
       const dim3 g3((a.S + 255) / 256, 1, a.B);
       ws_all_heads_kernel<<<g3, 256, 0, st>>>(p.scores, a.Hkv, a.S, scale_all);

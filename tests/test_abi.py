@@ -67,7 +67,7 @@ def test_window_scores_validation(lib):
     assert ws_call(lib, S(1, 32, 8, 4096, 128, 0)) == 2        # w
     assert ws_call(lib, S(1, 32, 8, 63, 128, 64)) == 2         # w > S
     assert ws_call(lib, S(1, 32, 8, 4096, 96, 64)) == 6        # D
-    assert ws_call(lib, S(1, 64, 8, 4096, 128, 128)) == 6      # G*w > 512
+    assert ws_call(lib, S(1, 64, 8, 4096, 128, 256)) == 6      # G*w > 1024
     assert ws_call(lib, ok, chan=FAKE, d_keep=0) == 2
     assert ws_call(lib, ok, chan=FAKE, d_keep=129) == 2
     assert ws_call(lib, ok, q=None) == 1
