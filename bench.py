@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8)
-    ap.add_argument("--streams", type=int, default=2, help="layers are spread round-robin over this many streams")
+    ap.add_argument("--streams", type=int, default=1, help="layers are spread round-robin over this many streams")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",

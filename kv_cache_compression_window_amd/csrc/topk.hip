@@ -1,13 +1,27 @@
 // Per-row top-k with a forced tail, kept indices in ascending order (gfx950).
 //
-// One workgroup per row.  Selection is a 4-digit (8-bit) MSB-first radix select
-// on order-preserving uint32 keys of the scores.  It finds the exact threshold key
-// T and how many keys equal to T must be taken.  A compaction pass in index order
-// then emits every key above T and the lowest-indexed keys equal to T, in
-// ascending position order.  That realises the lowest-index tie rule and the
-// ascending output with one deterministic pass.  Rows of up to kLdsKeys eligible
-// entries are cached in LDS as keys; longer rows are re-read from global memory
-// (L2) at every pass.
+// One workgroup of 1024 threads per row.  Scores become order-preserving uint32
+// keys.  Thread t holds the keys of the KPT consecutive positions t*KPT ..
+// t*KPT+KPT-1 of a tile of 1024*KPT positions, so that its kept positions come
+// out in order.  Rows that fit one tile keep their keys in registers for the
+// whole selection; longer rows (KPT = 32) are processed tile by tile and re-read
+// from L2 at every sweep.  Slots past the end of the row hold the row's minimum
+// key: they sit after every real position, so the lowest-index tie rule never
+// takes them, and the hot loops need no bounds test.
+//
+// Selection is an MSB-first radix select on  rel = key - min_key .  Digits of up
+// to 11 bits are taken from bit L-1 of the key range downwards, so the first
+// histogram already spreads the keys over the range they occupy (scores of one
+// row usually share their leading key bits).  Histograms live in LDS in eight
+// interleaved copies picked by lane, so lanes of one wave that fall into one bin
+// spread over eight counters.  The passes yield the exact rel T of the kp-th
+// largest eligible score and the number of keys equal to T that must be taken.
+// The compaction then keeps every key above T and the lowest-indexed keys equal
+// to T: a thread's first output slot is the exclusive scan, over the threads,
+// of its counts of keys > T and == T (one scan of both counts packed into
+// 16-bit halves), and it walks its own positions in order from there.  When
+// every key equal to T is taken (the usual case) one count of keys >= T is
+// enough.
 //
 // Sources: "Implement Scissorhands KV-cache compression & SnapKV prompt
 // compression" (cold-compress PR 11), PR description: SnapKV keeps the
@@ -21,47 +35,116 @@ namespace kvc {
 
 namespace {
 
-constexpr int NTH = 1024;             // threads per row
-constexpr int kLdsKeys = 32768;       // eligible entries cached in LDS
+constexpr int NTH = 1024;  // threads per row
 constexpr int NWAVE = NTH / 64;
+constexpr int DBITS = 11;  // digit width
+constexpr int NBIN = 1 << DBITS;
+constexpr int NCOPY = 8;   // interleaved histogram copies
 
-// Exclusive scan of one uint32 per thread over the workgroup (fixed order).
-__device__ inline uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh_wave, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = x;
+static_assert(NBIN == 2 * NTH, "each thread owns two bins when the threshold bin is searched");
+
+// Padded LDS index used to hand keys loaded in coalesced order (thread t takes
+// positions t, t+1024, ...) to the thread that owns them (t*KPT .. t*KPT+KPT-1):
+// one spare word per 32 keeps both the writes and the reads free of bank
+// conflicts.
+__device__ inline int xpose_idx(int p) { return p + (p >> 5); }
+constexpr int kXposeWords = 33 * NTH;  // padded size of a 32-key-per-thread tile
+
+struct TopkShared {
+  union {
+    uint32_t hist[NBIN * NCOPY];
+    uint32_t xpose[kXposeWords];
+  };
+  alignas(16) uint32_t wave_tot[NWAVE];
+  uint32_t red_min[NWAVE], red_max[NWAVE];
+  uint32_t bucket, krem, bcount;
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave: DPP shifts within rows of
+// 16 lanes, then the broadcasts of lane 15 and lane 31 into the later rows.
+__device__ inline uint32_t wave_inclusive_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+__device__ inline uint32_t wave_min(uint32_t x) {
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) sh_wave[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t w = (lane < NWAVE) ? sh_wave[lane] : 0u;
-    uint32_t wi = w;
+  for (int o = 32; o > 0; o >>= 1) x = min(x, (uint32_t)__shfl_xor(x, o));
+  return x;
+}
+
+__device__ inline uint32_t wave_max(uint32_t x) {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(wi, o);
-      if (lane >= o) wi += y;
-    }
-    if (lane < NWAVE) sh_wave[lane] = wi - w;  // exclusive prefix of the waves
-    if (lane == NWAVE - 1) *total = wi;
+  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor(x, o));
+  return x;
+}
+
+// Sum of the per-wave totals (already in LDS) of the waves before `wave`.
+__device__ inline uint32_t waves_before(const TopkShared& sh, int wave) {
+  const uint4* wt = reinterpret_cast<const uint4*>(sh.wave_tot);
+  uint32_t before = 0u;
+#pragma unroll
+  for (int q = 0; q < NWAVE / 4; ++q) {
+    const uint4 x = wt[q];
+    before += (4 * q < wave ? x.x : 0u) + (4 * q + 1 < wave ? x.y : 0u) + (4 * q + 2 < wave ? x.z : 0u) +
+              (4 * q + 3 < wave ? x.w : 0u);
   }
+  return before;
+}
+
+// Exclusive scan of one value per thread over the workgroup, in thread order,
+// and the workgroup total.  The LDS it uses is free again when it returns.
+__device__ inline uint32_t block_exclusive_scan(TopkShared& sh, uint32_t x, int lane, int wave, uint32_t* total) {
+  const uint32_t winc = wave_inclusive_scan(x);
+  if (lane == 63) sh.wave_tot[wave] = winc;
   __syncthreads();
-  const uint32_t r = sh_wave[wave] + incl - x;
+  const uint32_t r = waves_before(sh, wave) + winc - x;
+  *total = waves_before(sh, NWAVE);
   __syncthreads();
   return r;
 }
 
+// After a histogram pass: the bin where the count of keys, summed from the top
+// bin down, reaches krem.  Thread t owns bins 2047-2t and 2046-2t, so a scan in
+// thread order is a suffix sum over the bins and exactly one thread sees it
+// cross krem.  Leaves the bin, the rank still to take inside it and the bin's
+// count in sh.bucket, sh.krem and sh.bcount.
+__device__ inline void find_bin(TopkShared& sh, uint32_t krem, int tid, int lane, int wave) {
+  const int b_hi = NBIN - 1 - 2 * tid, b_lo = b_hi - 1;
+  const uint4* h = reinterpret_cast<const uint4*>(sh.hist);
+  const uint4 h0 = h[b_hi * 2], h1 = h[b_hi * 2 + 1], h2 = h[b_lo * 2], h3 = h[b_lo * 2 + 1];
+  const uint32_t c_hi = h0.x + h0.y + h0.z + h0.w + h1.x + h1.y + h1.z + h1.w;
+  const uint32_t c_lo = h2.x + h2.y + h2.z + h2.w + h3.x + h3.y + h3.z + h3.w;
+  const uint32_t local = c_hi + c_lo;
+  const uint32_t winc = wave_inclusive_scan(local);
+  if (lane == 63) sh.wave_tot[wave] = winc;
+  __syncthreads();
+  const uint32_t incl = waves_before(sh, wave) + winc, excl = incl - local;
+  if (excl < krem && incl >= krem) {
+    if (excl + c_hi >= krem) {
+      sh.bucket = (uint32_t)b_hi;
+      sh.krem = krem - excl;
+      sh.bcount = c_hi;
+    } else {
+      sh.bucket = (uint32_t)b_lo;
+      sh.krem = krem - excl - c_hi;
+      sh.bcount = c_lo;
+    }
+  }
+  __syncthreads();
+}
+
+template <int KPT, bool RESIDENT>
 __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ scores, int n, int k, int n_tail,
                                                     int32_t* __restrict__ idx) {
-  __shared__ uint32_t keys[kLdsKeys];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_wave[NWAVE];
-  __shared__ uint32_t sh_total;
-  __shared__ uint32_t sh_bucket, sh_krem;
-
-  const int tid = threadIdx.x;
+  constexpr int TILE = NTH * KPT;
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t row = blockIdx.x;
   const float* s = scores + row * (size_t)n;
   int32_t* out = idx + row * (size_t)k;
@@ -75,101 +158,164 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
     return;
   }
 
-  const bool cached = E <= kLdsKeys;
-  if (cached)
-    for (int i = tid; i < E; i += NTH) keys[i] = float_key(s[i]);
-  auto key_at = [&](int i) -> uint32_t { return cached ? keys[i] : float_key(s[i]); };
-
-  uint32_t prefix = 0u, mask = 0u;
-  uint32_t krem = (uint32_t)kp;  // still to take among keys matching the prefix
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0u;
-    __syncthreads();
-    for (int i0 = 0; i0 < E; i0 += NTH) {
-      const int i = i0 + tid;
-      uint32_t u = 0u;
-      bool active = false;
-      if (i < E) {
-        u = key_at(i);
-        active = (u & mask) == prefix;
-      }
-      const uint32_t bkt = (u >> shift) & 255u;
-      // Scores of one row often share their leading key bits, which would make
-      // the lanes of a wave collide on one counter.  The first two distinct
-      // buckets of the wave are therefore added once each by a leader lane;
-      // the rest use one atomic per lane.
+  const int ntiles = RESIDENT ? 1 : (E + TILE - 1) / TILE;
+  const bool vec = (KPT % 4 == 0) && ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
+  uint32_t u[KPT];
+  // keys of this thread's positions in tile t; positions past E read position
+  // E-1 (a duplicate, which leaves the key range unchanged)
+  auto load_keys = [&](int t) {
+    const int p0 = t * TILE + tid * KPT;
+    if (vec && p0 + KPT <= E) {
+      const float4* s4 = reinterpret_cast<const float4*>(s + p0);
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const unsigned long long pend = __ballot(active);
-        if (pend == 0ull) break;
-        const int leader = __ffsll((long long)pend) - 1;
-        const uint32_t lb = __shfl(bkt, leader);
-        const unsigned long long same = __ballot(active && bkt == lb);
-        if ((threadIdx.x & 63) == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
-        if (bkt == lb) active = false;
+      for (int j = 0; j < KPT / 4; ++j) {
+        const float4 f = s4[j];
+        u[4 * j] = float_key(f.x);
+        u[4 * j + 1] = float_key(f.y);
+        u[4 * j + 2] = float_key(f.z);
+        u[4 * j + 3] = float_key(f.w);
       }
-      if (active) atomicAdd(&hist[bkt], 1u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) u[i] = float_key(s[min(p0 + i, E - 1)]);
+    }
+  };
+
+  // key range of the eligible positions
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  if constexpr (RESIDENT) {
+    // coalesced loads, handed over through LDS
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int p = j * NTH + tid;
+      const uint32_t key = float_key(s[min(p, E - 1)]);
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+      sh.xpose[xpose_idx(p)] = key;
     }
     __syncthreads();
-    if (tid < 64) {
-      // lane l owns buckets 255-4l .. 252-4l (descending)
-      const int lane = tid;
-      uint32_t c[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) c[q] = hist[255 - 4 * lane - q];
-      const uint32_t local = c[0] + c[1] + c[2] + c[3];
-      uint32_t incl = local;
+    for (int i = 0; i < KPT; ++i) u[i] = sh.xpose[xpose_idx(tid * KPT + i)];
+  } else {
+    for (int t = 0; t < ntiles; ++t) {
+      load_keys(t);
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
+      for (int i = 0; i < KPT; ++i) {
+        kmin = min(kmin, u[i]);
+        kmax = max(kmax, u[i]);
       }
-      const uint32_t excl = incl - local;
-      const unsigned long long hit = __ballot(incl >= krem);
-      const int first = __ffsll(hit) - 1;  // lowest lane whose suffix count reaches krem
-      if (lane == first) {
-        uint32_t cum = excl;
+    }
+  }
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  if (lane == 0) {
+    sh.red_min[wave] = kmin;
+    sh.red_max[wave] = kmax;
+  }
+  __syncthreads();
+  kmin = sh.red_min[0];
+  kmax = sh.red_max[0];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (cum + c[q] >= krem) {
-            sh_bucket = 255u - 4u * lane - q;
-            sh_krem = krem - cum;
-            break;
-          }
-          cum += c[q];
+  for (int v = 1; v < NWAVE; ++v) {
+    kmin = min(kmin, sh.red_min[v]);
+    kmax = max(kmax, sh.red_max[v]);
+  }
+  const uint32_t range = kmax - kmin;
+  const int L = range == 0u ? 0 : 32 - __clz(range);  // bit length of every rel
+  const int npass = (L + DBITS - 1) / DBITS;
+
+  // from here on u holds rel = key - kmin (same order as the keys); slots past
+  // the row hold 0, the smallest rel
+  auto to_rel = [&](int t) {
+    const int nv = E - (t * TILE + tid * KPT);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) u[i] -= kmin;
+    if (nv < KPT) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        if (i >= nv) u[i] = 0u;
+    }
+  };
+  auto load_rel = [&](int t) {
+    load_keys(t);
+    to_rel(t);
+  };
+  if constexpr (RESIDENT) to_rel(0);
+
+  const int cp = lane & (NCOPY - 1);
+  uint32_t prefix = 0u;                            // fixed high bits of rel(T)
+  uint32_t krem = (uint32_t)kp;                    // still to take among the keys matching the prefix
+  uint32_t last_count = (uint32_t)(ntiles * TILE);  // keys equal to T (all of them when npass == 0)
+  for (int pass = 0; pass < npass; ++pass) {
+    const int hi = L - DBITS * pass;       // bits [hi, 32) of rel are fixed
+    const int shift = max(0, hi - DBITS);  // this digit is bits [shift, hi)
+    const uint32_t fixed = hi >= 32 ? 0u : ~0u << hi;
+#pragma unroll
+    for (int j = 0; j < NBIN * NCOPY / 4 / NTH; ++j)
+      reinterpret_cast<uint4*>(sh.hist)[j * NTH + tid] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      if constexpr (!RESIDENT) load_rel(t);
+      if (pass == 0) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) atomicAdd(&sh.hist[((u[i] >> shift) & (NBIN - 1)) * NCOPY + cp], 1u);
+      } else {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+          if ((u[i] & fixed) == prefix) atomicAdd(&sh.hist[((u[i] >> shift) & (NBIN - 1)) * NCOPY + cp], 1u);
+      }
+    }
+    __syncthreads();
+    find_bin(sh, krem, tid, lane, wave);
+    prefix |= sh.bucket << shift;
+    krem = sh.krem;
+    last_count = sh.bcount;
+  }
+  const uint32_t T = prefix;      // rel of the kp-th largest eligible score
+  const uint32_t take_eq = krem;  // keys equal to T to take, lowest positions first
+  // When T is 0 the pad slots count among the keys equal to T.  They come after
+  // every real position, so they are never taken, but they keep last_count above
+  // take_eq and so select the general compaction.
+  const bool all_eq = last_count == take_eq;
+
+  uint32_t gt_carry = 0u, eq_carry = 0u;  // counts of earlier tiles
+  for (int t = 0; t < ntiles; ++t) {
+    if constexpr (!RESIDENT) load_rel(t);
+    const int p0 = t * TILE + tid * KPT;
+    if (all_eq) {
+      uint32_t c = 0u;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) c += u[i] >= T;
+      uint32_t tot;
+      uint32_t pos = gt_carry + block_exclusive_scan(sh, c, lane, wave, &tot);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        if (u[i] >= T) {
+          if (pos < (uint32_t)kp) out[pos] = p0 + i;  // pos < kp holds; the guard keeps writes in the row
+          ++pos;
         }
       }
-    }
-    __syncthreads();
-    prefix |= sh_bucket << shift;
-    mask |= 255u << shift;
-    krem = sh_krem;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;  // exact key of the kp-th largest
-  const uint32_t take_eq = krem;  // keys equal to T to take, lowest index first
-
-  // ordered compaction: thread tid owns the contiguous segment [j0, j1)
-  // an odd segment length keeps the threads' LDS reads on distinct banks
-  const int seg = ((E + NTH - 1) / NTH) | 1;
-  const int j0 = min(E, tid * seg), j1 = min(E, j0 + seg);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t u = key_at(j);
-    n_gt += u > T;
-    n_eq += u == T;
-  }
-  const uint32_t eq_before = block_exclusive_scan(n_eq, sh_wave, &sh_total);
-  const uint32_t my_eq = (eq_before >= take_eq) ? 0u : min(n_eq, take_eq - eq_before);
-  const uint32_t pos0 = block_exclusive_scan(n_gt + my_eq, sh_wave, &sh_total);
-  uint32_t pos = pos0, eq_taken = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t u = key_at(j);
-    if (u > T || (u == T && eq_taken < my_eq)) {
-      if (pos < (uint32_t)kp) out[pos] = j;  // kp is exact; the guard only keeps writes in the row
-      ++pos;
-      eq_taken += (u == T);
+      gt_carry += tot;
+    } else {
+      uint32_t c = 0u;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) c += (u[i] > T ? 1u : 0u) + (u[i] == T ? 0x10000u : 0u);
+      uint32_t tot;
+      const uint32_t ex = block_exclusive_scan(sh, c, lane, wave, &tot);
+      // a tile holds at most 32768 keys, so neither 16-bit half carries
+      uint32_t gt_before = gt_carry + (ex & 0xFFFFu), eq_before = eq_carry + (ex >> 16);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const bool gt = u[i] > T, eq = u[i] == T;
+        if (gt || (eq && eq_before < take_eq)) {
+          const uint32_t pos = gt_before + min(eq_before, take_eq);
+          if (pos < (uint32_t)kp) out[pos] = p0 + i;  // pos < kp holds; the guard keeps writes in the row
+        }
+        gt_before += gt;
+        eq_before += eq;
+      }
+      gt_carry += tot & 0xFFFFu;
+      eq_carry += tot >> 16;
     }
   }
 }
@@ -177,7 +323,17 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
 }  // namespace
 
 hipError_t launch_topk(const float* scores, int rows, int n, int k, int n_tail, int32_t* idx, hipStream_t st) {
-  topk_kernel<<<rows, NTH, 0, st>>>(scores, n, k, n_tail, idx);
+  const int E = n - n_tail;
+  if (E <= NTH * 4)
+    topk_kernel<4, true><<<rows, NTH, 0, st>>>(scores, n, k, n_tail, idx);
+  else if (E <= NTH * 8)
+    topk_kernel<8, true><<<rows, NTH, 0, st>>>(scores, n, k, n_tail, idx);
+  else if (E <= NTH * 16)
+    topk_kernel<16, true><<<rows, NTH, 0, st>>>(scores, n, k, n_tail, idx);
+  else if (E <= NTH * 32)
+    topk_kernel<32, true><<<rows, NTH, 0, st>>>(scores, n, k, n_tail, idx);
+  else
+    topk_kernel<32, false><<<rows, NTH, 0, st>>>(scores, n, k, n_tail, idx);
   return hipGetLastError();
 }
 
