@@ -45,7 +45,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8)
-    ap.add_argument("--streams", type=int, default=1, help="layers are spread round-robin over this many streams")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="layers are spread round-robin over this many streams in the timed region")
+    ap.add_argument("--kernel-reps", type=int, default=20,
+                    help="passes over the layers in which each score call is timed alone on one stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -96,26 +99,20 @@ def main():
         st = ly["stream"]
         ly["score_call"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st,
                                                 reduce=L.KVC_REDUCE_GROUP, causal=True)
+        ly["score_call0"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], streams[0],
+                                                 reduce=L.KVC_REDUCE_GROUP, causal=True)
         ly["topk_call"] = L.bind_topk_select(ly["scores"], keep, w, ly["idx"], ly["tk_ws"], st)
         ly["gather_call"] = L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st)
 
-    def run_layer(ly, ev=None):
-        st = ly["stream"]
-        if ev is not None:
-            ev[0].record(st)
-        ly["score_call"]()
-        if ev is not None:
-            ev[1].record(st)
-        ly["topk_call"]()
-        ly["gather_call"]()
-
-    def step(evs=None):
+    def step():
         # the streams start after everything queued on the default stream
         cur = torch.cuda.current_stream(dev)
         for st in streams:
             st.wait_stream(cur)
-        for i, ly in enumerate(layers):
-            run_layer(ly, None if evs is None else evs[i])
+        for ly in layers:
+            ly["score_call"]()
+            ly["topk_call"]()
+            ly["gather_call"]()
         for st in streams:
             cur.wait_stream(st)
 
@@ -123,21 +120,33 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps between a synchronisation on each side; the score
-    # call of every layer is bracketed by HIP events on its own stream
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in layers] for _ in range(args.steps)]
+    # timed region: K steps between a synchronisation on each side
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     start.record()
-    for s in range(args.steps):
-        step(evs[s])
+    for _ in range(args.steps):
+        step()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     elapsed_ms = start.elapsed_time(end)
-    score_us = float(np.mean([a.elapsed_time(b) for row in evs for (a, b) in row])) * 1e3
+
+    # the dominant step, the window-score call, timed alone: every call of
+    # kernel-reps passes over the layers runs on one stream between two HIP
+    # events recorded on that stream (nothing else runs meanwhile)
+    st0 = streams[0]
+    st0.wait_stream(torch.cuda.current_stream(dev))
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.kernel_reps * len(layers))]
+    for r in range(args.kernel_reps):
+        for i, ly in enumerate(layers):
+            a, b = kev[r * len(layers) + i]
+            a.record(st0)
+            ly["score_call0"]()
+            b.record(st0)
+    torch.cuda.synchronize()
+    score_us = float(np.mean([a.elapsed_time(b) for (a, b) in kev])) * 1e3
 
     tokens = B * S * args.layers * args.steps
     value = tokens / (elapsed_ms * 1e-3)

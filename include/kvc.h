@@ -66,8 +66,9 @@ typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
 
 typedef enum {
   /* Mean over the G query heads of each GQA group and the w window rows:
-   * SnapKV's window scoring and Scissorhands' attention callback ([COLD]:
-   * "Mean pool over the grouped queries"). */
+   * SnapKV's window scoring and Scissorhands' attention callback ([COLD],
+   * attention-callback hunk: the callback receives the attention averaged over
+   * the query heads that share a KV head). */
   KVC_REDUCE_GROUP = 0,
   /* Mean over all H query heads and the w window rows, the same row written
    * for every KV head ([TOVA]: attn_weights.mean(1) followed by a repeat

@@ -7,7 +7,8 @@ in ``kv_cache_compression_window_amd.synth`` as exact float64 values of the
 stored bf16/fp32 data.
 
 Everything is the plain definition, written with numpy in float64, in the
-order the pages give the steps.  The sources are four web pages:
+order the pages give the steps.  The sources are the three web pages on the
+subject:
 
   [TOVA]    "Add TOVA press" (NVIDIA kvpress pull request 12), review thread.
   [COLD]    "Implement Scissorhands KV-cache compression & SnapKV prompt
@@ -115,7 +116,8 @@ def window_probs(q, k, valid=None, chan_keep=None, causal=True) -> np.ndarray:
 def window_scores(q, k, valid=None, chan_keep=None, reduce=REDUCE_GROUP, causal=True) -> np.ndarray:
     """Per-KV-head token scores [B, Hkv, S].
 
-    GROUP ([COLD] "Mean pool over the grouped queries"; SnapKV scores the
+    GROUP ([COLD] attention-callback hunk: the attention is averaged over the
+    query heads that share a KV head; SnapKV scores the
     prefix with the observation window): s[b,g,j] is the mean of P over the
     G query heads of group g and the w window rows (R4).
     ALL_HEADS ([TOVA] hassidm and SimJeg: attn_weights.mean(1) over all
