@@ -41,6 +41,10 @@ namespace kvc {
 
 namespace {
 
+// Staging registers use a native vector type: a 16-byte struct copied from
+// global memory to LDS would be turned into a memcpy through a stack object.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 struct WsParams {
   const void* q;
   const void* k;
@@ -74,12 +78,18 @@ union Frag {
   typename Mfma<T>::op_t o[TileGeom<T, D>::NSTEP];
 };
 
-// Keys per LDS tile of the stream kernels: 128 when a key row is at most 256
-// bytes and eight waves share the tile, else 64 (the ring of three tiles must
-// fit in LDS).
+// Keys per LDS tile of the stream kernels.
 template <typename T, int D, int NW>
 struct StreamTK {
-  static constexpr int value = (NW >= 8 && D * (int)sizeof(T) <= 256) ? 128 : 64;
+  static constexpr int value = 64;
+};
+
+// Tiles of staging registers of the stream kernels: K tiles are requested that
+// many tiles ahead of the LDS ring, within about 24 registers per thread.
+template <typename T, int D, int NW>
+struct StreamNSTG {
+  static constexpr int UPT = StreamTK<T, D, NW>::value * D * (int)sizeof(T) / 16 / (NW * 64);
+  static constexpr int value = UPT <= 2 ? 3 : UPT <= 3 ? 2 : 1;
 };
 
 // K tile staging: contiguous global rows -> registers -> padded LDS rows.
@@ -89,32 +99,35 @@ struct Stager {
   static constexpr int UPT = TK * G_::UPR / NT;
   static_assert((TK * G_::UPR) % NT == 0, "tile units must split evenly");
   static_assert(TK <= NT, "one validity byte per thread");
-  uint4 pre[UPT];
+  u32x4_t pre[UPT];
   uint8_t pre_valid;
 
+  // Every thread issues the same loads whatever the tile, so the compiler can
+  // count them: rows past key1 read row key1-1 instead (those keys are masked
+  // or discarded downstream), and without a validity mask the byte comes from
+  // the key data and is ignored.
   __device__ inline void load(const unsigned char* kbase, const uint8_t* vrow, int base, int key1, int tid) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * NT;
       const int row = u / G_::UPR, cu = u % G_::UPR;
-      const int key = base + row;
-      if (key < key1)
-        pre[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * G_::ROWB + cu * 16);
-      else
-        pre[i] = make_uint4(0u, 0u, 0u, 0u);
+      const int key = min(base + row, key1 - 1);
+      pre[i] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * G_::ROWB + cu * 16);
     }
-    if (vrow && tid < TK) pre_valid = (base + tid < key1) ? vrow[base + tid] : (uint8_t)0;
+    const uint8_t* vsrc = vrow ? vrow : kbase;
+    pre_valid = vsrc[min(base + (tid % TK), key1 - 1)];
   }
   __device__ inline void store(unsigned char* lds_k, uint8_t* lds_v, int tid, bool has_valid) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * NT;
       const int row = u / G_::UPR, cu = u % G_::UPR;
-      *reinterpret_cast<uint4*>(lds_k + row * G_::LSTRIDE + cu * 16) = pre[i];
+      *reinterpret_cast<u32x4_t*>(lds_k + row * G_::LSTRIDE + cu * 16) = pre[i];
     }
     if (has_valid && tid < TK) lds_v[tid] = pre_valid;
   }
 };
+
 
 template <typename T, int D>
 __device__ inline void read_frag(Frag<T, D>& f, const unsigned char* tile, int key_in_tile, int half) {
@@ -198,9 +211,11 @@ __device__ inline void fold_stats(const f32x16_t& a, float c, float& m_run, floa
   for (int v = 2; v < 16; v += 2) tmax = fmaxf(fmaxf(tmax, a[v]), a[v + 1]);
   const float mn = fmaxf(m_run, tmax * c);
   const float nmn = -mn;
-  float zs[4] = {0.f, 0.f, 0.f, 0.f};
+  float zs[4];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) zs[v & 3] += fast_exp2(fmaf(a[v], c, nmn));
+  for (int v = 0; v < 4; ++v) zs[v] = fast_exp2(fmaf(a[v], c, nmn));
+#pragma unroll
+  for (int v = 4; v < 16; ++v) zs[v & 3] += fast_exp2(fmaf(a[v], c, nmn));
   const float znew = z_run * fast_exp2(m_run - mn) + ((zs[0] + zs[1]) + (zs[2] + zs[3]));
   const bool live = mn != kNegInf;  // a slice with every key masked changes nothing
   z_run = live ? znew : z_run;
@@ -239,9 +254,10 @@ using bool_t = std::integral_constant<bool, B>;
 // Stream kernels (NW = 2, 4, 8 waves; one 32-row block per wave)
 // ---------------------------------------------------------------------------
 
-// The shared skeleton: prologue, tile loop with the three-tile LDS ring, and
-// the block stream.  `mfma(kf)` runs the contraction of one block, `epi(acc, t,
-// kb, masked)` its VALU work, `post(t)` runs after the barrier ending tile t.
+// The shared skeleton: prologue (two tiles into LDS, the next NSTG into the
+// staging registers), tile loop with the three-tile LDS ring, and the block
+// stream.  `mfma(kf)` runs the contraction of one block, `epi(acc, t, kb,
+// masked)` its VALU work, `post(t)` runs after the barrier ending tile t.
 template <typename T, int D, int NW, typename Mma, typename Epi, typename Post>
 __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* vrow, int key0, int key1,
                                      int ntiles, bool has_valid, int tid, int col, int half, int S, int w,
@@ -249,20 +265,27 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
                                      uint8_t (*lds_v)[StreamTK<T, D, NW>::value], Mma mfma, Epi epi, Post post) {
   constexpr int NT = NW * 64;
   constexpr int TK = StreamTK<T, D, NW>::value;
+  constexpr int NSTG = StreamNSTG<T, D, NW>::value;
   constexpr int KB = TK / 32;
   static_assert(KB % 2 == 0, "fragment double buffer alternates within a tile");
   using G_ = TileGeom<T, D>;
+  using Stg = Stager<T, D, NT, TK>;
 
-  Stager<T, D, NT, TK> stg;
+  static_assert(NSTG >= 1 && NSTG <= 3, "one to three staging sets");
+  Stg s0, s1, s2;  // the staging sets (s1, s2 unused with fewer)
   if (ntiles > 0) {
-    stg.load(kbase, vrow, key0, key1, tid);
-    stg.store(lds_k[0], lds_v[0], tid, has_valid);
+    s0.load(kbase, vrow, key0, key1, tid);
+    s0.store(lds_k[0], lds_v[0], tid, has_valid);
   }
   if (ntiles > 1) {
-    stg.load(kbase, vrow, key0 + TK, key1, tid);
-    stg.store(lds_k[1], lds_v[1], tid, has_valid);
+    s0.load(kbase, vrow, key0 + TK, key1, tid);
+    s0.store(lds_k[1], lds_v[1], tid, has_valid);
   }
-  if (ntiles > 2) stg.load(kbase, vrow, key0 + 2 * TK, key1, tid);
+  if (ntiles > 2) s0.load(kbase, vrow, key0 + 2 * TK, key1, tid);
+  if constexpr (NSTG > 1)
+    if (ntiles > 3) s1.load(kbase, vrow, key0 + 3 * TK, key1, tid);
+  if constexpr (NSTG > 2)
+    if (ntiles > 4) s2.load(kbase, vrow, key0 + 4 * TK, key1, tid);
   __syncthreads();
   if (ntiles <= 0) return;
 
@@ -271,7 +294,10 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
   read_frag<T, D>(kf[1], lds_k[0], 32 + col, half);
   f32x16_t acc = mfma(kf[0]);
 
-  for (int t = 0; t < ntiles; ++t) {
+  // tile t; `st` holds tile t+2 and is refilled with tile t+2+NSTG.  FULL: both
+  // tiles exist, so the store and the load are unconditional.
+  auto tile = [&](int t, Stg& st, auto full_tag) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int base = key0 + t * TK;
     const bool masked = has_valid || (base + TK > S) || (causal && base + TK - 1 > S - w);
     const unsigned char* next_tile = lds_k[(t + 1) % 3];
@@ -305,10 +331,23 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
       else run(bool_t<false>(), bool_t<true>());
     }
 
-    if (t + 2 < ntiles) stg.store(lds_k[(t + 2) % 3], lds_v[(t + 2) % 3], tid, has_valid);
+    if (FULL || t + 2 < ntiles) st.store(lds_k[(t + 2) % 3], lds_v[(t + 2) % 3], tid, has_valid);
     __syncthreads();
     post(t);
-    if (t + 3 < ntiles) stg.load(kbase, vrow, base + 3 * TK, key1, tid);
+    if (FULL || t + 2 + NSTG < ntiles) st.load(kbase, vrow, base + (2 + NSTG) * TK, key1, tid);
+  };
+  int t = 0;
+  for (; t + 2 * NSTG + 1 < ntiles; t += NSTG) {  // steady state
+    tile(t, s0, bool_t<true>());
+    if constexpr (NSTG > 1) tile(t + 1, s1, bool_t<true>());
+    if constexpr (NSTG > 2) tile(t + 2, s2, bool_t<true>());
+  }
+  for (; t < ntiles; t += NSTG) {
+    tile(t, s0, bool_t<false>());
+    if constexpr (NSTG > 1)
+      if (t + 1 < ntiles) tile(t + 1, s1, bool_t<false>());
+    if constexpr (NSTG > 2)
+      if (t + 2 < ntiles) tile(t + 2, s2, bool_t<false>());
   }
 }
 
@@ -384,7 +423,7 @@ __global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
   auto mfma = [&](const Frag<T, D>& kf) { return mma_block<T, D>(qf, kf); };
   auto epi = [&](f32x16_t& a, int t, int kb, bool masked) {
-    float cs[4] = {0.f, 0.f, 0.f, 0.f};
+    float cs[4];
     if (masked) {
       const int key = key0 + t * TK + kb * 32 + col;
 #pragma unroll
@@ -392,11 +431,14 @@ __global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
         const int r = rowblk + acc_row(v, lane);
         const int i = (r < p.R) ? (r % p.w) : 0;
         const float e = fast_exp2(fmaf(a[v], p.c, nb[v]));
-        cs[v & 3] += (!p.causal || key <= p.S - p.w + i) ? e : 0.0f;
+        const float x = (!p.causal || key <= p.S - p.w + i) ? e : 0.0f;
+        cs[v & 3] = v < 4 ? x : cs[v & 3] + x;
       }
     } else {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) cs[v & 3] += fast_exp2(fmaf(a[v], p.c, nb[v]));
+      for (int v = 0; v < 4; ++v) cs[v] = fast_exp2(fmaf(a[v], p.c, nb[v]));
+#pragma unroll
+      for (int v = 4; v < 16; ++v) cs[v & 3] += fast_exp2(fmaf(a[v], p.c, nb[v]));
     }
     // both lane halves publish their partial (16 of the 32 rows each)
     lds_red[t % 3][2 * wave + half][kb * 32 + col] = (cs[0] + cs[1]) + (cs[2] + cs[3]);

@@ -1,7 +1,7 @@
 """GPU parity of every C-ABI call against the fp64 oracle (small shapes).
 
 The shapes span every kernel variant: the stored-logits path (G*w <= 16), the
-two-pass path with 1, 2 and 4 waves and 1, 2 and 4 row blocks per wave, several
+two-pass path with 1, 2, 4 and 8 waves of 32 rows and row chunks, several
 key tiles and chunks with ragged ends, D = 64 and 128, fp32 and bf16, holes,
 channel masks, causal windows and both reductions.
 """
@@ -46,6 +46,14 @@ CASES = [
     ("two_pass_r512", 1, 64, 8, 513, 128, 64, "bf16", 0, 1, 0.0, 0, 1.0),
     ("two_pass_s_eq_w", 1, 8, 2, 40, 64, 40, "bf16", 0, 1, 0.0, 0, 1.0),
     ("two_pass_g1", 1, 4, 4, 260, 128, 32, "bf16", 0, 1, 0.0, 0, 1.0),
+    ("stream_r128", 1, 16, 4, 1200, 128, 32, "bf16", 0, 1, 0.0, 0, 1.0),
+    # eight-wave kernels: partial row blocks, row chunks, D = 64 with holes and
+    # channels, fewer tiles than staging sets, many tiles per chunk
+    ("w8_r200_causal", 1, 16, 4, 3000, 128, 50, "bf16", 0, 1, 0.0, 0, 1.0),
+    ("w8_r400_chunks", 1, 16, 4, 1500, 128, 100, "bf16", 0, 1, 0.0, 0, 1.0),
+    ("w8_d64_holes_chan", 2, 32, 8, 900, 64, 64, "bf16", 0, 1, 0.2, 32, 1.0),
+    ("w8_short_s70", 1, 32, 8, 70, 128, 64, "bf16", 0, 1, 0.0, 0, 1.0),
+    ("w8_long_s9000_allheads", 1, 8, 2, 9000, 128, 64, "bf16", 1, 1, 0.0, 0, 2.0),
 ]
 
 
