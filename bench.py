@@ -1,15 +1,20 @@
 """Throughput of the KV-cache scoring-and-pruning path on one MI355X.
 
-Workload: SnapKV prefill on a Llama-3-8B-shaped layer (batch 1, 32 query heads,
-8 KV heads, head_dim 128, S = 32768 cached positions, a 64-query observation
-window that is always kept, 4096 positions kept per KV head), bf16 N(0,1) Q/K/V
-with 1% of the prefix keys scaled by 4.  One step runs the whole path on each of
-8 distinct layers: window scores -> top-k with the window forced -> gather of
-the kept K/V.  The layers together (1.07 GB of K/V) exceed the 256 MB Infinity
-Cache, so every layer's keys come from HBM.
+Default workload (the one the metric is quoted on): SnapKV prefill on a
+Llama-3-8B-shaped layer (batch 1, 32 query heads, 8 KV heads, head_dim 128,
+S = 32768 cached positions, a 64-query observation window that is always kept,
+4096 positions kept per KV head), bf16 N(0,1) Q/K/V with 1% of the prefix keys
+scaled by 4.  One step runs the whole path on each of 8 distinct layers: window
+scores -> top-k with the window forced -> gather of the kept K/V.  The layers
+together (1.07 GB of K/V) exceed the 256 MB Infinity Cache, so every layer's
+keys come from HBM.
+
+--workload selects one of the other four workloads instead (TOVA tiny, TOVA
+batched, Scissorhands decode, ThinK + SnapKV at 128k); each prints the same kind
+of line with its own metric.
 
 Prints one JSON line.  value = KV tokens scored and pruned per second per layer
-(B * S * layers * steps / elapsed).
+(B * S * layers * steps / elapsed; token-steps for the decode workload).
 """
 from __future__ import annotations
 
@@ -29,6 +34,9 @@ METRIC = "KV tokens scored+pruned/s per layer (32k ctx, GQA 32/8) + % of HBM roo
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_window_scores_snapkv_32k.json")
 SCORE_SOURCES = ["window_scores.hip", "kvc_device.h", "kvc_plan.h"]
+WORKLOADS = ["snapkv_32k", "tova_tiny", "tova_batched", "scissor_decode", "think_128k"]
+DEFAULT_STEPS = {"snapkv_32k": (100, 10), "tova_tiny": (200, 20), "tova_batched": (20, 3),
+                 "scissor_decode": (800, 0), "think_128k": (10, 2)}
 
 
 def score_kernel_hash() -> str:
@@ -42,18 +50,359 @@ def score_kernel_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--workload", default="snapkv_32k", choices=WORKLOADS)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None, help="distinct layers rotated per step")
     ap.add_argument("--streams", type=int, default=2,
                     help="layers are spread round-robin over this many streams in the timed region")
     ap.add_argument("--kernel-reps", type=int, default=20,
-                    help="passes over the layers in which each score call is timed alone on one stream")
+                    help="passes over the layers in which each call of the dominant kernel is timed alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
-    return ap.parse_args()
+    a = ap.parse_args()
+    st, wu = DEFAULT_STEPS[a.workload]
+    a.steps = st if a.steps is None else a.steps
+    a.warmup = wu if a.warmup is None else a.warmup
+    return a
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1]))
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def timed_oracle(fn, budget_s):
+    """Run fn(n) for n = 0, 1, ... for about budget_s seconds; (calls, seconds)."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        fn(n)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return n, el
+
+
+class Ctx:
+    def __init__(self, args):
+        import torch
+
+        from kv_cache_compression_window_amd import binding, configs, synth
+        self.args, self.torch, self.L, self.configs, self.synth = args, torch, binding, configs, synth
+        self.dev = torch.device("cuda:0")
+        self.streams = [torch.cuda.Stream(device=self.dev) for _ in range(args.streams)]
+
+    def up(self, a, dtype="bf16"):
+        t = self.torch
+        if dtype == "bf16":
+            return t.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(t.bfloat16).to(self.dev)
+        return t.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+
+    def empty(self, shape, dtype):
+        return self.torch.empty(shape, dtype=dtype, device=self.dev)
+
+
+# ---------------------------------------------------------------------------
+# Workloads.  Each returns a dict:
+#   step()            one step of the timed region (all layers)
+#   reset()           optional: restore the initial state before a timed run
+#   units_per_step    tokens (or token-steps) per step, summed over the layers
+#   layers            distinct layers per step
+#   layer_bytes       algorithmic HBM bytes per layer and step
+#   kernel            (label, [calls on stream 0], algorithmic bytes per call, traffic)
+#   cpu(budget)       oracle baseline dict
+#   config            extra config keys
+# ---------------------------------------------------------------------------
+
+def wl_snapkv_32k(c: Ctx) -> dict:
+    L, torch, cfg = c.L, c.torch, c.configs.SNAPKV_32K
+    B, H, Hkv, S, D, w, keep = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.w, cfg.keep
+    nl = c.args.layers or cfg.layers
+    layers, host0 = [], None
+    for layer in range(nl):
+        p = c.synth.snapkv(layer)
+        layers.append(dict(q=c.up(p.q), k=c.up(p.k), v=c.up(p.v)))
+        host0 = host0 or p
+    ws_bytes = L.window_scores_ws_bytes(B, H, Hkv, S, D, w)
+    s0 = c.streams[0]
+    for i, ly in enumerate(layers):
+        st = c.streams[i % len(c.streams)]
+        ly["scores"] = c.empty((B, Hkv, S), torch.float32)
+        ly["idx"] = c.empty((B, Hkv, keep), torch.int32)
+        ly["k_out"] = c.empty((B, Hkv, keep, D), torch.bfloat16)
+        ly["v_out"] = c.empty((B, Hkv, keep, D), torch.bfloat16)
+        ly["ws"] = c.empty(ws_bytes, torch.uint8)
+        ly["tk_ws"] = c.empty(256, torch.uint8)
+        ly["calls"] = [L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st, reduce=L.KVC_REDUCE_GROUP,
+                                            causal=True),
+                       L.bind_topk_select(ly["scores"], keep, w, ly["idx"], ly["tk_ws"], st),
+                       L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st)]
+        ly["kcall"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], s0, reduce=L.KVC_REDUCE_GROUP,
+                                           causal=True)
+
+    def step():
+        for ly in layers:
+            for f in ly["calls"]:
+                f()
+
+    # algorithmic bytes per layer: K read once, Q read, scores written and read
+    # by the top-k, indices written and read, kept K and V read and written
+    k_bytes, q_bytes, s_bytes = B * Hkv * S * D * 2, B * H * w * D * 2, B * Hkv * S * 4
+    i_bytes, g_bytes = B * Hkv * keep * 4, 2 * 2 * B * Hkv * keep * D * 2
+    layer_bytes = k_bytes + q_bytes + 2 * s_bytes + 2 * i_bytes + g_bytes
+
+    def cpu(budget):
+        from oracle import kvc_oracle as O
+        q64, k64 = host0.q64(), host0.k64()
+        G = H // Hkv
+
+        def one(n):
+            g = n % Hkv
+            s, idx = O.snapkv(q64[:, g * G:(g + 1) * G], k64[:, g:g + 1], keep)
+            O.gather_compact(host0.k[:, g:g + 1], host0.v[:, g:g + 1], idx)
+        n, el = timed_oracle(one, budget)
+        # one KV head is 1/Hkv of a layer's work on all S positions
+        return {"value": round(B * S * n / Hkv / el, 1), "unit": "tokens/s", "cores": blas_threads(),
+                "kind": "oracle", "sample": f"{n} KV heads (of {Hkv} per layer) of layer 0, S={S}, fp64 numpy "
+                                            f"oracle (scores, top-k, gather), {el:.1f} s"}
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_hash") == score_kernel_hash():
+            traffic = tr.get("bytes_per_launch")
+    return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes,
+                kernel=("kvc_window_scores (pass 1 + merge + pass 2)", [ly["kcall"] for ly in layers],
+                        k_bytes + q_bytes + s_bytes, traffic),
+                cpu=cpu, metric=METRIC, unit="tokens/s", dtype="bf16", workload=cfg.name,
+                config={"B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep})
+
+
+def wl_tova(c: Ctx, cfg, gen, dtype, tdtype) -> dict:
+    L, torch = c.L, c.torch
+    B, H, Hkv, S, D, w, keep = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.w, cfg.keep
+    esz = 2 if dtype == "bf16" else 4
+    nl = c.args.layers or cfg.layers
+    layers, host0 = [], None
+    for layer in range(nl):
+        p = gen(layer)
+        layers.append(dict(q=c.up(p.q, dtype), k=c.up(p.k, dtype), v=c.up(p.v, dtype)))
+        host0 = host0 or p
+    ws_bytes = L.window_scores_ws_bytes(B, H, Hkv, S, D, w, L.KVC_BF16 if dtype == "bf16" else L.KVC_F32)
+    s0 = c.streams[0]
+    for i, ly in enumerate(layers):
+        st = c.streams[i % len(c.streams)]
+        ly["scores"] = c.empty((B, Hkv, S), torch.float32)
+        ly["idx"] = c.empty((B, Hkv, keep), torch.int32)
+        ly["k_out"] = c.empty((B, Hkv, keep, D), tdtype)
+        ly["v_out"] = c.empty((B, Hkv, keep, D), tdtype)
+        ly["ws"] = c.empty(ws_bytes, torch.uint8)
+        ly["tk_ws"] = c.empty(256, torch.uint8)
+        ly["calls"] = [L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st,
+                                            reduce=L.KVC_REDUCE_ALL_HEADS, causal=False),
+                       L.bind_topk_select(ly["scores"], keep, 0, ly["idx"], ly["tk_ws"], st),
+                       L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st)]
+        ly["kscore"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], s0,
+                                            reduce=L.KVC_REDUCE_ALL_HEADS, causal=False)
+        ly["kgather"] = L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], s0)
+
+    def step():
+        for ly in layers:
+            for f in ly["calls"]:
+                f()
+
+    k_bytes, q_bytes, s_bytes = B * Hkv * S * D * esz, B * H * w * D * esz, B * Hkv * S * 4
+    i_bytes, g_bytes = B * Hkv * keep * 4, 2 * 2 * B * Hkv * keep * D * esz
+    layer_bytes = k_bytes + q_bytes + 2 * s_bytes + 2 * i_bytes + g_bytes
+    # the dominant kernel: the gather when it moves more bytes than the scoring reads
+    if g_bytes > k_bytes:
+        kernel = ("kvc_gather_compact", [ly["kgather"] for ly in layers], g_bytes + i_bytes, None)
+    else:
+        kernel = ("kvc_window_scores", [ly["kscore"] for ly in layers], k_bytes + q_bytes + s_bytes, None)
+
+    def cpu(budget):
+        from oracle import kvc_oracle as O
+        q64, k64 = host0.q64(), host0.k64()
+
+        def one(n):
+            b = n % B
+            s, idx = O.tova(q64[b:b + 1], k64[b:b + 1], None, keep)
+            O.gather_compact(host0.k[b:b + 1], host0.v[b:b + 1], idx)
+        n, el = timed_oracle(one, budget)
+        return {"value": round(S * n / el, 1), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"{n} sequences (of {B} per layer) of layer 0, S={S}, fp64 numpy oracle (scores, top-k, "
+                          f"gather), {el:.1f} s"}
+    return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes,
+                kernel=kernel, cpu=cpu, metric=f"KV tokens scored+pruned/s per layer ({cfg.name})",
+                unit="tokens/s", dtype=dtype, workload=cfg.name,
+                config={"B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep})
+
+
+def wl_think_128k(c: Ctx) -> dict:
+    L, torch, cfg = c.L, c.torch, c.configs.THINK_128K
+    B, H, Hkv, S, D, w, keep, dk = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.w, cfg.keep, cfg.d_keep
+    nl = c.args.layers or cfg.layers
+    layers, host0 = [], None
+    for layer in range(nl):
+        p = c.synth.think_snapkv(layer)
+        layers.append(dict(q=c.up(p.q), k=c.up(p.k), v=c.up(p.v)))
+        host0 = host0 or p
+    ws_bytes = L.window_scores_ws_bytes(B, H, Hkv, S, D, w)
+    cs_bytes = L.channel_scores_ws_bytes(B, H, Hkv, S, D, w)
+    s0 = c.streams[0]
+    for i, ly in enumerate(layers):
+        st = c.streams[i % len(c.streams)]
+        ly["cs"] = c.empty((B, Hkv, D), torch.float32)
+        ly["ch"] = c.empty((B, Hkv, dk), torch.int32)
+        ly["scores"] = c.empty((B, Hkv, S), torch.float32)
+        ly["idx"] = c.empty((B, Hkv, keep), torch.int32)
+        ly["k_out"] = c.empty((B, Hkv, keep, D), torch.bfloat16)
+        ly["v_out"] = c.empty((B, Hkv, keep, D), torch.bfloat16)
+        ly["ws"] = c.empty(max(ws_bytes, cs_bytes), torch.uint8)
+        ly["tk_ws"] = c.empty(256, torch.uint8)
+        ly["calls"] = [L.bind_channel_scores(ly["q"], ly["k"], ly["cs"], ly["ws"], st),
+                       L.bind_topk_select(ly["cs"], dk, 0, ly["ch"], ly["tk_ws"], st),
+                       L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st, chan_idx=ly["ch"],
+                                            reduce=L.KVC_REDUCE_GROUP, causal=True),
+                       L.bind_topk_select(ly["scores"], keep, w, ly["idx"], ly["tk_ws"], st),
+                       L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st,
+                                             chan_idx=ly["ch"])]
+        ly["kcall"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], s0, chan_idx=ly["ch"],
+                                           reduce=L.KVC_REDUCE_GROUP, causal=True)
+
+    def step():
+        for ly in layers:
+            for f in ly["calls"]:
+                f()
+
+    # K once (channel pass and score passes), Q, scores written and read, indices
+    # written and read, kept K and V read and written
+    k_bytes, q_bytes, s_bytes = B * Hkv * S * D * 2, B * H * w * D * 2, B * Hkv * S * 4
+    i_bytes, g_bytes = B * Hkv * keep * 4, 2 * 2 * B * Hkv * keep * D * 2
+    layer_bytes = k_bytes + q_bytes + 2 * s_bytes + 2 * i_bytes + g_bytes
+
+    def cpu(budget):
+        from oracle import kvc_oracle as O
+        q64, k64 = host0.q64(), host0.k64()
+        G = H // Hkv
+
+        def one(n):
+            g = n % Hkv
+            _, ch, s, idx = O.think_snapkv(q64[:, g * G:(g + 1) * G], k64[:, g:g + 1], dk, keep)
+            O.gather_compact(host0.k[:, g:g + 1], host0.v[:, g:g + 1], idx, chan_keep=ch)
+        n, el = timed_oracle(one, budget)
+        return {"value": round(B * S * n / Hkv / el, 1), "unit": "tokens/s", "cores": blas_threads(),
+                "kind": "oracle", "sample": f"{n} KV heads (of {Hkv} per layer) of layer 0, S={S}, fp64 numpy "
+                                            f"oracle (channels, scores, top-k, gather), {el:.1f} s"}
+    return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes,
+                kernel=("kvc_window_scores with 64 of 128 key channels (pass 1 + merge + pass 2)",
+                        [ly["kcall"] for ly in layers], k_bytes + q_bytes + s_bytes, None),
+                cpu=cpu, metric=f"KV tokens scored+pruned/s per layer ({cfg.name})", unit="tokens/s", dtype="bf16",
+                workload=cfg.name, config={"B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep,
+                                           "d_keep": dk})
+
+
+def wl_scissor_decode(c: Ctx) -> dict:
+    L, torch, cfg = c.L, c.torch, c.configs.SCISSOR_DECODE
+    B, H, Hkv, C, D = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D
+    nl = c.args.layers or cfg.layers
+    nsteps = c.args.steps
+    W = (C + 31) // 32
+    layers = []
+    for layer in range(nl):
+        qs = np.stack([c.synth.scissor_query(layer, t) for t in range(nsteps)])  # [T, B, H, 1, D]
+        ly = dict(k=c.up(c.synth.scissor_cache(layer)), q=c.up(qs))
+        ly["valid"] = c.empty((B, Hkv, C), torch.uint8)
+        ly["hist"] = c.empty((cfg.hist_len, B * Hkv, W), torch.int32)
+        ly["counts"] = c.empty((B, Hkv, C), torch.int16)
+        ly["probs"] = c.empty((B, Hkv, C), torch.float32)
+        ly["frac"] = c.empty((B, Hkv, C), torch.float32)
+        ly["ev"] = c.empty((B, Hkv, cfg.n_evict), torch.int32)
+        ly["ws"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, C, D, 1), torch.uint8)
+        ly["tk_ws"] = c.empty(256, torch.uint8)
+        layers.append(ly)
+    s0 = c.streams[0]
+    for i, ly in enumerate(layers):
+        st = c.streams[i % len(c.streams)]
+        ly["st"] = st
+        ly["score"] = [L.bind_window_scores(ly["q"][t], ly["k"], ly["probs"], ly["ws"], st, valid=ly["valid"],
+                                            reduce=L.KVC_REDUCE_GROUP, causal=False) for t in range(nsteps)]
+        ly["kcall"] = L.bind_window_scores(ly["q"][0], ly["k"], ly["probs"], ly["ws"], s0, valid=ly["valid"],
+                                           reduce=L.KVC_REDUCE_GROUP, causal=False)
+        ly["topk"] = L.bind_topk_select(ly["frac"], cfg.n_evict, 0, ly["ev"], ly["tk_ws"], st)
+
+    state = {"t": 0}
+
+    def reset():
+        for ly in layers:
+            ly["valid"].fill_(1)
+            ly["hist"].zero_()
+            ly["counts"].zero_()
+        torch.cuda.synchronize()
+        state["t"] = 0
+
+    def step():
+        t = state["t"]
+        evict = (t + 1) % cfg.evict_every == 0
+        for ly in layers:
+            ly["score"][t]()
+            L.kvc_scissor_update(t, ly["valid"], ly["hist"], ly["counts"], probs=ly["probs"],
+                                 frac_out=ly["frac"] if evict else None, stream=ly["st"])
+            if evict:
+                ly["topk"]()
+                L.kvc_scissor_update(t, ly["valid"], ly["hist"], ly["counts"], evict_idx=ly["ev"], stream=ly["st"])
+        state["t"] = t + 1
+
+    # token-steps: valid slots per (b, g) at step t, times the batch
+    units = sum(B * (C - (t // cfg.evict_every) * cfg.n_evict) for t in range(nsteps))
+    k_bytes = B * Hkv * C * D * 2
+    # per step: K, Q, probabilities written and read, counts read and written,
+    # one bit-plane, validity
+    step_bytes = k_bytes + B * H * D * 2 + 2 * B * Hkv * C * 4 + 2 * B * Hkv * C * 2 + B * Hkv * W * 4 + B * Hkv * C
+
+    def cpu(budget):
+        from oracle import kvc_oracle as O
+        k64 = c.synth.stored_to_f64(c.synth.scissor_cache(0), "bf16")[0:1, 0:1]
+        G = H // Hkv
+        cache = O.ScissorhandsCache(1, 1, C, cfg.hist_len)
+        done = {"units": 0}
+
+        def one(n):
+            q = c.synth.stored_to_f64(c.synth.scissor_query(0, n % nsteps), "bf16")[0:1, 0:G]
+            done["units"] += int(cache.valid.sum())
+            O.scissorhands_step(cache, q, k64, n, cfg.evict_every, cfg.n_evict)
+        n, el = timed_oracle(one, budget)
+        # one (b, g) row is 1/Hkv of a sequence's work in a layer
+        return {"value": round(done["units"] / Hkv / el, 1), "unit": "token-steps/s", "cores": blas_threads(),
+                "kind": "oracle", "sample": f"{n} decode steps of one (batch, KV head) row of layer 0, C={C}, fp64 "
+                                            f"numpy oracle (probabilities, record, eviction), {el:.1f} s"}
+    return dict(step=step, reset=reset, units_per_step=units * nl / nsteps, layers=nl, layer_bytes=step_bytes,
+                kernel=("kvc_window_scores (w=1, stored logits)", [ly["kcall"] for ly in layers],
+                        k_bytes + B * H * D * 2 + B * Hkv * C * 4, None),
+                cpu=cpu, metric=f"KV token-steps scored+recorded/s per layer ({cfg.name})", unit="token-steps/s",
+                dtype="bf16", workload=cfg.name,
+                config={"B": B, "H": H, "Hkv": Hkv, "C": C, "D": D, "decode_steps": nsteps,
+                        "hist_len": cfg.hist_len, "evict_every": cfg.evict_every, "n_evict": cfg.n_evict})
+
+
+def build_workload(c: Ctx) -> dict:
+    wl = c.args.workload
+    if wl == "snapkv_32k":
+        return wl_snapkv_32k(c)
+    if wl == "tova_tiny":
+        return wl_tova(c, c.configs.TOVA_TINY, c.synth.tova_tiny, "f32", c.torch.float32)
+    if wl == "tova_batched":
+        return wl_tova(c, c.configs.TOVA_BATCHED, c.synth.tova_batched, "bf16", c.torch.bfloat16)
+    if wl == "think_128k":
+        return wl_think_128k(c)
+    return wl_scissor_decode(c)
 
 
 def main():
@@ -62,133 +411,84 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is data-parallel per "
               f"(batch, KV head) and is not sharded here.", file=sys.stderr)
         sys.exit(2)
-
-    import torch
-
-    from kv_cache_compression_window_amd import binding as L
-    from kv_cache_compression_window_amd import configs, synth
-
-    cfg = configs.SNAPKV_32K
-    B, H, Hkv, S, D, w, keep = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.w, cfg.keep
-    dev = torch.device("cuda:0")
-
-    def up(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
+    if args.workload == "scissor_decode" and not 1 <= args.steps <= 800:
+        print("the decode workload runs between 1 and 800 steps", file=sys.stderr)
+        sys.exit(2)
+    c = Ctx(args)
+    torch = c.torch
     t0 = time.time()
-    layers = []
-    for layer in range(args.layers):
-        p = synth.snapkv(layer)
-        layers.append(dict(q=up(p.q), k=up(p.k), v=up(p.v)))
-        if layer == 0:
-            host0 = p
-    gen_s = time.time() - t0
-    print(f"[bench] generated {args.layers} layers in {gen_s:.1f}s", file=sys.stderr, flush=True)
+    wl = build_workload(c)
+    print(f"[bench] {wl['workload']}: set up in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
-    streams = [torch.cuda.Stream(device=dev) for _ in range(args.streams)]
-    ws_bytes = L.window_scores_ws_bytes(B, H, Hkv, S, D, w)
-    for i, ly in enumerate(layers):
-        ly["stream"] = streams[i % len(streams)]
-        ly["scores"] = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
-        ly["idx"] = torch.empty((B, Hkv, keep), dtype=torch.int32, device=dev)
-        ly["k_out"] = torch.empty((B, Hkv, keep, D), dtype=torch.bfloat16, device=dev)
-        ly["v_out"] = torch.empty((B, Hkv, keep, D), dtype=torch.bfloat16, device=dev)
-        ly["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-        ly["tk_ws"] = torch.empty(256, dtype=torch.uint8, device=dev)
+    cur = torch.cuda.current_stream(c.dev)
 
-        st = ly["stream"]
-        ly["score_call"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st,
-                                                reduce=L.KVC_REDUCE_GROUP, causal=True)
-        ly["score_call0"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], streams[0],
-                                                 reduce=L.KVC_REDUCE_GROUP, causal=True)
-        ly["topk_call"] = L.bind_topk_select(ly["scores"], keep, w, ly["idx"], ly["tk_ws"], st)
-        ly["gather_call"] = L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st)
-
-    def step():
+    def run_steps(n):
         # the streams start after everything queued on the default stream
-        cur = torch.cuda.current_stream(dev)
-        for st in streams:
+        for st in c.streams:
             st.wait_stream(cur)
-        for ly in layers:
-            ly["score_call"]()
-            ly["topk_call"]()
-            ly["gather_call"]()
-        for st in streams:
+        for _ in range(n):
+            wl["step"]()
+        for st in c.streams:
             cur.wait_stream(st)
 
-    for _ in range(args.warmup):
-        step()
+    reset = wl.get("reset")
+    if reset is None:
+        run_steps(args.warmup)
+    else:  # a decode run: the warm-up is one whole run from a fresh state
+        reset()
+        run_steps(args.steps)
+        reset()
     torch.cuda.synchronize()
 
     # timed region: K steps between a synchronisation on each side
-    torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
-        step()
+    run_steps(args.steps)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     elapsed_ms = start.elapsed_time(end)
 
-    # the dominant step, the window-score call, timed alone: every call of
-    # kernel-reps passes over the layers runs on one stream between two HIP
-    # events recorded on that stream (nothing else runs meanwhile)
-    st0 = streams[0]
-    st0.wait_stream(torch.cuda.current_stream(dev))
+    # the dominant kernel timed alone: in each of kernel-reps passes over the
+    # layers every call runs on one stream between two HIP events recorded on it
+    label, kcalls, kbytes, traffic = wl["kernel"]
+    st0 = c.streams[0]
+    st0.wait_stream(cur)
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.kernel_reps * len(layers))]
+           for _ in range(args.kernel_reps * len(kcalls))]
     for r in range(args.kernel_reps):
-        for i, ly in enumerate(layers):
-            a, b = kev[r * len(layers) + i]
+        for i, f in enumerate(kcalls):
+            a, b = kev[r * len(kcalls) + i]
             a.record(st0)
-            ly["score_call0"]()
+            f()
             b.record(st0)
     torch.cuda.synchronize()
-    score_us = float(np.mean([a.elapsed_time(b) for (a, b) in kev])) * 1e3
+    k_us = float(np.mean([a.elapsed_time(b) for (a, b) in kev])) * 1e3
 
-    tokens = B * S * args.layers * args.steps
-    value = tokens / (elapsed_ms * 1e-3)
-    t_layer_us = elapsed_ms * 1e3 / (args.layers * args.steps)
-    # algorithmic bytes per layer: K read once, Q read, scores written and read
-    # by the top-k, indices written and read, kept K and V read and written
-    k_bytes = B * Hkv * S * D * 2
-    q_bytes = B * H * w * D * 2
-    s_bytes = B * Hkv * S * 4
-    i_bytes = B * Hkv * keep * 4
-    g_bytes = 2 * 2 * B * Hkv * keep * D * 2
-    layer_bytes = k_bytes + q_bytes + 2 * s_bytes + 2 * i_bytes + g_bytes
-    hbm_frac = layer_bytes / (HBM_PEAK_GBS * 1e9) / (t_layer_us * 1e-6)
-
-    # dominant step: the window scores (pass 1, merge, pass 2)
-    score_bytes = k_bytes + q_bytes + s_bytes
-    achieved = score_bytes / (score_us * 1e-6) / 1e9
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_hash") == score_kernel_hash():
-            traffic = tr.get("bytes_per_launch")
+    units = wl["units_per_step"] * args.steps
+    value = units / (elapsed_ms * 1e-3)
+    t_layer_us = elapsed_ms * 1e3 / (wl["layers"] * args.steps)
+    hbm_frac = wl["layer_bytes"] / (HBM_PEAK_GBS * 1e9) / (t_layer_us * 1e-6)
+    achieved = kbytes / (k_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "kvc_window_scores (pass 1 + merge + pass 2)", "avg_us": round(score_us, 2),
-                "algorithmic_bytes": score_bytes}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": label,
+                "avg_us": round(k_us, 2), "algorithmic_bytes": kbytes}
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=c.dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(host0, keep, args.cpu_seconds)
-
+    cpu = None if args.no_cpu_baseline else wl["cpu"](args.cpu_seconds)
+    config = {"workload": wl["workload"], **wl["config"], "layers_per_step": wl["layers"], "streams": args.streams,
+              "us_per_layer": round(t_layer_us, 3), "algorithmic_bytes_per_layer": wl["layer_bytes"],
+              "hbm_roofline_frac": round(hbm_frac, 4), "wall_s": round(wall, 4)}
     out = {
-        "metric": METRIC,
+        "metric": wl["metric"],
         "value": round(value, 1),
-        "unit": "tokens/s",
+        "unit": wl["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -196,47 +496,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wl["dtype"],
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep,
-                   "layers_per_step": args.layers, "streams": args.streams, "us_per_layer": round(t_layer_us, 3),
-                   "algorithmic_bytes_per_layer": layer_bytes, "hbm_roofline_frac": round(hbm_frac, 4),
-                   "wall_s": round(wall, 4)},
+        "config": config,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-
-
-def cpu_baseline(p, keep, budget_s):
-    """The fp64 oracle (unchanged) on whole KV heads of one layer of the same
-    workload, until about budget_s seconds of CPU work; tokens/s per layer."""
-    from oracle import kvc_oracle as O
-
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    q64, k64 = p.q64(), p.k64()
-    G = p.H // p.Hkv
-    done_heads = 0
-    t0 = time.perf_counter()
-    while True:
-        g = done_heads % p.Hkv
-        qg = q64[:, g * G:(g + 1) * G]
-        kg = k64[:, g:g + 1]
-        s, idx = O.snapkv(qg, kg, keep)
-        O.gather_compact(p.k[:, g:g + 1], p.v[:, g:g + 1], idx)
-        done_heads += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    # one KV head is 1/Hkv of a layer's work on all S positions
-    tokens = p.B * p.S * done_heads / p.Hkv
-    return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done_heads} KV heads (of {p.Hkv} per layer) of layer 0, S={p.S}, fp64 numpy oracle, "
-                      f"{el:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -106,10 +106,11 @@ def _workspace(nbytes: int, device, ws):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def window_scores_ws_bytes(B, H, Hkv, S, D, w) -> int:
+def window_scores_ws_bytes(B, H, Hkv, S, D, w, dtype=None) -> int:
     sh = KvcShape(B, H, Hkv, S, D, w)
     n = ctypes.c_size_t(0)
-    _check("kvc_window_scores", LIB.kvc_window_scores(ctypes.byref(sh), KVC_BF16, None, None, None, None, 0, 0, 0,
+    dt = KVC_BF16 if dtype is None else dtype
+    _check("kvc_window_scores", LIB.kvc_window_scores(ctypes.byref(sh), dt, None, None, None, None, 0, 0, 0,
                                                       None, None, ctypes.byref(n), None))
     return n.value
 
@@ -263,4 +264,16 @@ def bind_gather_compact(k, v, idx, k_out, v_out, stream, chan_idx=None):
             _ptr(k_out), _ptr(v_out), ctypes.c_void_p(stream.cuda_stream))
     call = _bound("kvc_gather_compact", args)
     call.keep_alive = (sh, k, v, idx, chan_idx, k_out, v_out)
+    return call
+
+
+def bind_channel_scores(q, k, out, ws, stream):
+    _need(q, "q_win", 4)
+    _need(k, "k", 4)
+    sh = _shape(q, k)
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    args = (ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(out), _ptr(ws), ctypes.byref(n),
+            ctypes.c_void_p(stream.cuda_stream))
+    call = _bound("kvc_channel_scores", args)
+    call.keep_alive = (sh, n, q, k, out, ws)
     return call

@@ -8,8 +8,8 @@
 //
 // Kernel 1 streams K once: every workgroup sums k^2 over a chunk of keys of one
 // (b, g).  The threads' partial sums are added in a fixed order through LDS.
-// Kernel 2 adds the chunk partials in chunk order and multiplies by the query
-// sums.  There are no float atomics, so the result is deterministic.
+// Kernel 2 adds the chunk partials and the query squares in a fixed order and
+// multiplies them.  There are no float atomics, so the result is deterministic.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
@@ -87,20 +87,39 @@ __global__ __launch_bounds__(NTH) void key_sq_partial_kernel(const uint4* __rest
   }
 }
 
+// One workgroup per (b, g): thread (slice s, channel d) adds the chunks and
+// query rows congruent to s modulo FS with up to 16 loads in flight, then the
+// FS slices are added in slice order.
+constexpr int FTH = 1024;
+
 template <typename T, int D>
-__global__ void channel_finish_kernel(const float* __restrict__ part, int nchunks, const T* __restrict__ q, int R,
-                                      float* __restrict__ out) {
+__global__ __launch_bounds__(FTH) void channel_finish_kernel(const float* __restrict__ part, int nchunks,
+                                                             const T* __restrict__ q, int R, float* __restrict__ out) {
+  constexpr int FS = FTH / D;
+  __shared__ float red_k[FS][D], red_q[FS][D];
   const size_t bg = blockIdx.x;
-  const int d = threadIdx.x;
-  if (d >= D) return;
+  const int d = threadIdx.x % D, sl = threadIdx.x / D;
   float ks = 0.0f;
-  for (int c = 0; c < nchunks; ++c) ks += part[(bg * nchunks + c) * D + d];
+#pragma unroll 16
+  for (int c = sl; c < nchunks; c += FS) ks += part[(bg * nchunks + c) * D + d];
   float qs = 0.0f;
-  for (int r = 0; r < R; ++r) {
+#pragma unroll 16
+  for (int r = sl; r < R; r += FS) {
     const float x = (float)q[(bg * R + r) * D + d];
     qs += x * x;
   }
-  out[bg * D + d] = qs * ks;
+  red_k[sl][d] = ks;
+  red_q[sl][d] = qs;
+  __syncthreads();
+  if (sl == 0) {
+    float k2 = 0.0f, q2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < FS; ++i) {
+      k2 += red_k[i][d];
+      q2 += red_q[i][d];
+    }
+    out[bg * D + d] = q2 * k2;
+  }
 }
 
 template <typename T, int D>
@@ -110,7 +129,7 @@ void run(const CsArgs& a, const CsPlan& plan, hipStream_t st) {
   key_sq_partial_kernel<T, D><<<grid, NTH, 0, st>>>(static_cast<const uint4*>(a.k), a.S, plan.CH, plan.nchunks,
                                                     a.Hkv, part);
   const int R = (a.H / a.Hkv) * a.w;
-  channel_finish_kernel<T, D><<<a.B * a.Hkv, D, 0, st>>>(part, plan.nchunks, static_cast<const T*>(a.q), R, a.out);
+  channel_finish_kernel<T, D><<<a.B * a.Hkv, FTH, 0, st>>>(part, plan.nchunks, static_cast<const T*>(a.q), R, a.out);
 }
 
 }  // namespace

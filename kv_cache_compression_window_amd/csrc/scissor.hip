@@ -67,6 +67,91 @@ __global__ __launch_bounds__(NTH) void scissor_record_kernel(int C, int W, int B
   }
 }
 
+// Number of nonzero bytes of a 16-byte unit.
+__device__ inline int nonzero_bytes(const uint4& u) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) n += ((w[i] >> (8 * k)) & 0xFFu) != 0u;
+  return n;
+}
+
+// The same step when C is a multiple of 32 and the rows are 16-byte aligned:
+// thread t owns the 32-slot words t, t + NTH, ... of its (b, g) row, loads the
+// validity, probabilities, counts and old history word of a word with
+// independent 16-byte loads, and writes the new word itself.
+__global__ __launch_bounds__(NTH) void scissor_record_words_kernel(int C, int W, int BHkv, int plane, int n_obs,
+                                                                    const float* __restrict__ probs,
+                                                                    const uint8_t* __restrict__ valid,
+                                                                    uint32_t* __restrict__ hist,
+                                                                    uint16_t* __restrict__ counts,
+                                                                    float* __restrict__ frac_out) {
+  __shared__ int red[NTH / 64];
+  const size_t bg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint4* v4 = reinterpret_cast<const uint4*>(valid + bg * C);
+
+  int cnt = 0;
+  for (int wd = tid; wd < W; wd += NTH) cnt += nonzero_bytes(v4[2 * wd]) + nonzero_bytes(v4[2 * wd + 1]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  if (lane == 0) red[wave] = cnt;
+  __syncthreads();
+  int S_t = 0;
+#pragma unroll
+  for (int wv = 0; wv < NTH / 64; ++wv) S_t += red[wv];
+  const double uniform = S_t > 0 ? 1.0 / (double)S_t : 0.0;
+  const float inv_obs = 1.0f / (float)n_obs;
+
+  uint32_t* prow = hist + ((size_t)plane * BHkv + bg) * W;
+  const float4* p4 = reinterpret_cast<const float4*>(probs + bg * C);
+  uint4* c4 = reinterpret_cast<uint4*>(counts + bg * C);
+  float4* f4 = frac_out ? reinterpret_cast<float4*>(frac_out + bg * C) : nullptr;
+  for (int wd = tid; wd < W; wd += NTH) {
+    const uint4 va = v4[2 * wd], vb = v4[2 * wd + 1];
+    float4 pr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pr[i] = p4[8 * wd + i];
+    uint4 cn[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cn[i] = c4[4 * wd + i];
+    const uint32_t old = prow[wd];
+    const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+    uint32_t word = 0u;
+    uint32_t cw[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      cw[4 * i] = cn[i].x;
+      cw[4 * i + 1] = cn[i].y;
+      cw[4 * i + 2] = cn[i].z;
+      cw[4 * i + 3] = cn[i].w;
+    }
+    float fr[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const bool v = ((vw[j >> 2] >> (8 * (j & 3))) & 0xFFu) != 0u;
+      const float pj = (j & 3) == 0 ? pr[j >> 2].x : (j & 3) == 1 ? pr[j >> 2].y : (j & 3) == 2 ? pr[j >> 2].z
+                                                                                              : pr[j >> 2].w;
+      const bool low = v && ((double)pj < uniform);
+      word |= (uint32_t)low << j;
+      const uint32_t sh = 16 * (j & 1);
+      const int cold = (int)((cw[j >> 1] >> sh) & 0xFFFFu);
+      const int cnew = cold + (int)low - (int)((old >> j) & 1u);
+      cw[j >> 1] = (cw[j >> 1] & ~(0xFFFFu << sh)) | ((uint32_t)cnew << sh);
+      fr[j] = v ? (float)cnew * inv_obs : kNegInf;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c4[4 * wd + i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
+    prow[wd] = word;
+    if (f4) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f4[8 * wd + i] = make_float4(fr[4 * i], fr[4 * i + 1], fr[4 * i + 2], fr[4 * i + 3]);
+    }
+  }
+}
+
 __global__ void scissor_evict_kernel(int C, int n_evict, const int32_t* __restrict__ evict_idx,
                                      uint8_t* __restrict__ valid) {
   const size_t bg = blockIdx.x;
@@ -76,6 +161,8 @@ __global__ void scissor_evict_kernel(int C, int n_evict, const int32_t* __restri
   }
 }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 }  // namespace
 
 hipError_t launch_scissor(const ScissorArgs& a, hipStream_t st) {
@@ -84,8 +171,14 @@ hipError_t launch_scissor(const ScissorArgs& a, hipStream_t st) {
   if (a.probs) {
     const int plane = (int)(a.step % a.hist_len);
     const int64_t obs = a.step + 1 < a.hist_len ? a.step + 1 : a.hist_len;
-    scissor_record_kernel<<<BHkv, NTH, 0, st>>>(a.C, W, BHkv, plane, (int)obs, a.probs, a.valid, a.hist,
-                                                a.counts, a.frac_out);
+    const bool words = a.C % 32 == 0 && aligned16(a.probs) && aligned16(a.valid) && aligned16(a.counts) &&
+                       (!a.frac_out || aligned16(a.frac_out));
+    if (words)
+      scissor_record_words_kernel<<<BHkv, NTH, 0, st>>>(a.C, W, BHkv, plane, (int)obs, a.probs, a.valid, a.hist,
+                                                        a.counts, a.frac_out);
+    else
+      scissor_record_kernel<<<BHkv, NTH, 0, st>>>(a.C, W, BHkv, plane, (int)obs, a.probs, a.valid, a.hist,
+                                                  a.counts, a.frac_out);
   }
   if (a.evict_idx && a.n_evict > 0) scissor_evict_kernel<<<BHkv, 256, 0, st>>>(a.C, a.n_evict, a.evict_idx, a.valid);
   return hipGetLastError();

@@ -1,11 +1,13 @@
 // Per-row top-k with a forced tail, kept indices in ascending order (gfx950).
 //
 // One workgroup of 1024 threads per row.  Scores become order-preserving uint32
-// keys.  Thread t holds the keys of the KPT consecutive positions t*KPT ..
-// t*KPT+KPT-1 of a tile of 1024*KPT positions, so that its kept positions come
-// out in order.  Rows that fit one tile keep their keys in registers for the
-// whole selection; longer rows (KPT = 32) are processed tile by tile and re-read
-// from L2 at every sweep.  Slots past the end of the row hold the row's minimum
+// keys.  For the compaction thread t holds the keys of the KPT consecutive
+// positions t*KPT .. t*KPT+KPT-1 of a tile of 1024*KPT positions, so that its
+// kept positions come out in order; keys are loaded in coalesced order and
+// handed to their owners through LDS.  Rows that fit one tile keep their keys in
+// registers for the whole selection; longer rows (KPT = 32) are processed tile
+// by tile and re-read from L2 at every sweep, in coalesced order for the
+// histogram passes (which take any order).  Slots past the end of the row hold the row's minimum
 // key: they sit after every real position, so the lowest-index tie rule never
 // takes them, and the hot loops need no bounds test.
 //
@@ -159,26 +161,26 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
   }
 
   const int ntiles = RESIDENT ? 1 : (E + TILE - 1) / TILE;
-  const bool vec = (KPT % 4 == 0) && ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
   uint32_t u[KPT];
-  // keys of this thread's positions in tile t; positions past E read position
-  // E-1 (a duplicate, which leaves the key range unchanged)
-  auto load_keys = [&](int t) {
-    const int p0 = t * TILE + tid * KPT;
-    if (vec && p0 + KPT <= E) {
-      const float4* s4 = reinterpret_cast<const float4*>(s + p0);
+  // Keys of tile t in coalesced order (slot i of thread t holds position
+  // t*TILE + i*NTH + tid; positions past E read position E-1, a duplicate that
+  // leaves the key range unchanged).  The histogram passes take any order.
+  auto load_coalesced = [&](int t) {
 #pragma unroll
-      for (int j = 0; j < KPT / 4; ++j) {
-        const float4 f = s4[j];
-        u[4 * j] = float_key(f.x);
-        u[4 * j + 1] = float_key(f.y);
-        u[4 * j + 2] = float_key(f.z);
-        u[4 * j + 3] = float_key(f.w);
-      }
-    } else {
+    for (int i = 0; i < KPT; ++i) u[i] = float_key(s[min(t * TILE + i * NTH + tid, E - 1)]);
+  };
+  // Keys of tile t in owner order (slot i of thread t holds position
+  // t*TILE + tid*KPT + i): loaded in coalesced order and handed over through LDS.
+  auto load_owned = [&](int t) {
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) u[i] = float_key(s[min(p0 + i, E - 1)]);
+    for (int j = 0; j < KPT; ++j) {
+      const int p = j * NTH + tid;
+      sh.xpose[xpose_idx(p)] = float_key(s[min(t * TILE + p, E - 1)]);
     }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) u[i] = sh.xpose[xpose_idx(tid * KPT + i)];
+    __syncthreads();
   };
 
   // key range of the eligible positions
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
     for (int i = 0; i < KPT; ++i) u[i] = sh.xpose[xpose_idx(tid * KPT + i)];
   } else {
     for (int t = 0; t < ntiles; ++t) {
-      load_keys(t);
+      load_coalesced(t);
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         kmin = min(kmin, u[i]);
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
 
   // from here on u holds rel = key - kmin (same order as the keys); slots past
   // the row hold 0, the smallest rel
-  auto to_rel = [&](int t) {
+  auto to_rel_owned = [&](int t) {
     const int nv = E - (t * TILE + tid * KPT);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) u[i] -= kmin;
@@ -236,11 +238,23 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
         if (i >= nv) u[i] = 0u;
     }
   };
-  auto load_rel = [&](int t) {
-    load_keys(t);
-    to_rel(t);
+  // tiles of the non-resident passes (coalesced order)
+  auto load_rel_coalesced = [&](int t) {
+    load_coalesced(t);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) u[i] -= kmin;
+    if (t == ntiles - 1) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        if (t * TILE + i * NTH + tid >= E) u[i] = 0u;
+    }
   };
-  if constexpr (RESIDENT) to_rel(0);
+  // tiles of the non-resident compaction (owner order)
+  auto load_rel_owned = [&](int t) {
+    load_owned(t);
+    to_rel_owned(t);
+  };
+  if constexpr (RESIDENT) to_rel_owned(0);
 
   const int cp = lane & (NCOPY - 1);
   uint32_t prefix = 0u;                            // fixed high bits of rel(T)
@@ -255,7 +269,7 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
       reinterpret_cast<uint4*>(sh.hist)[j * NTH + tid] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
-      if constexpr (!RESIDENT) load_rel(t);
+      if constexpr (!RESIDENT) load_rel_coalesced(t);
       if (pass == 0) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) atomicAdd(&sh.hist[((u[i] >> shift) & (NBIN - 1)) * NCOPY + cp], 1u);
@@ -280,7 +294,7 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
 
   uint32_t gt_carry = 0u, eq_carry = 0u;  // counts of earlier tiles
   for (int t = 0; t < ntiles; ++t) {
-    if constexpr (!RESIDENT) load_rel(t);
+    if constexpr (!RESIDENT) load_rel_owned(t);
     const int p0 = t * TILE + tid * KPT;
     if (all_eq) {
       uint32_t c = 0u;
