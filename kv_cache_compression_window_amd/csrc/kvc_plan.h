@@ -45,9 +45,9 @@ inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, WsPlan* p) {
   p->nrch = (nrb + p->NW - 1) / p->NW;
   p->Rpad = p->nrch * p->NW * 32;
   const long long bg = (long long)B * Hkv;
-  // workgroups to aim for: about eight waves per CU on the two-pass path, many
-  // one-wave workgroups on the (HBM-bound) stored-logits path
-  const long long target = p->store ? 4096 : 256LL * 8 / p->NW;
+  // workgroups to aim for: about eight waves per CU on the two-pass path, two
+  // four-wave streaming workgroups per CU on the (HBM-bound) stored-logits path
+  const long long target = p->store ? 512 : 256LL * 8 / p->NW;
   long long nch = (target + bg - 1) / bg;
   const long long max_ch = (S + kTileKeys - 1) / kTileKeys;
   if (nch > max_ch) nch = max_ch;

@@ -600,6 +600,184 @@ __global__ __launch_bounds__(64) void ws_scores_wave_kernel(WsParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Stored-logits kernels (at most 16 rows per KV head: TOVA and decode steps)
+//
+// This path is bound by reading K once.  Four independent waves per workgroup
+// stream interleaved 32-key blocks of a chunk.  A wave reads a block with
+// coalesced 16-byte loads (each instruction covers 1 KB of consecutive rows),
+// NBUF blocks ahead, and hands it to the MFMA fragment layout through its own
+// padded LDS slot (the wave's LDS operations run in order, so no barrier is
+// needed).  MFMA A = key block, B = query block, so the lane of column r holds
+// 16 keys of row r: it keeps row r's running (max, sum of exp2) and writes the
+// scaled logits of its keys.  The finish kernel merges the chunk statistics and
+// reduces the normalised logits.
+// ---------------------------------------------------------------------------
+constexpr int kLogNW = 4;          // waves per workgroup
+constexpr int kFinishRows = 1024;  // rows the finish kernel merges in LDS
+
+// One 32-key block in coalesced order: unit u of the lane is the 16 bytes at
+// offset u*1024 + lane*16 of the block; v is the validity byte of key lane%32.
+template <typename T, int D>
+struct KBlock {
+  static constexpr int UPL = 32 * TileGeom<T, D>::ROWB / 16 / 64;  // units per lane
+  u32x4_t d[UPL];
+  uint8_t v;
+};
+
+template <typename T, int D>
+struct LogitsNBUF {
+  static constexpr int value = KBlock<T, D>::UPL <= 4 ? 3 : KBlock<T, D>::UPL <= 8 ? 2 : 1;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kLogNW * 64) void ws_logits_kernel(WsParams p) {
+  using G_ = TileGeom<T, D>;
+  using KB = KBlock<T, D>;
+  constexpr int NBUF = LogitsNBUF<T, D>::value;
+  __shared__ uint32_t lds_keep[D / 32];
+  __shared__ float2 lds_st[kLogNW][32];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k[kLogNW][32 * G_::LSTRIDE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int chunk = blockIdx.x;
+  const size_t bg = (size_t)blockIdx.z * p.Hkv + blockIdx.y;
+  const int key0 = chunk * p.CH;
+  const int key1 = min(p.S, key0 + p.CH);
+  const int nblk = (key1 - key0 + 31) / 32;
+  const int nb = nblk > wave ? (nblk - wave + kLogNW - 1) / kLogNW : 0;  // this wave's blocks
+  const bool has_valid = p.valid != nullptr;
+  const uint8_t* vrow = has_valid ? p.valid + bg * p.S : nullptr;
+
+  const uint32_t* keep = build_keep<D, kLogNW * 64>(lds_keep, p, bg, tid);
+  const int r = col;  // this lane's query row
+  Frag<T, D> qf;
+  load_query<T, D>(qf, p, bg, r, half, keep);
+  int lim = p.S - 1;
+  if (p.causal && r < p.R) lim = min(p.S - 1, p.S - p.w + r % p.w);
+  float m_run = kNegInf, z_run = 0.0f;
+
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
+  unsigned char* slot = lds_k[wave];
+  auto blk_key = [&](int i) { return key0 + (wave + i * kLogNW) * 32; };
+  // Unconditional loads: rows past S read row S-1 instead (never used), and
+  // without a validity mask the byte comes from the key data and is ignored.
+  auto load_blk = [&](KB& b, int i) {
+    const int kb0 = blk_key(i);
+#pragma unroll
+    for (int u = 0; u < KB::UPL; ++u) {
+      const int off = u * 1024 + lane * 16;
+      const int key = min(kb0 + off / G_::ROWB, p.S - 1);
+      b.d[u] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * G_::ROWB + off % G_::ROWB);
+    }
+    const uint8_t* vsrc = vrow ? vrow : kbase;
+    b.v = vsrc[min(kb0 + col, p.S - 1)];
+  };
+  auto process = [&](const KB& b, int i) {
+    const int kb0 = blk_key(i);
+    // coalesced units -> padded rows of the wave's LDS slot -> fragments
+#pragma unroll
+    for (int u = 0; u < KB::UPL; ++u) {
+      const int off = u * 1024 + lane * 16;
+      *reinterpret_cast<u32x4_t*>(slot + (off / G_::ROWB) * G_::LSTRIDE + off % G_::ROWB) = b.d[u];
+    }
+    __builtin_amdgcn_wave_barrier();
+    Frag<T, D> kf;
+    read_frag<T, D>(kf, slot, col, half);
+    __builtin_amdgcn_wave_barrier();
+    f32x16_t a = mma_block<T, D>(kf, qf);
+    const bool masked = has_valid || kb0 + 32 > key1 || (p.causal && kb0 + 31 > p.S - p.w);
+    if (masked) {
+      const uint32_t vmask = has_valid ? (uint32_t)__ballot(b.v != 0) : 0xFFFFFFFFu;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = acc_row(v, lane);
+        const bool ok = (kb0 + kk <= lim) & (kb0 + kk < key1) & (((vmask >> kk) & 1u) != 0u);
+        a[v] = ok ? a[v] : kNegInf;
+      }
+    }
+    if (r < p.R) {
+      float* dst = p.logits + (bg * p.R + r) * (size_t)p.Spad + kb0 + 4 * half;
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4)
+        *reinterpret_cast<float4*>(dst + 8 * v4) =
+            make_float4(a[4 * v4] * p.c, a[4 * v4 + 1] * p.c, a[4 * v4 + 2] * p.c, a[4 * v4 + 3] * p.c);
+    }
+    fold_stats(a, p.c, m_run, z_run);
+  };
+
+  KB kb[NBUF];
+#pragma unroll
+  for (int j = 0; j < NBUF; ++j) load_blk(kb[j], j);
+  int i = 0;
+  for (; i + 2 * NBUF <= nb; i += NBUF) {  // steady state: no conditional loads
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      process(kb[j], i + j);
+      load_blk(kb[j], i + j + NBUF);
+    }
+  }
+  for (; i < nb; i += NBUF) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      if (i + j < nb) {
+        process(kb[j], i + j);
+        if (i + j + NBUF < nb) load_blk(kb[j], i + j + NBUF);
+      }
+    }
+  }
+
+  // row statistics: lane halves, then the waves in order
+  lse2_merge(m_run, z_run, __shfl_xor(m_run, 32), __shfl_xor(z_run, 32));
+  if (half == 0) lds_st[wave][col] = make_float2(m_run, z_run);
+  __syncthreads();
+  if (tid < 32) {
+    float m = lds_st[0][tid].x, z = lds_st[0][tid].y;
+#pragma unroll
+    for (int wv = 1; wv < kLogNW; ++wv) lse2_merge(m, z, lds_st[wv][tid].x, lds_st[wv][tid].y);
+    p.part[(size_t)chunk * p.rows_total + bg * p.Rpad + tid] = make_float2(m, z);
+  }
+}
+
+// Stored-logits finish: merge the chunk statistics of the rows needed (the R
+// rows of one KV head, or of every KV head of the sequence for ALL_HEADS) into
+// LDS, in chunk order, then s[b,g,j] = scale * sum over the rows of
+// exp2(logit - lse2).  Rows with no allowed key contribute 0.
+__global__ __launch_bounds__(256) void ws_finish_logits_kernel(WsParams p, int all_heads, float scale) {
+  __shared__ float lds_lse[kFinishRows];
+  const int b = blockIdx.z;
+  const int g0 = all_heads ? 0 : blockIdx.y;
+  const int ng = all_heads ? p.Hkv : 1;
+  const int nrows = ng * p.R;
+  for (int t = threadIdx.x; t < nrows; t += blockDim.x) {
+    const int g = g0 + t / p.R, r = t % p.R;
+    const size_t row = ((size_t)b * p.Hkv + g) * p.Rpad + r;
+    float m = kNegInf, z = 0.0f;
+#pragma unroll 8
+    for (int c = 0; c < p.nchunks; ++c) {
+      const float2 pc = p.part[(size_t)c * p.rows_total + row];
+      lse2_merge(m, z, pc.x, pc.y);
+    }
+    lds_lse[t] = (m == kNegInf || !(z > 0.0f)) ? kPosInf : m + log2f(z);
+  }
+  __syncthreads();
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= p.S) return;
+  float s = 0.0f;
+  for (int gi = 0; gi < ng; ++gi) {
+    const size_t bg = (size_t)b * p.Hkv + g0 + gi;
+    float sg = 0.0f;
+    for (int r = 0; r < p.R; ++r) sg += fast_exp2(p.logits[(bg * p.R + r) * (size_t)p.Spad + j] - lds_lse[gi * p.R + r]);
+    s += sg;
+  }
+  s *= scale;
+  if (all_heads) {
+    for (int g = 0; g < p.Hkv; ++g) p.scores[((size_t)b * p.Hkv + g) * p.S + j] = s;
+  } else {
+    p.scores[((size_t)b * p.Hkv + g0) * p.S + j] = s;
+  }
+}
+
 // Per row: combine the chunk partials into lse2 = max + log2(sum).  Sixteen
 // lanes share a row (each takes every 16th chunk) and combine by a fixed
 // butterfly.  Rows past R (padding) and rows with no allowed key get +inf, so
@@ -727,7 +905,19 @@ hipError_t launch_window_scores(const WsArgs& a, const WsPlan& plan, hipStream_t
   };
   const int rows_per_launch = plan.NW * 32;
 
-  for (int c = 0; c < plan.nrch; ++c) {  // row statistics (and stored logits)
+  if (plan.store && (!a.reduce || a.Hkv * plan.R <= kFinishRows)) {
+    // stored-logits path: one launch writes the logits and the chunk statistics,
+    // one launch merges them and reduces
+    if (bf && a.D == 128) ws_logits_kernel<__bf16, 128><<<grid, kLogNW * 64, 0, st>>>(p);
+    else if (bf) ws_logits_kernel<__bf16, 64><<<grid, kLogNW * 64, 0, st>>>(p);
+    else if (a.D == 128) ws_logits_kernel<float, 128><<<grid, kLogNW * 64, 0, st>>>(p);
+    else ws_logits_kernel<float, 64><<<grid, kLogNW * 64, 0, st>>>(p);
+    const int all = a.reduce ? 1 : 0;
+    const dim3 g2((a.S + 255) / 256, all ? 1 : a.Hkv, a.B);
+    ws_finish_logits_kernel<<<g2, 256, 0, st>>>(p, all, all ? 1.0f / (float)(a.H * a.w) : p.out_scale);
+    return hipGetLastError();
+  }
+  for (int c = 0; c < plan.nrch; ++c) {  // row statistics
     p.row0 = c * rows_per_launch;
     run(false);
   }
