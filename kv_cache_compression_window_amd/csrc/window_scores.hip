@@ -778,31 +778,29 @@ __global__ __launch_bounds__(256) void ws_finish_logits_kernel(WsParams p, int a
   }
 }
 
-// Per row: combine the chunk partials into lse2 = max + log2(sum).  Sixteen
-// lanes share a row (each takes every 16th chunk) and combine by a fixed
-// butterfly.  Rows past R (padding) and rows with no allowed key get +inf, so
-// their probabilities are 0.
-__global__ __launch_bounds__(256) void ws_merge_kernel(const float2* __restrict__ part, float* __restrict__ lse,
-                                                       int rows_total, int Rpad, int R, int nchunks) {
-  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  float m = kNegInf, z = 0.0f;
-  if (row < rows_total) {
-    for (int c = sub; c < nchunks; c += 16) {
-      const float2 pc = part[(size_t)c * rows_total + row];
-      lse2_merge(m, z, pc.x, pc.y);
+// Per row: combine the chunk partials into lse2 = M + log2(sum over chunks of
+// z_c * exp2(m_c - M)), M the largest chunk maximum, summed in chunk order.
+// One thread per row, so each chunk's partials are read coalesced across the
+// rows.  Rows past R (padding) and rows with no allowed key get +inf, so their
+// probabilities are 0.
+__global__ __launch_bounds__(64) void ws_merge_kernel(const float2* __restrict__ part, float* __restrict__ lse,
+                                                      int rows_total, int Rpad, int R, int nchunks) {
+  const int row = blockIdx.x * 64 + threadIdx.x;
+  if (row >= rows_total) return;
+  const float2* pr = part + row;
+  float m = kNegInf;
+#pragma unroll 8
+  for (int c = 0; c < nchunks; ++c) m = fmaxf(m, pr[(size_t)c * rows_total].x);
+  float z = 0.0f;
+  if (m != kNegInf) {
+#pragma unroll 8
+    for (int c = 0; c < nchunks; ++c) {
+      const float2 pc = pr[(size_t)c * rows_total];
+      z += pc.y * fast_exp2(pc.x - m);  // an empty chunk (-inf, 0) adds 0
     }
   }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    const float m2 = __shfl_xor(m, o);
-    const float z2 = __shfl_xor(z, o);
-    lse2_merge(m, z, m2, z2);
-  }
-  if (row < rows_total && sub == 0) {
-    const int r = row % Rpad;
-    lse[row] = (r >= R || m == kNegInf || !(z > 0.0f)) ? kPosInf : m + log2f(z);
-  }
+  const int r = row % Rpad;
+  lse[row] = (r >= R || m == kNegInf || !(z > 0.0f)) ? kPosInf : m + log2f(z);
 }
 
 // Stored-logits path: s[b,g,j] = scale * sum over the rows of exp2(logit - lse2).
@@ -921,8 +919,8 @@ hipError_t launch_window_scores(const WsArgs& a, const WsPlan& plan, hipStream_t
     p.row0 = c * rows_per_launch;
     run(false);
   }
-  ws_merge_kernel<<<(p.rows_total + 15) / 16, 256, 0, st>>>(p.part, p.lse, p.rows_total, plan.Rpad, plan.R,
-                                                            plan.nchunks);
+  ws_merge_kernel<<<(p.rows_total + 63) / 64, 64, 0, st>>>(p.part, p.lse, p.rows_total, plan.Rpad, plan.R,
+                                                           plan.nchunks);
   const float scale_all = 1.0f / (float)(a.H * a.w);
   if (plan.store) {
     const dim3 g2((a.S + 255) / 256, a.reduce ? 1 : a.Hkv, a.B);

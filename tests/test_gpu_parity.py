@@ -54,6 +54,11 @@ CASES = [
     ("w8_d64_holes_chan", 2, 32, 8, 900, 64, 64, "bf16", 0, 1, 0.2, 32, 1.0),
     ("w8_short_s70", 1, 32, 8, 70, 128, 64, "bf16", 0, 1, 0.0, 0, 1.0),
     ("w8_long_s9000_allheads", 1, 8, 2, 9000, 128, 64, "bf16", 1, 1, 0.0, 0, 2.0),
+    # kept key channels on 2, 4 and 8 waves, down to a single kept channel
+    ("chan_nw2_holes", 2, 8, 2, 900, 128, 16, "bf16", 0, 1, 0.25, 40, 1.0),
+    ("chan_nw4_allheads", 1, 16, 4, 1300, 128, 32, "bf16", 1, 1, 0.0, 64, 2.0),
+    ("chan_d1", 1, 32, 8, 500, 128, 64, "bf16", 0, 1, 0.0, 1, 1.0),
+    ("chan_d65", 1, 32, 8, 400, 128, 64, "bf16", 0, 1, 0.0, 65, 1.0),
 ]
 
 
