@@ -138,7 +138,7 @@ def wl_snapkv_32k(c: Ctx) -> dict:
         ly["k_out"] = c.empty((B, Hkv, keep, D), torch.bfloat16)
         ly["v_out"] = c.empty((B, Hkv, keep, D), torch.bfloat16)
         ly["ws"] = c.empty(ws_bytes, torch.uint8)
-        ly["tk_ws"] = c.empty(256, torch.uint8)
+        ly["tk_ws"] = c.empty(L.topk_ws_bytes(B * Hkv, S), torch.uint8)
         ly["calls"] = [L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st, reduce=L.KVC_REDUCE_GROUP,
                                             causal=True),
                        L.bind_topk_select(ly["scores"], keep, w, ly["idx"], ly["tk_ws"], st),
@@ -204,7 +204,7 @@ def wl_tova(c: Ctx, cfg, gen, dtype, tdtype) -> dict:
         ly["k_out"] = c.empty((B, Hkv, keep, D), tdtype)
         ly["v_out"] = c.empty((B, Hkv, keep, D), tdtype)
         ly["ws"] = c.empty(ws_bytes, torch.uint8)
-        ly["tk_ws"] = c.empty(256, torch.uint8)
+        ly["tk_ws"] = c.empty(L.topk_ws_bytes(B * Hkv, S), torch.uint8)
         ly["calls"] = [L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st,
                                             reduce=L.KVC_REDUCE_ALL_HEADS, causal=False),
                        L.bind_topk_select(ly["scores"], keep, 0, ly["idx"], ly["tk_ws"], st),
@@ -266,7 +266,7 @@ def wl_think_128k(c: Ctx) -> dict:
         ly["k_out"] = c.empty((B, Hkv, keep, D), torch.bfloat16)
         ly["v_out"] = c.empty((B, Hkv, keep, D), torch.bfloat16)
         ly["ws"] = c.empty(max(ws_bytes, cs_bytes), torch.uint8)
-        ly["tk_ws"] = c.empty(256, torch.uint8)
+        ly["tk_ws"] = c.empty(max(L.topk_ws_bytes(B * Hkv, D), L.topk_ws_bytes(B * Hkv, S)), torch.uint8)
         ly["calls"] = [L.bind_channel_scores(ly["q"], ly["k"], ly["cs"], ly["ws"], st),
                        L.bind_topk_select(ly["cs"], dk, 0, ly["ch"], ly["tk_ws"], st),
                        L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st, chan_idx=ly["ch"],
@@ -326,7 +326,7 @@ def wl_scissor_decode(c: Ctx) -> dict:
         ly["frac"] = c.empty((B, Hkv, C), torch.float32)
         ly["ev"] = c.empty((B, Hkv, cfg.n_evict), torch.int32)
         ly["ws"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, C, D, 1), torch.uint8)
-        ly["tk_ws"] = c.empty(256, torch.uint8)
+        ly["tk_ws"] = c.empty(L.topk_ws_bytes(B * Hkv, C), torch.uint8)
         layers.append(ly)
     s0 = c.streams[0]
     for i, ly in enumerate(layers):

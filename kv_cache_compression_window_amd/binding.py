@@ -181,6 +181,13 @@ def kvc_channel_scores(q, k, out=None, ws=None, stream=None):
     return out
 
 
+def topk_ws_bytes(rows, n) -> int:
+    """Workspace bytes kvc_topk_select needs for rows of n scores."""
+    nb = ctypes.c_size_t(0)
+    _check("kvc_topk_select", LIB.kvc_topk_select(None, rows, n, 0, 0, None, None, ctypes.byref(nb), None))
+    return nb.value
+
+
 def kvc_topk_select(scores, k, n_tail=0, idx=None, ws=None, stream=None):
     """idx [..., k] int32 (ascending) of each row of scores [..., n]."""
     if not scores.is_contiguous() or scores.dtype != torch.float32 or not scores.is_cuda:

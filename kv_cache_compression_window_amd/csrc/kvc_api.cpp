@@ -151,7 +151,7 @@ kvc_status kvc_topk_select(const float* scores, int32_t rows, int32_t n, int32_t
   if (rows == 0 || k == 0) return KVC_OK;
   if (!scores || !idx) return KVC_ERR_NULL;
   if (misaligned4(scores) || misaligned4(idx)) return KVC_ERR_ALIGN;
-  return hip_status(kvc::launch_topk(scores, rows, n, k, n_tail, idx, stream));
+  return hip_status(kvc::launch_topk(scores, rows, n, k, n_tail, idx, ws, stream));
 }
 
 kvc_status kvc_gather_compact(const kvc_shape* sh, kvc_dtype dt, const void* k, const void* v, const int32_t* idx,

@@ -33,7 +33,7 @@ struct CsArgs {
 };
 hipError_t launch_channel_scores(const CsArgs& a, const CsPlan& plan, hipStream_t st);
 
-hipError_t launch_topk(const float* scores, int rows, int n, int k, int n_tail, int32_t* idx,
+hipError_t launch_topk(const float* scores, int rows, int n, int k, int n_tail, int32_t* idx, void* ws,
                        hipStream_t st);
 
 struct GatherArgs {

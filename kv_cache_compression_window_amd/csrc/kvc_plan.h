@@ -87,12 +87,37 @@ inline void cs_make_plan(int B, int Hkv, int S, int D, CsPlan* p) {
   p->bytes = align256((size_t)bg * p->nchunks * D * sizeof(float));
 }
 
-// kvc_topk_select needs no workspace beyond a small fixed area (kept so the
-// signature can grow a multi-workgroup select without an ABI change).
+// kvc_topk_select: rows of at most kTopkResident positions are selected by one
+// workgroup each (no workspace beyond a small fixed area).  Longer rows are cut
+// into slices of kTopkSlice positions, one workgroup each; the workspace holds
+// per row three global digit histograms and the selection state, and per slice
+// the counts above and at the threshold.
+constexpr int kTopkResident = 32768;
+constexpr int kTopkSlice = 4096;
+constexpr int kTopkBins = 2048;  // bins of the widest digit
+
+struct TkPlan {
+  int nslices;
+  size_t off_hist, off_state, off_cnt, bytes;
+};
+
+inline void topk_make_plan(int rows, int n, TkPlan* p) {
+  p->nslices = (n + kTopkSlice - 1) / kTopkSlice;
+  size_t off = 0;
+  p->off_hist = off;
+  off += align256((size_t)rows * 3 * kTopkBins * sizeof(uint32_t));
+  p->off_state = off;
+  off += align256((size_t)rows * 8 * sizeof(uint32_t));
+  p->off_cnt = off;
+  off += align256((size_t)rows * p->nslices * 2 * sizeof(uint32_t));
+  p->bytes = off;
+}
+
 inline size_t topk_ws_bytes(int rows, int n) {
-  (void)rows;
-  (void)n;
-  return 256;
+  if (n <= kTopkResident) return 256;
+  TkPlan p;
+  topk_make_plan(rows, n, &p);
+  return p.bytes;
 }
 
 }  // namespace kvc

@@ -334,10 +334,286 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rows longer than one resident tile: slices of kTopkSlice positions, one
+// 256-thread workgroup each, in six launches per call:
+//   zero   the three global digit histograms of every row; write the tail;
+//   hist q (q = 0, 1, 2)  find the bin of digit q-1 in its global histogram
+//          (so every slice knows the selected high bits), then count digit q of
+//          the slice's keys that carry those bits into LDS and add the nonzero
+//          bins to the row's global histogram;
+//   count  find the last bin: the threshold key T and the number of keys equal
+//          to T to take; count the slice's keys above and at T;
+//   write  the slice's first output slot is the sum of the counts of the
+//          earlier slices; its kept positions follow in order.
+// The digits are fixed (key bits 31..21, 20..10, 9..0), so three passes always
+// reach the exact T.  Slice 0 of each pass leaves the selection state in the
+// workspace for the next launch.
+// ---------------------------------------------------------------------------
+constexpr int SNT = 256;
+constexpr int SWAVE = SNT / 64;
+constexpr int SKPT = kTopkSlice / SNT;  // keys per thread
+static_assert(SKPT * SNT == kTopkSlice, "slices split evenly over the threads");
+static_assert(kTopkBins == NBIN, "the widest digit has 11 bits");
+
+__host__ __device__ constexpr int split_shift(int q) { return q == 0 ? 21 : q == 1 ? 10 : 0; }
+__host__ __device__ constexpr int split_bits(int q) { return q == 2 ? 10 : 11; }
+
+// Scan and reduction scratch of a slice workgroup.
+struct SplitScan {
+  uint32_t wave_tot[SWAVE];
+  uint32_t bucket, krem, red[2 * SWAVE];
+};
+
+// Inclusive scan over the 256 threads in thread order.
+__device__ inline uint32_t split_inclusive_scan(SplitScan& sh, uint32_t x, int lane, int wave) {
+  const uint32_t winc = wave_inclusive_scan(x);
+  if (lane == 63) sh.wave_tot[wave] = winc;
+  __syncthreads();
+  uint32_t before = 0u;
+#pragma unroll
+  for (int v = 0; v < SWAVE; ++v) before += v < wave ? sh.wave_tot[v] : 0u;
+  __syncthreads();
+  return before + winc;
+}
+
+// After digit pass q with its global histogram gh (nb bins): the bin where the
+// count, summed from the top bin down, reaches krem, and the rank still to take
+// inside it.  Thread t owns bins nb-1-bpt*t .. nb-bpt-bpt*t (descending), so
+// the scan in thread order is the suffix sum and one thread sees it cross krem.
+__device__ inline void split_find_bin(SplitScan& sh, const uint32_t* gh, int nb, uint32_t krem, int tid, int lane,
+                                      int wave, uint32_t* bucket, uint32_t* krem_out) {
+  const int bpt = nb / SNT;
+  uint32_t c[NBIN / SNT];
+  uint32_t local = 0u;
+#pragma unroll
+  for (int j = 0; j < NBIN / SNT; ++j) {
+    c[j] = j < bpt ? gh[nb - 1 - bpt * tid - j] : 0u;
+    local += c[j];
+  }
+  const uint32_t incl = split_inclusive_scan(sh, local, lane, wave);
+  const uint32_t excl = incl - local;
+  if (excl < krem && incl >= krem) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int j = 0; j < NBIN / SNT; ++j) {
+      if (j < bpt && acc < krem && acc + c[j] >= krem) {
+        sh.bucket = (uint32_t)(nb - 1 - bpt * tid - j);
+        sh.krem = krem - acc;
+      }
+      acc += c[j];
+    }
+  }
+  __syncthreads();
+  *bucket = sh.bucket;
+  *krem_out = sh.krem;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(SNT) void topk_split_zero_kernel(uint32_t* __restrict__ hist, int32_t* __restrict__ idx,
+                                                              int k, int kp, int E, int n_tail) {
+  const size_t row = blockIdx.x;
+  uint4* gh = reinterpret_cast<uint4*>(hist + row * 3 * kTopkBins);
+  for (int i = threadIdx.x; i < 3 * kTopkBins / 4; i += SNT) gh[i] = make_uint4(0u, 0u, 0u, 0u);
+  int32_t* out = idx + row * (size_t)k;
+  for (int i = threadIdx.x; i < n_tail; i += SNT) out[kp + i] = E + i;
+}
+
+template <int PASS>
+__global__ __launch_bounds__(SNT) void topk_split_hist_kernel(const float* __restrict__ scores, int n, int E, int kp,
+                                                              uint32_t* __restrict__ hist,
+                                                              uint32_t* __restrict__ state) {
+  __shared__ SplitScan sh;
+  __shared__ __attribute__((aligned(16))) uint32_t lds_hist[NBIN * NCOPY];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t row = blockIdx.y;
+  const int slice = blockIdx.x;
+  const float* s = scores + row * (size_t)n;
+  uint32_t* gh = hist + row * 3 * kTopkBins;
+  uint32_t* st = state + row * 8;
+
+  uint32_t prefix = 0u, krem = (uint32_t)kp;  // selected high bits, rank still to take
+  if constexpr (PASS >= 1) {
+    if constexpr (PASS == 2) {
+      prefix = st[0];
+      krem = st[1];
+    }
+    uint32_t b, kr;
+    split_find_bin(sh, gh + (PASS - 1) * kTopkBins, 1 << split_bits(PASS - 1), krem, tid, lane, wave, &b, &kr);
+    prefix |= b << split_shift(PASS - 1);
+    krem = kr;
+    if (slice == 0 && tid == 0) {
+      st[2 * (PASS - 1)] = prefix;
+      st[2 * (PASS - 1) + 1] = krem;
+    }
+  }
+  constexpr int NB = 1 << split_bits(PASS), SHIFT = split_shift(PASS);
+  constexpr uint32_t HI = PASS == 0 ? 0u : ~0u << (SHIFT + split_bits(PASS));  // bits fixed before this pass
+#pragma unroll
+  for (int j = 0; j < NB * NCOPY / 4 / SNT; ++j)
+    reinterpret_cast<uint4*>(lds_hist)[j * SNT + tid] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  const int base = slice * kTopkSlice;
+  const int cp = lane & (NCOPY - 1);
+  uint32_t key[SKPT];
+#pragma unroll
+  for (int j = 0; j < SKPT; ++j) key[j] = float_key(s[min(base + j * SNT + tid, E - 1)]);
+#pragma unroll
+  for (int j = 0; j < SKPT; ++j)
+    if (base + j * SNT + tid < E && (key[j] & HI) == prefix)
+      atomicAdd(&lds_hist[((key[j] >> SHIFT) & (NB - 1)) * NCOPY + cp], 1u);
+  __syncthreads();
+  for (int b = tid; b < NB; b += SNT) {
+    const uint4* h = reinterpret_cast<const uint4*>(&lds_hist[b * NCOPY]);
+    const uint4 h0 = h[0], h1 = h[1];
+    const uint32_t c = h0.x + h0.y + h0.z + h0.w + h1.x + h1.y + h1.z + h1.w;
+    if (c) atomicAdd(&gh[PASS * kTopkBins + b], c);
+  }
+}
+
+__global__ __launch_bounds__(SNT) void topk_split_count_kernel(const float* __restrict__ scores, int n, int E,
+                                                               const uint32_t* __restrict__ hist,
+                                                               uint32_t* __restrict__ state,
+                                                               uint32_t* __restrict__ cnt, int nslices) {
+  __shared__ SplitScan sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t row = blockIdx.y;
+  const int slice = blockIdx.x;
+  const float* s = scores + row * (size_t)n;
+  uint32_t* st = state + row * 8;
+  uint32_t b, take_eq;
+  split_find_bin(sh, hist + row * 3 * kTopkBins + 2 * kTopkBins, 1 << split_bits(2), st[3], tid, lane, wave, &b,
+                 &take_eq);
+  const uint32_t T = st[2] | b;  // key of the kp-th largest eligible score
+  if (slice == 0 && tid == 0) {
+    st[4] = T;
+    st[5] = take_eq;
+  }
+  const int base = slice * kTopkSlice;
+  uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+  for (int j = 0; j < SKPT; ++j) {
+    const int p = base + j * SNT + tid;
+    const uint32_t key = float_key(s[min(p, E - 1)]);
+    gt += (p < E && key > T) ? 1u : 0u;
+    eq += (p < E && key == T) ? 1u : 0u;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    gt += (uint32_t)__shfl_xor(gt, o);
+    eq += (uint32_t)__shfl_xor(eq, o);
+  }
+  if (lane == 0) {
+    sh.red[2 * wave] = gt;
+    sh.red[2 * wave + 1] = eq;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t g = 0u, e = 0u;
+#pragma unroll
+    for (int v = 0; v < SWAVE; ++v) {
+      g += sh.red[2 * v];
+      e += sh.red[2 * v + 1];
+    }
+    cnt[(row * nslices + slice) * 2] = g;
+    cnt[(row * nslices + slice) * 2 + 1] = e;
+  }
+}
+
+__global__ __launch_bounds__(SNT) void topk_split_write_kernel(const float* __restrict__ scores, int n, int E, int k,
+                                                               int kp, const uint32_t* __restrict__ state,
+                                                               const uint32_t* __restrict__ cnt, int nslices,
+                                                               int32_t* __restrict__ idx) {
+  __shared__ SplitScan sh;
+  __shared__ uint32_t lds_xpose[kTopkSlice + kTopkSlice / 32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t row = blockIdx.y;
+  const int slice = blockIdx.x;
+  const float* s = scores + row * (size_t)n;
+  int32_t* out = idx + row * (size_t)k;
+  const uint32_t T = state[row * 8 + 4], take_eq = state[row * 8 + 5];
+
+  // counts of the earlier slices
+  uint32_t gt_b = 0u, eq_b = 0u;
+  for (int i = tid; i < slice; i += SNT) {
+    gt_b += cnt[(row * nslices + i) * 2];
+    eq_b += cnt[(row * nslices + i) * 2 + 1];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    gt_b += (uint32_t)__shfl_xor(gt_b, o);
+    eq_b += (uint32_t)__shfl_xor(eq_b, o);
+  }
+  if (lane == 0) {
+    sh.red[2 * wave] = gt_b;
+    sh.red[2 * wave + 1] = eq_b;
+  }
+  // the slice's keys, loaded in coalesced order and handed to their owners
+  // (thread t takes positions base + 16t .. base + 16t + 15)
+  const int base = slice * kTopkSlice;
+#pragma unroll
+  for (int j = 0; j < SKPT; ++j) {
+    const int q = j * SNT + tid;
+    lds_xpose[xpose_idx(q)] = float_key(s[min(base + q, E - 1)]);
+  }
+  __syncthreads();
+  gt_b = 0u;
+  eq_b = 0u;
+#pragma unroll
+  for (int v = 0; v < SWAVE; ++v) {
+    gt_b += sh.red[2 * v];
+    eq_b += sh.red[2 * v + 1];
+  }
+  const int p0 = base + tid * SKPT;
+  uint32_t u[SKPT];
+#pragma unroll
+  for (int i = 0; i < SKPT; ++i) u[i] = lds_xpose[xpose_idx(tid * SKPT + i)];
+  uint32_t c = 0u;
+#pragma unroll
+  for (int i = 0; i < SKPT; ++i) {
+    const bool ok = p0 + i < E;
+    c += (ok && u[i] > T ? 1u : 0u) + (ok && u[i] == T ? 0x10000u : 0u);
+  }
+  // a slice holds at most 4096 keys, so neither 16-bit half carries
+  const uint32_t ex = split_inclusive_scan(sh, c, lane, wave) - c;
+  gt_b += ex & 0xFFFFu;
+  eq_b += ex >> 16;
+#pragma unroll
+  for (int i = 0; i < SKPT; ++i) {
+    const bool ok = p0 + i < E;
+    const bool gt = ok && u[i] > T, eq = ok && u[i] == T;
+    if (gt || (eq && eq_b < take_eq)) {
+      const uint32_t pos = gt_b + min(eq_b, take_eq);
+      if (pos < (uint32_t)kp) out[pos] = p0 + i;  // pos < kp holds; the guard keeps writes in the row
+    }
+    gt_b += gt;
+    eq_b += eq;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_topk(const float* scores, int rows, int n, int k, int n_tail, int32_t* idx, hipStream_t st) {
+hipError_t launch_topk(const float* scores, int rows, int n, int k, int n_tail, int32_t* idx, void* ws,
+                       hipStream_t st) {
   const int E = n - n_tail;
+  const int kp = k - n_tail;
+  if (E > kTopkResident && kp > 0 && kp < E && rows <= 65535) {
+    TkPlan plan;
+    topk_make_plan(rows, n, &plan);
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(w + plan.off_hist);
+    uint32_t* state = reinterpret_cast<uint32_t*>(w + plan.off_state);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(w + plan.off_cnt);
+    const int ns = (E + kTopkSlice - 1) / kTopkSlice;  // at most plan.nslices
+    const dim3 g(ns, rows);
+    topk_split_zero_kernel<<<rows, SNT, 0, st>>>(hist, idx, k, kp, E, n_tail);
+    topk_split_hist_kernel<0><<<g, SNT, 0, st>>>(scores, n, E, kp, hist, state);
+    topk_split_hist_kernel<1><<<g, SNT, 0, st>>>(scores, n, E, kp, hist, state);
+    topk_split_hist_kernel<2><<<g, SNT, 0, st>>>(scores, n, E, kp, hist, state);
+    topk_split_count_kernel<<<g, SNT, 0, st>>>(scores, n, E, hist, state, cnt, plan.nslices);
+    topk_split_write_kernel<<<g, SNT, 0, st>>>(scores, n, E, k, kp, state, cnt, plan.nslices, idx);
+    return hipGetLastError();
+  }
   if (E <= NTH * 4)
     topk_kernel<4, true><<<rows, NTH, 0, st>>>(scores, n, k, n_tail, idx);
   else if (E <= NTH * 8)

@@ -121,6 +121,25 @@ def test_topk_validation(lib):
     assert f(FAKE, 0, 100, 10, 0, FAKE, FAKE, ctypes.byref(n), None) == 0  # no rows: no-op
 
 
+def test_topk_workspace_long_rows(lib):
+    f = lib.LIB.kvc_topk_select
+
+    def query(rows, n):
+        nb = ctypes.c_size_t(0)
+        assert f(None, rows, n, 1, 0, None, None, ctypes.byref(nb), None) == 0
+        return nb.value
+
+    # rows of at most 32768 scores: one workgroup each, a small fixed area
+    assert query(8, 32768) == query(1, 100)
+    # longer rows: three 2048-bin digit histograms per row and two counts per
+    # 4096-position slice
+    big = query(8, 131072)
+    assert big >= 8 * 3 * 2048 * 4 + 8 * 32 * 2 * 4
+    assert query(16, 131072) > big and query(8, 262144) > big
+    small = ctypes.c_size_t(query(8, 32768))
+    assert f(FAKE, 8, 131072, 100, 0, FAKE, FAKE, ctypes.byref(small), None) == 5
+
+
 def test_gather_and_channel_validation(lib):
     S = lib.KvcShape
     sh = S(1, 8, 8, 4096, 128, 1)

@@ -65,7 +65,7 @@ def test_c2_snapkv_32k_full():
     ko = torch.empty((p.B, p.Hkv, cfg.keep, p.D), dtype=torch.bfloat16, device="cuda")
     vo = torch.empty_like(ko)
     ws = torch.empty(L.window_scores_ws_bytes(p.B, p.H, p.Hkv, p.S, p.D, p.w), dtype=torch.uint8, device="cuda")
-    tk_ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    tk_ws = torch.empty(L.topk_ws_bytes(p.B * p.Hkv, p.S), dtype=torch.uint8, device="cuda")
     # the same pre-bound calls as the timed loop
     L.bind_window_scores(q, k, scores, ws, st, reduce=L.KVC_REDUCE_GROUP, causal=True)()
     L.bind_topk_select(scores, cfg.keep, cfg.n_tail, idx, tk_ws, st)()

@@ -100,7 +100,11 @@ def test_window_scores(case):
     # register-resident limit, one past it, and ties that straddle tiles
     (2, 32768, 1000, 0, 1), (3, 32769, 2000, 0, 3), (2, 70000, 30000, 7, 2), (1, 98304, 40000, 0, 0),
     # 16 keys per thread, rows not 16-byte aligned, threshold at the smallest value with pad slots
-    (3, 12000, 3000, 0, 5), (3, 30001, 5000, 1, 0), (2, 20000, 15000, 0, 2), (4, 8191, 4000, 3, 2)])
+    (3, 12000, 3000, 0, 5), (3, 30001, 5000, 1, 0), (2, 20000, 15000, 0, 2), (4, 8191, 4000, 3, 2),
+    # rows cut into 4096-position slices: one kept, all but one, nothing left to
+    # select (k == n_tail), all kept, one value everywhere, -inf holes, odd length
+    (3, 50000, 1, 0, 0), (2, 45000, 44999, 0, 0), (2, 40000, 100, 100, 0), (1, 40064, 40064, 64, 0),
+    (2, 50000, 7000, 5, 1), (3, 80000, 5000, 0, 401), (2, 65537, 8000, 3, 0)])
 def test_topk(rows, n, k, n_tail, levels):
     say(f"topk rows={rows} n={n} k={k} tail={n_tail} levels={levels}")
     s = synth.random_scores(rows * 7 + n, rows, n, levels)
@@ -118,13 +122,14 @@ def test_topk(rows, n, k, n_tail, levels):
 def test_topk_signed_zeros():
     """Mixed-sign scores with exact +0 and -0 (equal, so the lower index wins)."""
     say("topk signed zeros")
-    s = synth.random_scores(77, 4, 3000, 0) - np.float32(0.5)
-    s[:, 5::9] = np.float32(0.0)
-    s[:, 9::9] = np.float32(-0.0)
-    for k, tail in ((1, 0), (700, 3), (2990, 3)):
-        idx = lib().kvc_topk_select(dev(s), k, tail)
-        torch.cuda.synchronize()
-        assert np.array_equal(idx.cpu().numpy().astype(np.int64), O.topk_select(s.astype(np.float64), k, tail))
+    for n, cases in ((3000, ((1, 0), (700, 3), (2990, 3))), (70000, ((1, 0), (30000, 3), (69990, 3)))):
+        s = synth.random_scores(77, 4, n, 0) - np.float32(0.5)
+        s[:, 5::9] = np.float32(0.0)
+        s[:, 9::9] = np.float32(-0.0)
+        for k, tail in cases:
+            idx = lib().kvc_topk_select(dev(s), k, tail)
+            torch.cuda.synchronize()
+            assert np.array_equal(idx.cpu().numpy().astype(np.int64), O.topk_select(s.astype(np.float64), k, tail))
 
 
 @pytest.mark.parametrize("dt,D,chan", [("bf16", 128, True), ("bf16", 64, False), ("f32", 128, True),
