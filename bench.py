@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="distinct layers rotated per step")
-    ap.add_argument("--streams", type=int, default=2,
+    ap.add_argument("--streams", type=int, default=3,
                     help="layers are spread round-robin over this many streams in the timed region")
     ap.add_argument("--kernel-reps", type=int, default=20,
                     help="passes over the layers in which each call of the dominant kernel is timed alone")
