@@ -34,9 +34,9 @@ METRIC = "KV tokens scored+pruned/s per layer (32k ctx, GQA 32/8) + % of HBM roo
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_window_scores_snapkv_32k.json")
 SCORE_SOURCES = ["window_scores.hip", "kvc_device.h", "kvc_plan.h"]
-WORKLOADS = ["snapkv_32k", "tova_tiny", "tova_batched", "scissor_decode", "think_128k"]
+WORKLOADS = ["snapkv_32k", "tova_tiny", "tova_batched", "scissor_decode", "think_128k", "think_128k_kc"]
 DEFAULT_STEPS = {"snapkv_32k": (100, 10), "tova_tiny": (200, 20), "tova_batched": (20, 3),
-                 "scissor_decode": (800, 0), "think_128k": (10, 2)}
+                 "scissor_decode": (800, 0), "think_128k": (10, 2), "think_128k_kc": (10, 2)}
 
 
 def score_kernel_hash() -> str:
@@ -155,6 +155,10 @@ def wl_snapkv_32k(c: Ctx) -> dict:
     # by the top-k, indices written and read, kept K and V read and written
     k_bytes, q_bytes, s_bytes = B * Hkv * S * D * 2, B * H * w * D * 2, B * Hkv * S * 4
     i_bytes, g_bytes = B * Hkv * keep * 4, 2 * 2 * B * Hkv * keep * D * 2
+    if compress:
+        # kept K channels read and written, V rows read and written, the window
+        # queries' kept channels read and written
+        g_bytes = 2 * B * Hkv * keep * dk * 2 + 2 * B * Hkv * keep * D * 2 + 2 * B * H * w * dk * 2
     layer_bytes = k_bytes + q_bytes + 2 * s_bytes + 2 * i_bytes + g_bytes
 
     def cpu(budget):
@@ -245,7 +249,10 @@ def wl_tova(c: Ctx, cfg, gen, dtype, tdtype) -> dict:
                 config={"B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep})
 
 
-def wl_think_128k(c: Ctx) -> dict:
+def wl_think_128k(c: Ctx, compress: bool = False) -> dict:
+    """ThinK + SnapKV at 128k.  compress: the kept keys are stored with their
+    64 kept channels only and the window queries are cut to the same channels
+    (the page's options 3b/3c) instead of zero-filled 128-channel keys (3a)."""
     L, torch, cfg = c.L, c.torch, c.configs.THINK_128K
     B, H, Hkv, S, D, w, keep, dk = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.w, cfg.keep, cfg.d_keep
     nl = c.args.layers or cfg.layers
@@ -263,7 +270,7 @@ def wl_think_128k(c: Ctx) -> dict:
         ly["ch"] = c.empty((B, Hkv, dk), torch.int32)
         ly["scores"] = c.empty((B, Hkv, S), torch.float32)
         ly["idx"] = c.empty((B, Hkv, keep), torch.int32)
-        ly["k_out"] = c.empty((B, Hkv, keep, D), torch.bfloat16)
+        ly["k_out"] = c.empty((B, Hkv, keep, dk if compress else D), torch.bfloat16)
         ly["v_out"] = c.empty((B, Hkv, keep, D), torch.bfloat16)
         ly["ws"] = c.empty(max(ws_bytes, cs_bytes), torch.uint8)
         ly["tk_ws"] = c.empty(max(L.topk_ws_bytes(B * Hkv, D), L.topk_ws_bytes(B * Hkv, S)), torch.uint8)
@@ -271,9 +278,14 @@ def wl_think_128k(c: Ctx) -> dict:
                        L.bind_topk_select(ly["cs"], dk, 0, ly["ch"], ly["tk_ws"], st),
                        L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st, chan_idx=ly["ch"],
                                             reduce=L.KVC_REDUCE_GROUP, causal=True),
-                       L.bind_topk_select(ly["scores"], keep, w, ly["idx"], ly["tk_ws"], st),
-                       L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st,
-                                             chan_idx=ly["ch"])]
+                       L.bind_topk_select(ly["scores"], keep, w, ly["idx"], ly["tk_ws"], st)]
+        if compress:
+            ly["q_c"] = c.empty((B, H, w, dk), torch.bfloat16)
+            ly["calls"] += [L.bind_gather_compress(ly["k"], ly["v"], ly["idx"], ly["ch"], ly["k_out"], ly["v_out"], st),
+                            L.bind_query_channels(ly["q"], ly["ch"], ly["q_c"], st)]
+        else:
+            ly["calls"].append(L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st,
+                                                     chan_idx=ly["ch"]))
         ly["kcall"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], s0, chan_idx=ly["ch"],
                                            reduce=L.KVC_REDUCE_GROUP, causal=True)
 
@@ -286,6 +298,10 @@ def wl_think_128k(c: Ctx) -> dict:
     # written and read, kept K and V read and written
     k_bytes, q_bytes, s_bytes = B * Hkv * S * D * 2, B * H * w * D * 2, B * Hkv * S * 4
     i_bytes, g_bytes = B * Hkv * keep * 4, 2 * 2 * B * Hkv * keep * D * 2
+    if compress:
+        # kept K channels read and written, V rows read and written, the window
+        # queries' kept channels read and written
+        g_bytes = 2 * B * Hkv * keep * dk * 2 + 2 * B * Hkv * keep * D * 2 + 2 * B * H * w * dk * 2
     layer_bytes = k_bytes + q_bytes + 2 * s_bytes + 2 * i_bytes + g_bytes
 
     def cpu(budget):
@@ -296,7 +312,11 @@ def wl_think_128k(c: Ctx) -> dict:
         def one(n):
             g = n % Hkv
             _, ch, s, idx = O.think_snapkv(q64[:, g * G:(g + 1) * G], k64[:, g:g + 1], dk, keep)
-            O.gather_compact(host0.k[:, g:g + 1], host0.v[:, g:g + 1], idx, chan_keep=ch)
+            if compress:
+                O.gather_compress(host0.k[:, g:g + 1], host0.v[:, g:g + 1], idx, ch)
+                O.query_channels(host0.q[:, g * G:(g + 1) * G], ch)
+            else:
+                O.gather_compact(host0.k[:, g:g + 1], host0.v[:, g:g + 1], idx, chan_keep=ch)
         n, el = timed_oracle(one, budget)
         return {"value": round(B * S * n / Hkv / el, 1), "unit": "tokens/s", "cores": blas_threads(),
                 "kind": "oracle", "sample": f"{n} KV heads (of {Hkv} per layer) of layer 0, S={S}, fp64 numpy "
@@ -304,9 +324,10 @@ def wl_think_128k(c: Ctx) -> dict:
     return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes,
                 kernel=("kvc_window_scores with 64 of 128 key channels (pass 1 + merge + pass 2)",
                         [ly["kcall"] for ly in layers], k_bytes + q_bytes + s_bytes, None),
-                cpu=cpu, metric=f"KV tokens scored+pruned/s per layer ({cfg.name})", unit="tokens/s", dtype="bf16",
-                workload=cfg.name, config={"B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep,
-                                           "d_keep": dk})
+                cpu=cpu, metric=f"KV tokens scored+pruned/s per layer ({cfg.name}{'_kc' if compress else ''})",
+                unit="tokens/s", dtype="bf16", workload=cfg.name + ("_kc" if compress else ""),
+                config={"B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep, "d_keep": dk,
+                        "stored_key_channels": dk if compress else D})
 
 
 def wl_scissor_decode(c: Ctx) -> dict:
@@ -402,6 +423,8 @@ def build_workload(c: Ctx) -> dict:
         return wl_tova(c, c.configs.TOVA_BATCHED, c.synth.tova_batched, "bf16", c.torch.bfloat16)
     if wl == "think_128k":
         return wl_think_128k(c)
+    if wl == "think_128k_kc":
+        return wl_think_128k(c, compress=True)
     return wl_scissor_decode(c)
 
 

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 typedef enum {
   KVC_OK = 0,
@@ -199,6 +199,52 @@ kvc_status kvc_topk_select(const float* scores, int32_t rows, int32_t n, int32_t
 kvc_status kvc_gather_compact(const kvc_shape* sh, kvc_dtype dt, const void* k, const void* v,
                               const int32_t* idx, int32_t n_keep, const int32_t* chan_idx,
                               int32_t d_keep, void* k_out, void* v_out, hipStream_t stream);
+
+/*
+ * kvc_gather_compress — compacted cache that stores only the kept key channels
+ * ([THINK] review thread, options 3b and 3c: keep the pruned key cache apart
+ * so that pruning channels also saves their memory).
+ *   k_out[b,g,r,j] = k[b,g,idx[b,g,r],chan_idx[b,g,j]]   for j < d_keep
+ *   v_out[b,g,r,:] = v[b,g,idx[b,g,r],:]                 (V keeps every channel)
+ * A bit copy.  The order of chan_idx is the stored channel order
+ * (kvc_topk_select gives ascending); entries must be in [0, D) (an entry
+ * outside writes 0).
+ *   k, v        [B, Hkv, S, D] (sh->w is ignored); v may be NULL (then v_out is unused).
+ *   idx         [B, Hkv, n_keep] int32 in [0, S) (clamped into range).
+ *   chan_idx    [B, Hkv, d_keep] int32, required, 1 <= d_keep <= D.
+ *   k_out       [B, Hkv, n_keep, d_keep]; k and k_out need element alignment only.
+ *   v_out       [B, Hkv, n_keep, D]; v and v_out 16-byte aligned.
+ * Outputs must not overlap the inputs.
+ */
+kvc_status kvc_gather_compress(const kvc_shape* sh, kvc_dtype dt, const void* k, const void* v,
+                               const int32_t* idx, int32_t n_keep, const int32_t* chan_idx,
+                               int32_t d_keep, void* k_out, void* v_out, hipStream_t stream);
+
+/*
+ * kvc_channel_expand — the zeros added back to a compressed key cache
+ * ([THINK] option 3b: a cache class that restores the pruned channels as zeros
+ * when the keys are used).
+ *   k_full[b,g,r,c] = k_c[b,g,r,j] where chan_idx[b,g,j] == c (the largest such
+ *                     j if an entry repeats), +0.0 for every other channel.
+ *   k_c [B, Hkv, n, d_keep];  chan_idx [B, Hkv, d_keep];  k_full out [B, Hkv, n, D].
+ *   1 <= d_keep <= D, D in {64, 128}; n == 0 is a no-op.  Element alignment.
+ * Expanding kvc_gather_compress's keys gives kvc_gather_compact's, bit for bit.
+ */
+kvc_status kvc_channel_expand(int32_t B, int32_t Hkv, int32_t n, int32_t D, kvc_dtype dt, const void* k_c,
+                              const int32_t* chan_idx, int32_t d_keep, void* k_full, hipStream_t stream);
+
+/*
+ * kvc_query_channels — queries cut to their KV head's kept key channels
+ * ([THINK] option 3c: prune the query the same way, so that attention runs on
+ * the compressed keys; q_c . k_c equals q . k with the pruned key channels
+ * zeroed, up to the order of the sum).
+ *   q_c[b,h,i,j] = q[b,h,i,chan_idx[b, h/G, j]],  G = H / Hkv.
+ *   q [B, H, n, D];  chan_idx [B, Hkv, d_keep];  q_c out [B, H, n, d_keep].
+ *   1 <= d_keep <= D, D in {64, 128}; n == 0 is a no-op.  Element alignment.
+ */
+kvc_status kvc_query_channels(int32_t B, int32_t H, int32_t Hkv, int32_t n, int32_t D, kvc_dtype dt,
+                              const void* q, const int32_t* chan_idx, int32_t d_keep, void* q_c,
+                              hipStream_t stream);
 
 /* Text for a status code (static storage). */
 const char* kvc_status_string(kvc_status s);

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_
 
 # every symbol include/kvc.h declares
 EXPORTS = ["kvc_window_scores", "kvc_scissor_update", "kvc_channel_scores", "kvc_topk_select",
-           "kvc_gather_compact", "kvc_status_string", "kvc_abi_version"]
+           "kvc_gather_compact", "kvc_gather_compress", "kvc_channel_expand", "kvc_query_channels",
+           "kvc_status_string", "kvc_abi_version"]
 
 
 class KvcShape(ctypes.Structure):
@@ -50,6 +51,9 @@ def _load():
         "kvc_channel_scores": [SH, I32, P, P, P, P, SZP, P],
         "kvc_topk_select": [P, I32, I32, I32, I32, P, P, SZP, P],
         "kvc_gather_compact": [SH, I32, P, P, P, I32, P, I32, P, P, P],
+        "kvc_gather_compress": [SH, I32, P, P, P, I32, P, I32, P, P, P],
+        "kvc_channel_expand": [I32, I32, I32, I32, I32, P, P, I32, P, P],
+        "kvc_query_channels": [I32, I32, I32, I32, I32, I32, P, P, I32, P, P],
         "kvc_status_string": [I32],
         "kvc_abi_version": [],
     }
@@ -222,6 +226,49 @@ def kvc_gather_compact(k, v, idx, chan_idx=None, k_out=None, v_out=None, stream=
     return k_out, v_out
 
 
+def kvc_gather_compress(k, v, idx, chan_idx, k_out=None, v_out=None, stream=None):
+    """k_out [B,Hkv,n_keep,d_keep] (kept rows, kept key channels) and v_out
+    [B,Hkv,n_keep,D] (kept rows) of the rows idx [B,Hkv,n_keep]."""
+    _need(k, "k", 4)
+    _need(chan_idx, "chan_idx", 3)
+    B, Hkv, S, D = k.shape
+    n_keep, d_keep = idx.shape[2], chan_idx.shape[2]
+    sh = KvcShape(B, Hkv, Hkv, S, D, 1)
+    if k_out is None:
+        k_out = torch.empty((B, Hkv, n_keep, d_keep), dtype=k.dtype, device=k.device)
+    if v is not None and v_out is None:
+        v_out = torch.empty((B, Hkv, n_keep, D), dtype=v.dtype, device=v.device)
+    _check("kvc_gather_compress", LIB.kvc_gather_compress(ctypes.byref(sh), _dtype_code(k), _ptr(k), _ptr(v),
+                                                          _ptr(idx), n_keep, _ptr(chan_idx), d_keep, _ptr(k_out),
+                                                          _ptr(v_out), _stream(stream)))
+    return k_out, v_out
+
+
+def kvc_channel_expand(k_c, chan_idx, D, k_full=None, stream=None):
+    """k_full [B,Hkv,n,D]: the compressed keys k_c [B,Hkv,n,d_keep] with zeros added back."""
+    _need(k_c, "k_c", 4)
+    _need(chan_idx, "chan_idx", 3)
+    B, Hkv, n, d_keep = k_c.shape
+    if k_full is None:
+        k_full = torch.empty((B, Hkv, n, D), dtype=k_c.dtype, device=k_c.device)
+    _check("kvc_channel_expand", LIB.kvc_channel_expand(B, Hkv, n, D, _dtype_code(k_c), _ptr(k_c), _ptr(chan_idx),
+                                                        d_keep, _ptr(k_full), _stream(stream)))
+    return k_full
+
+
+def kvc_query_channels(q, chan_idx, q_c=None, stream=None):
+    """q_c [B,H,n,d_keep]: each query head's rows q [B,H,n,D] cut to its KV head's kept channels."""
+    _need(q, "q", 4)
+    _need(chan_idx, "chan_idx", 3)
+    B, H, n, D = q.shape
+    Hkv, d_keep = chan_idx.shape[1], chan_idx.shape[2]
+    if q_c is None:
+        q_c = torch.empty((B, H, n, d_keep), dtype=q.dtype, device=q.device)
+    _check("kvc_query_channels", LIB.kvc_query_channels(B, H, Hkv, n, D, _dtype_code(q), _ptr(q), _ptr(chan_idx),
+                                                        d_keep, _ptr(q_c), _stream(stream)))
+    return q_c
+
+
 # ----------------------------------------------------------------------------
 # Pre-bound calls: marshal the arguments once and return a function that makes
 # the C call with them (one foreign call per use).  For loops that launch the
@@ -271,6 +318,25 @@ def bind_gather_compact(k, v, idx, k_out, v_out, stream, chan_idx=None):
             _ptr(k_out), _ptr(v_out), ctypes.c_void_p(stream.cuda_stream))
     call = _bound("kvc_gather_compact", args)
     call.keep_alive = (sh, k, v, idx, chan_idx, k_out, v_out)
+    return call
+
+
+def bind_gather_compress(k, v, idx, chan_idx, k_out, v_out, stream):
+    B, Hkv, S, D = k.shape
+    sh = KvcShape(B, Hkv, Hkv, S, D, 1)
+    args = (ctypes.byref(sh), _dtype_code(k), _ptr(k), _ptr(v), _ptr(idx), idx.shape[2], _ptr(chan_idx),
+            chan_idx.shape[2], _ptr(k_out), _ptr(v_out), ctypes.c_void_p(stream.cuda_stream))
+    call = _bound("kvc_gather_compress", args)
+    call.keep_alive = (sh, k, v, idx, chan_idx, k_out, v_out)
+    return call
+
+
+def bind_query_channels(q, chan_idx, q_c, stream):
+    B, H, n, D = q.shape
+    args = (B, H, chan_idx.shape[1], n, D, _dtype_code(q), _ptr(q), _ptr(chan_idx), chan_idx.shape[2], _ptr(q_c),
+            ctypes.c_void_p(stream.cuda_stream))
+    call = _bound("kvc_query_channels", args)
+    call.keep_alive = (q, chan_idx, q_c)
     return call
 
 

@@ -4,7 +4,9 @@
 // +0.0, and v_out likewise without channel pruning.  Source: "Add ThinK_Press"
 // (kvpress PR 18), option 3a: put zeros in the key cache.
 //
-// One thread moves one 16-byte unit of one row of K and the same unit of V.
+// One thread moves one 16-byte unit of one row of K and the same unit of V
+// (V only when k is NULL: the kept-channel key cache is then written by the
+// channel gathers).
 // Consecutive threads cover consecutive units of a row, so every kept row is
 // read as whole 128-byte lines and the output is written densely.  Output
 // stores are non-temporal: the compacted cache is not read again by this layer.
@@ -45,6 +47,14 @@ __global__ __launch_bounds__(NTH) void gather_kernel(const uint4* __restrict__ k
   const int src = min(max(idx[bg * n_keep + r], 0), S - 1);
   const size_t in_off = (bg * S + src) * UPR + cu;
   const size_t out_off = (bg * n_keep + r) * UPR + cu;
+  if (v) {
+    const uint4 vv = v[in_off];
+    __builtin_nontemporal_store(vv.x, &v_out[out_off].x);
+    __builtin_nontemporal_store(vv.y, &v_out[out_off].y);
+    __builtin_nontemporal_store(vv.z, &v_out[out_off].z);
+    __builtin_nontemporal_store(vv.w, &v_out[out_off].w);
+  }
+  if (!k) return;  // V only
   uint4 kv = k[in_off];
   if (chan_idx) {
     uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
@@ -65,13 +75,6 @@ __global__ __launch_bounds__(NTH) void gather_kernel(const uint4* __restrict__ k
   __builtin_nontemporal_store(kv.y, &k_out[out_off].y);
   __builtin_nontemporal_store(kv.z, &k_out[out_off].z);
   __builtin_nontemporal_store(kv.w, &k_out[out_off].w);
-  if (v) {
-    const uint4 vv = v[in_off];
-    __builtin_nontemporal_store(vv.x, &v_out[out_off].x);
-    __builtin_nontemporal_store(vv.y, &v_out[out_off].y);
-    __builtin_nontemporal_store(vv.z, &v_out[out_off].z);
-    __builtin_nontemporal_store(vv.w, &v_out[out_off].w);
-  }
 }
 
 template <int ESZ, int D>

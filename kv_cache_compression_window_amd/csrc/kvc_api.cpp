@@ -186,4 +186,116 @@ kvc_status kvc_gather_compact(const kvc_shape* sh, kvc_dtype dt, const void* k, 
   return hip_status(kvc::launch_gather(a, stream));
 }
 
+kvc_status kvc_gather_compress(const kvc_shape* sh, kvc_dtype dt, const void* k, const void* v, const int32_t* idx,
+                               int32_t n_keep, const int32_t* chan_idx, int32_t d_keep, void* k_out, void* v_out,
+                               hipStream_t stream) {
+  if (!sh) return KVC_ERR_NULL;
+  if (dt != KVC_F32 && dt != KVC_BF16) return KVC_ERR_DTYPE;
+  kvc_status st = check_shape(sh, false);
+  if (st != KVC_OK) return st;
+  if (n_keep < 0 || n_keep > sh->S || d_keep < 1 || d_keep > sh->D) return KVC_ERR_SHAPE;
+  if (n_keep == 0) return KVC_OK;
+  if (!k || !idx || !chan_idx || !k_out) return KVC_ERR_NULL;
+  if (v && !v_out) return KVC_ERR_NULL;
+  const uintptr_t ea = dt == KVC_BF16 ? 1u : 3u;
+  if ((reinterpret_cast<uintptr_t>(k) & ea) || (reinterpret_cast<uintptr_t>(k_out) & ea) || misaligned4(idx) ||
+      misaligned4(chan_idx) || (v && (misaligned16(v) || misaligned16(v_out))))
+    return KVC_ERR_ALIGN;
+  if ((long long)sh->B * sh->Hkv > 65535) return KVC_ERR_UNSUPPORTED;  // grid y limit
+  if (v) {
+    kvc::GatherArgs g;
+    g.bf16 = dt == KVC_BF16;
+    g.B = sh->B;
+    g.Hkv = sh->Hkv;
+    g.S = sh->S;
+    g.D = sh->D;
+    g.k = nullptr;
+    g.v = v;
+    g.idx = idx;
+    g.n_keep = n_keep;
+    g.chan_idx = nullptr;
+    g.d_keep = 0;
+    g.k_out = nullptr;
+    g.v_out = v_out;
+    const hipError_t e = kvc::launch_gather(g, stream);
+    if (e != hipSuccess) return KVC_ERR_HIP;
+  }
+  kvc::ChanRowsArgs a;
+  a.esz = dt == KVC_BF16 ? 2 : 4;
+  a.groups = sh->B * sh->Hkv;
+  a.H = 0;
+  a.Hkv = sh->Hkv;
+  a.in = k;
+  a.out = k_out;
+  a.idx = idx;
+  a.chan = chan_idx;
+  a.n_rows = n_keep;
+  a.in_rows = sh->S;
+  a.in_ch = sh->D;
+  a.out_ch = d_keep;
+  a.d_keep = d_keep;
+  a.expand = 0;
+  return hip_status(kvc::launch_chan_rows(a, stream));
+}
+
+kvc_status kvc_channel_expand(int32_t B, int32_t Hkv, int32_t n, int32_t D, kvc_dtype dt, const void* k_c,
+                              const int32_t* chan_idx, int32_t d_keep, void* k_full, hipStream_t stream) {
+  if (dt != KVC_F32 && dt != KVC_BF16) return KVC_ERR_DTYPE;
+  if (B < 1 || Hkv < 1 || n < 0) return KVC_ERR_SHAPE;
+  if (D != 64 && D != 128) return KVC_ERR_UNSUPPORTED;
+  if (d_keep < 1 || d_keep > D) return KVC_ERR_SHAPE;
+  if (n == 0) return KVC_OK;
+  if (!k_c || !chan_idx || !k_full) return KVC_ERR_NULL;
+  const uintptr_t ea = dt == KVC_BF16 ? 1u : 3u;
+  if ((reinterpret_cast<uintptr_t>(k_c) & ea) || (reinterpret_cast<uintptr_t>(k_full) & ea) || misaligned4(chan_idx))
+    return KVC_ERR_ALIGN;
+  if ((long long)B * Hkv > 65535) return KVC_ERR_UNSUPPORTED;  // grid y limit
+  kvc::ChanRowsArgs a;
+  a.esz = dt == KVC_BF16 ? 2 : 4;
+  a.groups = B * Hkv;
+  a.H = 0;
+  a.Hkv = Hkv;
+  a.in = k_c;
+  a.out = k_full;
+  a.idx = nullptr;
+  a.chan = chan_idx;
+  a.n_rows = n;
+  a.in_rows = n;
+  a.in_ch = d_keep;
+  a.out_ch = D;
+  a.d_keep = d_keep;
+  a.expand = 1;
+  return hip_status(kvc::launch_chan_rows(a, stream));
+}
+
+kvc_status kvc_query_channels(int32_t B, int32_t H, int32_t Hkv, int32_t n, int32_t D, kvc_dtype dt, const void* q,
+                              const int32_t* chan_idx, int32_t d_keep, void* q_c, hipStream_t stream) {
+  if (dt != KVC_F32 && dt != KVC_BF16) return KVC_ERR_DTYPE;
+  if (B < 1 || H < 1 || Hkv < 1 || n < 0 || H % Hkv != 0) return KVC_ERR_SHAPE;
+  if (D != 64 && D != 128) return KVC_ERR_UNSUPPORTED;
+  if (d_keep < 1 || d_keep > D) return KVC_ERR_SHAPE;
+  if (n == 0) return KVC_OK;
+  if (!q || !chan_idx || !q_c) return KVC_ERR_NULL;
+  const uintptr_t ea = dt == KVC_BF16 ? 1u : 3u;
+  if ((reinterpret_cast<uintptr_t>(q) & ea) || (reinterpret_cast<uintptr_t>(q_c) & ea) || misaligned4(chan_idx))
+    return KVC_ERR_ALIGN;
+  if ((long long)B * H > 65535) return KVC_ERR_UNSUPPORTED;  // grid y limit
+  kvc::ChanRowsArgs a;
+  a.esz = dt == KVC_BF16 ? 2 : 4;
+  a.groups = B * H;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.in = q;
+  a.out = q_c;
+  a.idx = nullptr;
+  a.chan = chan_idx;
+  a.n_rows = n;
+  a.in_rows = n;
+  a.in_ch = D;
+  a.out_ch = d_keep;
+  a.d_keep = d_keep;
+  a.expand = 0;
+  return hip_status(kvc::launch_chan_rows(a, stream));
+}
+
 }  // extern "C"

@@ -48,7 +48,23 @@ struct GatherArgs {
   void* k_out;
   void* v_out;
 };
-hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st);  // k may be NULL (V only)
+
+// Row-wise channel gathers of ThinK's compressed key cache (channels.hip).
+struct ChanRowsArgs {
+  int esz;              // element bytes: 2 (bf16) or 4 (f32)
+  int groups;           // (b, KV head) pairs, or (b, query head) pairs when H > 0
+  int H, Hkv;           // H > 0: group g is query head g % H of batch g / H and uses its KV head's channels
+  const void* in;
+  void* out;
+  const int32_t* idx;   // [groups][n_rows] source rows, or NULL (output row r reads input row r)
+  const int32_t* chan;  // [channel rows][d_keep]
+  int n_rows, in_rows;  // output rows and input rows per group
+  int in_ch, out_ch;    // channels per input and per output row
+  int d_keep;
+  int expand;           // 0: out[j] = in[chan[j]];  1: out[chan[j]] = in[j], other channels +0.0
+};
+hipError_t launch_chan_rows(const ChanRowsArgs& a, hipStream_t st);
 
 struct ScissorArgs {
   int B, Hkv, C, hist_len;

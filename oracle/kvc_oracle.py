@@ -38,6 +38,9 @@ Readings where the pages are silent or garbled (each is used below):
   R17 ThinK squares the per-channel products (as the code does).
   R18 ThinK's per-query-head scores are summed over the GQA group.
   R21 pruned key channels are written as +0.0.
+  R25 a compressed key cache keeps the kept channels in chan_idx order; the
+      zero-back writes them in increasing j, so a repeated entry keeps the
+      last j.
   Rows with no allowed key (every slot a hole) have P = 0.
 
 Parity pins for every function live in tests/test_oracle_pins.py.
@@ -214,6 +217,51 @@ def gather_compact(k: np.ndarray, v: np.ndarray, idx: np.ndarray, chan_keep=None
         k_out = np.where(keep[:, :, None, :], k_out, np.zeros((), dtype=k.dtype))
     v_out = None if v is None else np.take_along_axis(v, idx[..., None], axis=2)
     return k_out, v_out
+
+
+# ----------------------------------------------------------------------------
+# O9: ThinK's compressed key cache (options 3b and 3c)
+# ----------------------------------------------------------------------------
+
+def gather_compress(k: np.ndarray, v, idx: np.ndarray, chan_idx: np.ndarray):
+    """Kept rows with only the kept key channels, in chan_idx order ([THINK]
+    review thread, options 3b/3c: the pruned key cache is stored apart):
+    K'[b,g,r,j] = K[b,g,idx[b,g,r],chan_idx[b,g,j]];  V'[b,g,r] = V[b,g,idx[b,g,r]].
+    Copies stored values bit for bit."""
+    B, Hkv = k.shape[0], k.shape[1]
+    n_keep, d_keep = idx.shape[2], chan_idx.shape[2]
+    k_out = np.empty((B, Hkv, n_keep, d_keep), dtype=k.dtype)
+    for b in range(B):
+        for g in range(Hkv):
+            rows = k[b, g][np.asarray(idx[b, g], dtype=np.int64)]
+            k_out[b, g] = rows[:, np.asarray(chan_idx[b, g], dtype=np.int64)]
+    v_out = None if v is None else np.take_along_axis(v, np.asarray(idx, dtype=np.int64)[..., None], axis=2)
+    return k_out, v_out
+
+
+def channel_expand(k_c: np.ndarray, chan_idx: np.ndarray, D: int) -> np.ndarray:
+    """The zeros added back ([THINK] option 3b): K[b,g,:,chan_idx[b,g,j]] =
+    K_c[b,g,:,j] for each j in increasing order (a repeated entry keeps the
+    last j), every other channel +0."""
+    B, Hkv, n, d_keep = k_c.shape
+    out = np.zeros((B, Hkv, n, D), dtype=k_c.dtype)
+    for b in range(B):
+        for g in range(Hkv):
+            for j in range(d_keep):
+                out[b, g, :, int(chan_idx[b, g, j])] = k_c[b, g, :, j]
+    return out
+
+
+def query_channels(q: np.ndarray, chan_idx: np.ndarray) -> np.ndarray:
+    """Queries cut to their KV head's kept key channels ([THINK] option 3c:
+    prune the query as well): q_c[b,h,i,j] = q[b,h,i,chan_idx[b,h//G,j]]."""
+    B, H = q.shape[0], q.shape[1]
+    G = H // chan_idx.shape[1]
+    out = np.empty(q.shape[:3] + (chan_idx.shape[2],), dtype=q.dtype)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = q[b, h][:, np.asarray(chan_idx[b, h // G], dtype=np.int64)]
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.abi_version() == 1
+    assert lib.abi_version() == 2
     for code in range(8):
         s = lib.LIB.kvc_status_string(code).decode()
         assert s and s != "unknown status"
@@ -119,6 +119,50 @@ def test_topk_validation(lib):
     q = ctypes.c_size_t(0)
     assert f(None, 8, 100, 10, 0, None, None, ctypes.byref(q), None) == 0 and q.value > 0
     assert f(FAKE, 0, 100, 10, 0, FAKE, FAKE, ctypes.byref(n), None) == 0  # no rows: no-op
+
+
+def test_compressed_key_cache_validation(lib):
+    """kvc_gather_compress, kvc_channel_expand and kvc_query_channels reject bad
+    arguments before any launch (only error paths and no-ops are called here)."""
+    sh = lib.KvcShape(1, 8, 8, 100, 128, 1)
+    odd1 = ctypes.c_void_p(0x100001)  # not 2-byte aligned
+    odd2 = ctypes.c_void_p(0x100002)  # 2-byte aligned only
+    f = lib.LIB.kvc_gather_compress
+    shp = ctypes.byref(sh)
+    assert f(None, 1, FAKE, FAKE, FAKE, 10, FAKE, 64, FAKE, FAKE, None) == 1
+    assert f(shp, 1, FAKE, FAKE, FAKE, 10, None, 64, FAKE, FAKE, None) == 1   # chan_idx required
+    assert f(shp, 1, FAKE, FAKE, None, 10, FAKE, 64, FAKE, FAKE, None) == 1
+    assert f(shp, 1, FAKE, FAKE, FAKE, 10, FAKE, 64, FAKE, None, None) == 1   # v without v_out
+    assert f(shp, 5, FAKE, FAKE, FAKE, 10, FAKE, 64, FAKE, FAKE, None) == 3
+    assert f(shp, 1, FAKE, FAKE, FAKE, 10, FAKE, 0, FAKE, FAKE, None) == 2
+    assert f(shp, 1, FAKE, FAKE, FAKE, 10, FAKE, 129, FAKE, FAKE, None) == 2
+    assert f(shp, 1, FAKE, FAKE, FAKE, 101, FAKE, 64, FAKE, FAKE, None) == 2
+    assert f(shp, 1, odd1, FAKE, FAKE, 10, FAKE, 64, FAKE, FAKE, None) == 4
+    assert f(shp, 0, odd2, FAKE, FAKE, 10, FAKE, 64, FAKE, FAKE, None) == 4   # f32 needs 4 bytes
+    assert f(shp, 1, FAKE, ODD, FAKE, 10, FAKE, 64, FAKE, FAKE, None) == 4    # V rows need 16 bytes
+    assert f(ctypes.byref(lib.KvcShape(1, 8, 8, 100, 96, 1)), 1, FAKE, FAKE, FAKE, 10, FAKE, 64, FAKE, FAKE,
+             None) == 6
+    assert f(shp, 1, FAKE, FAKE, FAKE, 0, FAKE, 64, FAKE, FAKE, None) == 0    # nothing to gather
+
+    e = lib.LIB.kvc_channel_expand
+    assert e(1, 8, 10, 96, 1, FAKE, FAKE, 64, FAKE, None) == 6
+    assert e(1, 8, 10, 128, 1, FAKE, FAKE, 0, FAKE, None) == 2
+    assert e(1, 8, 10, 64, 1, FAKE, FAKE, 65, FAKE, None) == 2
+    assert e(0, 8, 10, 128, 1, FAKE, FAKE, 64, FAKE, None) == 2
+    assert e(1, 8, -1, 128, 1, FAKE, FAKE, 64, FAKE, None) == 2
+    assert e(1, 8, 10, 128, 2, FAKE, FAKE, 64, FAKE, None) == 3
+    assert e(1, 8, 10, 128, 1, None, FAKE, 64, FAKE, None) == 1
+    assert e(1, 8, 10, 128, 1, FAKE, FAKE, 64, odd1, None) == 4
+    assert e(300, 300, 10, 128, 1, FAKE, FAKE, 64, FAKE, None) == 6  # more (b, g) rows than the grid takes
+    assert e(1, 8, 0, 128, 1, FAKE, FAKE, 64, FAKE, None) == 0
+
+    qf = lib.LIB.kvc_query_channels
+    assert qf(1, 30, 8, 4, 128, 1, FAKE, FAKE, 64, FAKE, None) == 2    # H not a multiple of Hkv
+    assert qf(1, 32, 8, 4, 96, 1, FAKE, FAKE, 64, FAKE, None) == 6
+    assert qf(1, 32, 8, 4, 128, 1, FAKE, FAKE, 129, FAKE, None) == 2
+    assert qf(1, 32, 8, 4, 128, 1, FAKE, None, 64, FAKE, None) == 1
+    assert qf(1, 32, 8, 4, 128, 0, odd2, FAKE, 64, FAKE, None) == 4
+    assert qf(1, 32, 8, 0, 128, 1, FAKE, FAKE, 64, FAKE, None) == 0
 
 
 def test_topk_workspace_long_rows(lib):

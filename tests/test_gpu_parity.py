@@ -59,6 +59,7 @@ CASES = [
     ("chan_nw4_allheads", 1, 16, 4, 1300, 128, 32, "bf16", 1, 1, 0.0, 64, 2.0),
     ("chan_d1", 1, 32, 8, 500, 128, 64, "bf16", 0, 1, 0.0, 1, 1.0),
     ("chan_d65", 1, 32, 8, 400, 128, 64, "bf16", 0, 1, 0.0, 65, 1.0),
+    ("chan_r320_chunks_holes", 1, 40, 8, 700, 128, 64, "bf16", 0, 1, 0.1, 48, 1.0),
 ]
 
 
@@ -130,6 +131,59 @@ def test_topk_signed_zeros():
             idx = lib().kvc_topk_select(dev(s), k, tail)
             torch.cuda.synchronize()
             assert np.array_equal(idx.cpu().numpy().astype(np.int64), O.topk_select(s.astype(np.float64), k, tail))
+
+
+def _bits_equal(t, ref, what):
+    got = host_bits(t)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.array_equal(np.ascontiguousarray(got).view(np.uint8), np.ascontiguousarray(ref).view(np.uint8)), what
+
+
+@pytest.mark.parametrize("dt,D,d_keep,order", [
+    ("bf16", 128, 64, "sorted"), ("bf16", 128, 1, "sorted"), ("bf16", 128, 128, "perm"), ("bf16", 64, 37, "perm"),
+    ("f32", 128, 64, "perm"), ("f32", 64, 64, "sorted"), ("f32", 128, 3, "perm")])
+def test_compressed_key_cache(dt, D, d_keep, order):
+    """ThinK options 3b/3c: kept-channel keys, the zeros added back, and the
+    pruned queries, bit-exact against the oracle (odd d_keep: rows of the
+    compressed keys are not 16-byte multiples)."""
+    say(f"compressed key cache {dt} D={D} d_keep={d_keep} {order}")
+    B, H, Hkv, S, n_keep, w = 2, 12, 3, 517, 129, 5
+    p = synth.random_problem(17, B, H, Hkv, S, D, w, dtype=dt)
+    rs = np.random.default_rng(D * 1000 + d_keep)
+    idx = np.stack([np.stack([np.sort(rs.choice(S, n_keep, replace=False)) for _ in range(Hkv)])
+                    for _ in range(B)]).astype(np.int32)
+    ch = np.stack([np.stack([rs.permutation(D)[:d_keep] for _ in range(Hkv)]) for _ in range(B)]).astype(np.int32)
+    if order == "sorted":
+        ch = np.sort(ch, axis=-1)
+    L = lib()
+    kd, vd, idd, chd = dev(p.k, dt), dev(p.v, dt), dev(idx), dev(ch)
+    kc, vc = L.kvc_gather_compress(kd, vd, idd, chd)
+    full = L.kvc_channel_expand(kc, chd, D)
+    qc = L.kvc_query_channels(dev(p.q, dt), chd)
+    k0, v0 = L.kvc_gather_compact(kd, vd, idd, chan_idx=chd)
+    kc_only, none_v = L.kvc_gather_compress(kd, None, idd, chd)
+    torch.cuda.synchronize()
+    ref_kc, ref_vc = O.gather_compress(p.k, p.v, idx, ch)
+    _bits_equal(kc, ref_kc, "compressed K")
+    _bits_equal(vc, ref_vc, "V rows")
+    _bits_equal(full, O.channel_expand(ref_kc, ch, D), "zeros added back")
+    _bits_equal(qc, O.query_channels(p.q, ch), "pruned queries")
+    _bits_equal(kc_only, ref_kc, "compressed K without V")
+    assert none_v is None
+    # option 3b's expansion is option 3a's zero-filled cache
+    assert torch.equal(full.view(torch.int16) if dt == "bf16" else full.view(torch.int32),
+                       k0.view(torch.int16) if dt == "bf16" else k0.view(torch.int32))
+
+
+def test_channel_expand_repeated_entry():
+    """A repeated channel takes the last of its positions (R25), as the oracle."""
+    say("channel expand repeated entry")
+    rs = np.random.default_rng(3)
+    k_c = rs.standard_normal((1, 2, 70, 4)).astype(np.float32)
+    ch = np.array([[[5, 9, 5, 60], [1, 1, 1, 2]]], dtype=np.int32)
+    full = lib().kvc_channel_expand(dev(k_c), dev(ch), 64)
+    torch.cuda.synchronize()
+    _bits_equal(full, O.channel_expand(k_c, ch, 64), "repeated entry")
 
 
 @pytest.mark.parametrize("dt,D,chan", [("bf16", 128, True), ("bf16", 64, False), ("f32", 128, True),

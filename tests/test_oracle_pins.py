@@ -276,6 +276,66 @@ def test_gather_matches_row_copy_loops(dtype):
 
 
 # ----------------------------------------------------------------------------
+# O9 compressed key cache
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_compress_then_expand_equals_zeroed_gather(dtype):
+    """Option 3b: adding the zeros back to the compressed keys gives the
+    zero-filled cache of option 3a (O8, pinned above) bit for bit, whatever
+    the order of the channel list; V is the same kept rows."""
+    p = synth.random_problem(41, 2, 6, 3, 23, 8, 1, dtype=dtype)
+    rs = np.random.default_rng(5)
+    idx = np.stack([np.stack([np.sort(rs.choice(23, 9, replace=False)) for _ in range(3)]) for _ in range(2)])
+    ch = np.stack([np.stack([rs.permutation(8)[:5] for _ in range(3)]) for _ in range(2)])
+    kc, vc = O.gather_compress(p.k, p.v, idx, ch)
+    assert kc.shape == (2, 3, 9, 5) and kc.dtype == p.k.dtype
+    k0, v0 = O.gather_compact(p.k, p.v, idx, chan_keep=ch)
+    assert O.channel_expand(kc, ch, 8).tobytes() == k0.tobytes()
+    assert vc.tobytes() == v0.tobytes()
+    # every channel kept, in order: the plain row gather
+    kall, _ = O.gather_compress(p.k, None, idx, np.broadcast_to(np.arange(8), (2, 3, 8)))
+    assert kall.tobytes() == O.gather_compact(p.k, None, idx)[0].tobytes()
+
+
+def test_compress_and_expand_by_hand():
+    """Rows 2 and 0 of a 3x4 key block, channels 3 and 1, checked by hand."""
+    k = np.arange(12, dtype=np.float32).reshape(1, 1, 3, 4)
+    ch = np.array([[[3, 1]]])
+    kc, _ = O.gather_compress(k, None, np.array([[[2, 0]]]), ch)
+    assert kc[0, 0].tolist() == [[11.0, 9.0], [3.0, 1.0]]
+    assert O.channel_expand(kc, ch, 4)[0, 0].tolist() == [[0.0, 9.0, 0.0, 11.0], [0.0, 1.0, 0.0, 3.0]]
+    # a repeated entry keeps the last j (R25)
+    rep = O.channel_expand(np.array([[[[5.0, 7.0]]]], dtype=np.float32), np.array([[[2, 2]]]), 4)
+    assert rep[0, 0, 0].tolist() == [0.0, 0.0, 7.0, 0.0]
+    # queries: head h of 4 uses the channels of KV head h // 2
+    q = np.arange(2 * 4 * 1 * 4, dtype=np.float32).reshape(2, 4, 1, 4)
+    chq = np.array([[[0, 3], [2, 1]], [[1, 1], [3, 0]]])
+    qc = O.query_channels(q, chq)
+    assert qc[0, :, 0].tolist() == [[0, 3], [4, 7], [10, 9], [14, 13]]
+    assert qc[1, :, 0].tolist() == [[17, 17], [21, 21], [27, 24], [31, 28]]
+
+
+def test_pruned_queries_on_compressed_keys_equal_zeroed_key_logits():
+    """Option 3c: the pruned queries against the compressed keys give the
+    logits of the full queries against the zero-filled keys (option 3a)."""
+    B, H, Hkv, S, D, w = 2, 8, 2, 19, 16, 4
+    p = synth.random_problem(43, B, H, Hkv, S, D, w, dtype="f32")
+    rs = np.random.default_rng(9)
+    ch = np.stack([np.stack([rs.permutation(D)[:7] for _ in range(Hkv)]) for _ in range(B)])
+    idx = np.broadcast_to(np.arange(S), (B, Hkv, S))
+    kc, _ = O.gather_compress(p.k, None, idx, ch)
+    k0, _ = O.gather_compact(p.k, None, idx, chan_keep=ch)
+    qc = O.query_channels(p.q, ch)
+    G = H // Hkv
+    for b in range(B):
+        for h in range(H):
+            got = qc[b, h].astype(np.float64) @ kc[b, h // G].astype(np.float64).T
+            want = p.q[b, h].astype(np.float64) @ k0[b, h // G].astype(np.float64).T
+            assert np.allclose(got, want, rtol=1e-13, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
 # O5 Scissorhands
 # ----------------------------------------------------------------------------
 
