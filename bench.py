@@ -155,10 +155,6 @@ def wl_snapkv_32k(c: Ctx) -> dict:
     # by the top-k, indices written and read, kept K and V read and written
     k_bytes, q_bytes, s_bytes = B * Hkv * S * D * 2, B * H * w * D * 2, B * Hkv * S * 4
     i_bytes, g_bytes = B * Hkv * keep * 4, 2 * 2 * B * Hkv * keep * D * 2
-    if compress:
-        # kept K channels read and written, V rows read and written, the window
-        # queries' kept channels read and written
-        g_bytes = 2 * B * Hkv * keep * dk * 2 + 2 * B * Hkv * keep * D * 2 + 2 * B * H * w * dk * 2
     layer_bytes = k_bytes + q_bytes + 2 * s_bytes + 2 * i_bytes + g_bytes
 
     def cpu(budget):
