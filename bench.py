@@ -34,9 +34,11 @@ METRIC = "KV tokens scored+pruned/s per layer (32k ctx, GQA 32/8) + % of HBM roo
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_window_scores_snapkv_32k.json")
 SCORE_SOURCES = ["window_scores.hip", "kvc_device.h", "kvc_plan.h"]
-WORKLOADS = ["snapkv_32k", "tova_tiny", "tova_batched", "scissor_decode", "think_128k", "think_128k_kc"]
+WORKLOADS = ["snapkv_32k", "tova_tiny", "tova_batched", "scissor_decode", "think_128k", "think_128k_kc",
+             "snapkv_think_32k"]
 DEFAULT_STEPS = {"snapkv_32k": (100, 10), "tova_tiny": (200, 20), "tova_batched": (20, 3),
-                 "scissor_decode": (800, 0), "think_128k": (10, 2), "think_128k_kc": (10, 2)}
+                 "scissor_decode": (800, 0), "think_128k": (10, 2), "think_128k_kc": (10, 2),
+                 "snapkv_think_32k": (100, 10)}
 
 
 def score_kernel_hash() -> str:
@@ -120,9 +122,13 @@ class Ctx:
 #   config            extra config keys
 # ---------------------------------------------------------------------------
 
-def wl_snapkv_32k(c: Ctx) -> dict:
+def wl_snapkv_32k(c: Ctx, then_think: bool = False) -> dict:
+    """SnapKV at 32k.  then_think: ThinK after it, on the kept keys only (channel
+    scores of the kept keys, channel top-k, kept keys stored with their 64 best
+    channels)."""
     L, torch, cfg = c.L, c.torch, c.configs.SNAPKV_32K
     B, H, Hkv, S, D, w, keep = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.w, cfg.keep
+    dk = 64
     nl = c.args.layers or cfg.layers
     layers, host0 = [], None
     for layer in range(nl):
@@ -143,6 +149,15 @@ def wl_snapkv_32k(c: Ctx) -> dict:
                                             causal=True),
                        L.bind_topk_select(ly["scores"], keep, w, ly["idx"], ly["tk_ws"], st),
                        L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st)]
+        if then_think:
+            ly["cs"] = c.empty((B, Hkv, D), torch.float32)
+            ly["ch"] = c.empty((B, Hkv, dk), torch.int32)
+            ly["rows"] = torch.arange(keep, dtype=torch.int32, device="cuda").expand(B, Hkv, keep).contiguous()
+            ly["kc"] = c.empty((B, Hkv, keep, dk), torch.bfloat16)
+            ly["cs_ws"] = c.empty(L.channel_scores_ws_bytes(B, H, Hkv, keep, D, w), torch.uint8)
+            ly["calls"] += [L.bind_channel_scores(ly["q"], ly["k_out"], ly["cs"], ly["cs_ws"], st),
+                            L.bind_topk_select(ly["cs"], dk, 0, ly["ch"], ly["tk_ws"], st),
+                            L.bind_gather_compress(ly["k_out"], None, ly["rows"], ly["ch"], ly["kc"], None, st)]
         ly["kcall"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], s0, reduce=L.KVC_REDUCE_GROUP,
                                            causal=True)
 
@@ -155,6 +170,9 @@ def wl_snapkv_32k(c: Ctx) -> dict:
     # by the top-k, indices written and read, kept K and V read and written
     k_bytes, q_bytes, s_bytes = B * Hkv * S * D * 2, B * H * w * D * 2, B * Hkv * S * 4
     i_bytes, g_bytes = B * Hkv * keep * 4, 2 * 2 * B * Hkv * keep * D * 2
+    if then_think:
+        # kept K read by the channel scores, kept channels read and written
+        g_bytes += B * Hkv * keep * D * 2 + 2 * B * Hkv * keep * dk * 2
     layer_bytes = k_bytes + q_bytes + 2 * s_bytes + 2 * i_bytes + g_bytes
 
     def cpu(budget):
@@ -164,8 +182,14 @@ def wl_snapkv_32k(c: Ctx) -> dict:
 
         def one(n):
             g = n % Hkv
-            s, idx = O.snapkv(q64[:, g * G:(g + 1) * G], k64[:, g:g + 1], keep)
-            O.gather_compact(host0.k[:, g:g + 1], host0.v[:, g:g + 1], idx)
+            qg, kg = q64[:, g * G:(g + 1) * G], k64[:, g:g + 1]
+            if then_think:
+                s, idx, cs, ch = O.snapkv_then_think(qg, kg, keep, dk)
+                ko, _ = O.gather_compact(host0.k[:, g:g + 1], host0.v[:, g:g + 1], idx)
+                O.gather_compress(ko, None, np.broadcast_to(np.arange(keep), idx.shape), ch)
+            else:
+                s, idx = O.snapkv(qg, kg, keep)
+                O.gather_compact(host0.k[:, g:g + 1], host0.v[:, g:g + 1], idx)
         n, el = timed_oracle(one, budget)
         # one KV head is 1/Hkv of a layer's work on all S positions
         return {"value": round(B * S * n / Hkv / el, 1), "unit": "tokens/s", "cores": blas_threads(),
@@ -181,8 +205,11 @@ def wl_snapkv_32k(c: Ctx) -> dict:
     return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes,
                 kernel=("kvc_window_scores (pass 1 + merge + pass 2)", [ly["kcall"] for ly in layers],
                         k_bytes + q_bytes + s_bytes, traffic),
-                cpu=cpu, metric=METRIC, unit="tokens/s", dtype="bf16", workload=cfg.name,
-                config={"B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep})
+                cpu=cpu, metric=(f"KV tokens scored+pruned/s per layer ({cfg.name}, then ThinK on the kept keys)"
+                                 if then_think else METRIC), unit="tokens/s", dtype="bf16",
+                workload=cfg.name + ("_then_think" if then_think else ""),
+                config={"B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep,
+                        **({"d_keep": dk} if then_think else {})})
 
 
 def wl_tova(c: Ctx, cfg, gen, dtype, tdtype) -> dict:
@@ -413,6 +440,8 @@ def build_workload(c: Ctx) -> dict:
     wl = c.args.workload
     if wl == "snapkv_32k":
         return wl_snapkv_32k(c)
+    if wl == "snapkv_think_32k":
+        return wl_snapkv_32k(c, then_think=True)
     if wl == "tova_tiny":
         return wl_tova(c, c.configs.TOVA_TINY, c.synth.tova_tiny, "f32", c.torch.float32)
     if wl == "tova_batched":

@@ -140,6 +140,11 @@ kvc_status kvc_window_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_wi
  *   plane = step % hist_len: counts += low - old bit;  bit <- low.
  *   If frac_out != NULL, it then writes
  *   frac_out[b,g,c] = counts / min(step+1, hist_len) at valid slots and -inf at holes.
+ * When probs == NULL and frac_out != NULL, frac_out is written the same way from
+ * the current counts, with `step` the last recorded step.  This serves sampled
+ * recording ([COLD] review thread: Scissorhands checks and records the attention
+ * only every M steps): record with step = the number of recordings so far, and
+ * ask for the fraction at an eviction step that records nothing.
  * When evict_idx != NULL (after the record, if both are given):
  *   valid[b, g, evict_idx[b,g,e]] = 0 for e < n_evict.  The indices must be in
  *   [0, C) (e.g. kvc_topk_select over frac_out with k = n_evict).

@@ -89,9 +89,10 @@ kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
   if (n_evict < 0 || n_evict > C) return KVC_ERR_SHAPE;
   if (!valid) return KVC_ERR_NULL;
   if (probs && (!hist || !counts)) return KVC_ERR_NULL;
-  if (probs && (misaligned4(probs) || misaligned4(hist) || (frac_out && misaligned4(frac_out)) ||
-                (reinterpret_cast<uintptr_t>(counts) & 1u)))
-    return KVC_ERR_ALIGN;
+  if (frac_out && !counts) return KVC_ERR_NULL;
+  if (probs && (misaligned4(probs) || misaligned4(hist))) return KVC_ERR_ALIGN;
+  if ((probs || frac_out) && (reinterpret_cast<uintptr_t>(counts) & 1u)) return KVC_ERR_ALIGN;
+  if (frac_out && misaligned4(frac_out)) return KVC_ERR_ALIGN;
   kvc::ScissorArgs a;
   a.B = B;
   a.Hkv = Hkv;
@@ -102,10 +103,10 @@ kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
   a.valid = valid;
   a.hist = hist;
   a.counts = counts;
-  a.frac_out = probs ? frac_out : nullptr;
+  a.frac_out = frac_out;
   a.evict_idx = evict_idx;
   a.n_evict = evict_idx ? n_evict : 0;
-  if (!a.probs && !a.evict_idx) return KVC_OK;
+  if (!a.probs && !a.frac_out && !a.evict_idx) return KVC_OK;
   return hip_status(kvc::launch_scissor(a, stream));
 }
 

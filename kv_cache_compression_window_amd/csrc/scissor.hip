@@ -163,6 +163,18 @@ __global__ void scissor_evict_kernel(int C, int n_evict, const int32_t* __restri
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// The fraction from the current counts, without a record (sampled recording:
+// an eviction step need not be a recording step): counts / n_obs at valid
+// slots, -inf at holes, as the record kernels write it.
+__global__ __launch_bounds__(NTH) void scissor_frac_kernel(long long total, int n_obs,
+                                                            const uint8_t* __restrict__ valid,
+                                                            const uint16_t* __restrict__ counts,
+                                                            float* __restrict__ frac_out) {
+  const float inv_obs = 1.0f / (float)n_obs;
+  for (long long i = (long long)blockIdx.x * NTH + threadIdx.x; i < total; i += (long long)gridDim.x * NTH)
+    frac_out[i] = valid[i] ? (float)counts[i] * inv_obs : kNegInf;
+}
+
 }  // namespace
 
 hipError_t launch_scissor(const ScissorArgs& a, hipStream_t st) {
@@ -179,6 +191,12 @@ hipError_t launch_scissor(const ScissorArgs& a, hipStream_t st) {
     else
       scissor_record_kernel<<<BHkv, NTH, 0, st>>>(a.C, W, BHkv, plane, (int)obs, a.probs, a.valid, a.hist,
                                                   a.counts, a.frac_out);
+  } else if (a.frac_out) {
+    const long long total = (long long)BHkv * a.C;
+    const int obs = (int)(a.step + 1 < a.hist_len ? a.step + 1 : a.hist_len);
+    const long long blocks = (total + NTH - 1) / NTH;
+    scissor_frac_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), NTH, 0, st>>>(total, obs, a.valid, a.counts,
+                                                                                    a.frac_out);
   }
   if (a.evict_idx && a.n_evict > 0) scissor_evict_kernel<<<BHkv, 256, 0, st>>>(a.C, a.n_evict, a.evict_idx, a.valid);
   return hipGetLastError();

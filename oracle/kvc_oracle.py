@@ -38,6 +38,11 @@ Readings where the pages are silent or garbled (each is used below):
   R17 ThinK squares the per-channel products (as the code does).
   R18 ThinK's per-query-head scores are summed over the GQA group.
   R21 pruned key channels are written as +0.0.
+  R26 sampled recording every M steps records at the steps t with t % M == 0;
+      evictions keep their own cadence and use the fraction over the
+      recordings so far.
+  R27 SnapKV then ThinK: the channel scores use the kept keys only and the
+      same window queries.
   R25 a compressed key cache keeps the kept channels in chan_idx order; the
       zero-back writes them in increasing j, so a repeated entry keeps the
       last j.
@@ -314,12 +319,19 @@ class ScissorhandsCache:
 
 
 def scissorhands_step(cache: ScissorhandsCache, q_t: np.ndarray, k: np.ndarray, t: int,
-                      evict_every: int, n_evict: int):
+                      evict_every: int, n_evict: int, record_every: int = 1):
     """One decode step: group-mean attention of the step's query over the
     valid slots, record it, and every evict_every steps evict n_evict slots
-    per (batch, KV head).  Returns (probs, low bits, evicted indices or None)."""
-    probs = window_scores(q_t, k, valid=cache.valid, reduce=REDUCE_GROUP, causal=False)
-    low = cache.update_attn_history(probs)
+    per (batch, KV head).  With record_every = M > 1 the attention is checked
+    and recorded only at the steps t with t % M == 0 ([COLD] review thread:
+    Scissorhands records every M steps), so the history and the fraction's
+    denominator count recorded steps (R26).  Returns (probs, low bits,
+    evicted indices or None); probs and low are None at a step that records
+    nothing."""
+    probs = low = None
+    if t % record_every == 0:
+        probs = window_scores(q_t, k, valid=cache.valid, reduce=REDUCE_GROUP, causal=False)
+        low = cache.update_attn_history(probs)
     evicted = cache.evict(n_evict) if (t + 1) % evict_every == 0 else None
     return probs, low, evicted
 
@@ -344,6 +356,19 @@ def snapkv(q, k, keep: int, chan_keep=None):
     s = window_scores(q, k, chan_keep=chan_keep, reduce=REDUCE_GROUP, causal=True)
     idx = topk_select(s.reshape(B * Hkv, S), keep, n_tail=w).reshape(B, Hkv, keep)
     return s, idx
+
+
+def snapkv_then_think(q, k, keep: int, d_keep: int):
+    """The other order ([THINK] review thread: ThinK combined with a press on
+    the sequence dimension, applied after it): SnapKV keeps `keep` positions
+    with every channel, then the channel scores are taken over the kept keys
+    only, with the same window queries, and d_keep key channels are kept (R27).
+    Returns (token scores, kept positions, channel scores, kept channels)."""
+    s, idx = snapkv(q, k, keep)
+    k_kept = np.take_along_axis(k, np.asarray(idx, dtype=np.int64)[..., None], axis=2)
+    cs = channel_scores(q, k_kept)
+    ch = select_channels(cs, d_keep)
+    return s, idx, cs, ch
 
 
 def think_snapkv(q, k, d_keep: int, keep: int):

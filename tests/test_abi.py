@@ -101,6 +101,10 @@ def test_scissor_validation(lib):
     assert f(8, 8, 4096, 400, 0, FAKE, FAKE, FAKE, None, None, None, 0, None) == 1
     assert f(8, 8, 4096, 400, 0, None, FAKE, None, None, None, FAKE, 4097, None) == 2
     assert f(8, 8, 4096, 400, 0, ctypes.c_void_p(0x100002), FAKE, FAKE, FAKE, None, None, 0, None) == 4
+    # the fraction alone (sampled recording) needs the counts, 2-byte aligned, and a 4-byte aligned output
+    assert f(8, 8, 4096, 400, 3, None, FAKE, None, None, FAKE, None, 0, None) == 1
+    assert f(8, 8, 4096, 400, 3, None, FAKE, None, ctypes.c_void_p(0x100001), FAKE, None, 0, None) == 4
+    assert f(8, 8, 4096, 400, 3, None, FAKE, None, FAKE, ctypes.c_void_p(0x100002), None, 0, None) == 4
     # nothing to do is not an error
     assert f(8, 8, 4096, 400, 0, None, FAKE, None, None, None, None, 0, None) == 0
 

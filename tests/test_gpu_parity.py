@@ -175,6 +175,40 @@ def test_compressed_key_cache(dt, D, d_keep, order):
                        k0.view(torch.int16) if dt == "bf16" else k0.view(torch.int32))
 
 
+def test_snapkv_then_think_composition():
+    """R27 on the GPU: window scores, top-k with the window forced, gather; then
+    the channel scores of the kept keys, the channel top-k and the compressed
+    gather of the kept keys.  The oracle follows the GPU's kept positions."""
+    say("snapkv then think")
+    B, H, Hkv, S, D, w, keep, dk = 1, 16, 4, 3000, 128, 16, 512, 64
+    p = synth.random_problem(51, B, H, Hkv, S, D, w, dtype="bf16", heavy_frac=0.02)
+    L = lib()
+    q, k, v = dev(p.q, "bf16"), dev(p.k, "bf16"), dev(p.v, "bf16")
+    s = L.kvc_window_scores(q, k, reduce=L.KVC_REDUCE_GROUP, causal=True)
+    idx = L.kvc_topk_select(s.view(-1, S), keep, w).view(B, Hkv, keep)
+    ko, vo = L.kvc_gather_compact(k, v, idx)
+    cs = L.kvc_channel_scores(q, ko)
+    ch = L.kvc_topk_select(cs.view(-1, D), dk).view(B, Hkv, dk)
+    rows = torch.arange(keep, dtype=torch.int32, device="cuda").expand(B, Hkv, keep).contiguous()
+    kc, _ = L.kvc_gather_compress(ko, None, rows, ch)
+    torch.cuda.synchronize()
+    q64, k64 = p.q64(), p.k64()
+    ref_s, _ = O.snapkv(q64, k64, keep)
+    sg = s.cpu().numpy()
+    check_scores(sg, ref_s, "token scores")
+    ig = idx.cpu().numpy()
+    check_kept(ig, sg, ref_s, keep, w)
+    check_gather(ko, vo, p.k, p.v, ig)
+    k_kept = np.take_along_axis(k64, ig.astype(np.int64)[..., None], axis=2)
+    ref_cs = O.channel_scores(q64, k_kept)
+    csg = cs.cpu().numpy()
+    check_scores(csg, ref_cs, "channel scores of the kept keys")
+    chg = ch.cpu().numpy()
+    check_kept(chg, csg, ref_cs, dk, 0)
+    ref_kc, _ = O.gather_compress(p.k, None, ig, chg)
+    _bits_equal(kc, ref_kc, "compressed kept keys")
+
+
 def test_channel_expand_repeated_entry():
     """A repeated channel takes the last of its positions (R25), as the oracle."""
     say("channel expand repeated entry")
@@ -275,6 +309,78 @@ def test_scissorhands_lockstep_small():
                 assert np.array_equal(cnt[b, g], unpack_planes(hist_now, bg, C).sum(axis=1))
                 if evict:
                     cache.attn_history[0, 0] = unpack_planes(hist_now, bg, C)
+                    fr = cache.low_fraction()[0, 0]
+                    fg = frac.cpu().numpy()[b, g]
+                    assert np.array_equal(np.isinf(fg), np.isinf(fr))
+                    fin = np.isfinite(fr)
+                    assert np.allclose(fg[fin], fr[fin], rtol=1e-6, atol=0)
+                    want = O.topk_select(fr[None], n_ev)[0]
+                    assert np.array_equal(idx.cpu().numpy()[b, g], want), f"step {t} evictions"
+                    v_exp = v_before[b, g].copy()
+                    v_exp[want] = 0
+                    assert np.array_equal(valid.cpu().numpy()[b, g], v_exp)
+
+
+def test_scissorhands_sampled_lockstep_small():
+    """Recording every M = 3 steps (R26): the step index passed to the record is
+    the number of recordings so far; an eviction step that records nothing asks
+    for the fraction alone.  Teacher-forced against the oracle as above."""
+    say("scissorhands sampled lockstep small")
+    B, H, Hkv, C, D, hist_len, every, n_ev, steps, M = 2, 8, 2, 300, 128, 4, 5, 7, 26, 3
+    L = lib()
+    k = synth.random_problem(4, B, Hkv, Hkv, C, D, 1, dtype="bf16", heavy_frac=0.05)
+    kd = dev(k.k, "bf16")
+    k64 = k.k64()
+    valid = torch.ones((B, Hkv, C), dtype=torch.uint8, device="cuda")
+    W = (C + 31) // 32
+    hist = torch.zeros((hist_len, B * Hkv, W), dtype=torch.int32, device="cuda")
+    counts = torch.zeros((B, Hkv, C), dtype=torch.int16, device="cuda")
+    frac = torch.empty((B, Hkv, C), dtype=torch.float32, device="cuda")
+    n_rec = 0
+    for t in range(steps):
+        record = t % M == 0
+        evict = (t + 1) % every == 0
+        v_before = valid.cpu().numpy().copy()
+        hist_before = hist.cpu().numpy().copy()
+        probs = None
+        if record:
+            q = synth.random_problem(2000 + t, B, H, Hkv, 1, D, 1, dtype="bf16", with_v=False).q
+            probs = L.kvc_window_scores(dev(q, "bf16"), kd, valid=valid, reduce=0, causal=False)
+            L.kvc_scissor_update(n_rec, valid, hist, counts, probs=probs, frac_out=frac if evict else None)
+            n_rec += 1
+        elif evict:
+            L.kvc_scissor_update(n_rec - 1, valid, hist, counts, frac_out=frac)
+        idx = None
+        if evict:
+            idx = L.kvc_topk_select(frac, n_ev)
+            L.kvc_scissor_update(n_rec - 1, valid, hist, counts, evict_idx=idx)
+        torch.cuda.synchronize()
+        hist_now = hist.cpu().numpy()
+        cnt = counts.cpu().numpy().view(np.uint16).astype(np.int64)
+        ref_p = None
+        if record:
+            ref_p = O.window_scores(O_bf16(q), k64, valid=v_before, reduce=0, causal=False)
+            check_scores(probs.cpu().numpy(), ref_p, f"step {t} probs")
+        for b in range(B):
+            for g in range(Hkv):
+                bg = b * Hkv + g
+                planes_now = unpack_planes(hist_now, bg, C)
+                assert np.array_equal(cnt[b, g], planes_now.sum(axis=1))
+                cache = O.ScissorhandsCache(1, 1, C, hist_len)
+                cache.valid[0, 0] = v_before[b, g].astype(bool)
+                if record:
+                    cache.attn_history[0, 0] = unpack_planes(hist_before, bg, C)
+                    cache.attn_counter = n_rec - 1
+                    low = cache.update_attn_history(ref_p[b, g][None, None])[0, 0]
+                    got = planes_now[:, (n_rec - 1) % hist_len].astype(bool)
+                    near = np.abs(ref_p[b, g] * v_before[b, g].sum() - 1.0) <= 1e-5
+                    assert np.array_equal(got[~near], low[~near]), f"step {t} bg {bg} low bits"
+                else:
+                    # nothing recorded: the history is unchanged
+                    assert np.array_equal(hist_now[:, bg], hist_before[:, bg])
+                if evict:
+                    cache.attn_history[0, 0] = planes_now
+                    cache.attn_counter = n_rec
                     fr = cache.low_fraction()[0, 0]
                     fg = frac.cpu().numpy()[b, g]
                     assert np.array_equal(np.isinf(fg), np.isinf(fr))

@@ -335,6 +335,29 @@ def test_pruned_queries_on_compressed_keys_equal_zeroed_key_logits():
             assert np.allclose(got, want, rtol=1e-13, atol=1e-13)
 
 
+def test_snapkv_then_think_channel_scores_over_kept_keys():
+    """R27: in the SnapKV-then-ThinK order the channel score of channel d is
+    (sum over window rows and group heads of q^2) times the sum of k^2 over the
+    kept positions only, checked by a loop over the kept rows; keeping every
+    position gives ThinK's own channel scores."""
+    B, H, Hkv, S, D, w, keep = 1, 4, 2, 40, 8, 6, 15
+    p = synth.random_problem(47, B, H, Hkv, S, D, w, dtype="f32")
+    q64, k64 = p.q64(), p.k64()
+    s, idx, cs, ch = O.snapkv_then_think(q64, k64, keep, 3)
+    s_ref, idx_ref = O.snapkv(q64, k64, keep)
+    assert np.array_equal(idx, idx_ref) and np.array_equal(s, s_ref)
+    G = H // Hkv
+    for b in range(B):
+        for g in range(Hkv):
+            for d in range(D):
+                qsq = sum(q64[b, h, i, d] ** 2 for h in range(g * G, (g + 1) * G) for i in range(w))
+                ksq = sum(k64[b, g, int(j), d] ** 2 for j in idx[b, g])
+                assert math.isclose(cs[b, g, d], qsq * ksq, rel_tol=1e-12)
+            assert np.array_equal(ch[b, g], O.select_channels(cs, 3)[b, g])
+    _, _, cs_all, _ = O.snapkv_then_think(q64, k64, S, 3)
+    assert np.allclose(cs_all, O.channel_scores(q64, k64), rtol=1e-12, atol=0)
+
+
 # ----------------------------------------------------------------------------
 # O5 Scissorhands
 # ----------------------------------------------------------------------------
@@ -377,6 +400,35 @@ def test_scissorhands_ring_equals_windowed_sum(hist):
         assert counts.min() >= 0 and counts.max() <= min(t + 1, hist)
         if t % 6 == 5:
             cache.evict(1)
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_scissorhands_sampled_recording(M):
+    """R26: recording every M steps keeps exactly the recorded steps' low bits:
+    the counts equal the brute-force sum of the low matrix over the last
+    min(recordings, history) recordings, the fraction divides by that number,
+    and M = 1 is every-step recording."""
+    B, H, Hkv, C, D, hist, steps, every, n_ev = 1, 4, 2, 40, 8, 4, 20, 6, 2
+    rs = np.random.default_rng(11 + M)
+    k = rs.standard_normal((B, Hkv, C, D))
+    cache = O.ScissorhandsCache(B, Hkv, C, hist)
+    recorded = []
+    for t in range(steps):
+        q = rs.standard_normal((B, H, 1, D))
+        valid_before = cache.valid.copy()
+        probs, low, _ = O.scissorhands_step(cache, q, k, t, evict_every=every, n_evict=n_ev, record_every=M)
+        if t % M == 0:
+            ref = O.window_scores(q, k, valid=valid_before, reduce=O.REDUCE_GROUP, causal=False)
+            assert np.array_equal(probs, ref)
+            recorded.append(np.asarray(low, dtype=np.int64))
+        else:
+            assert probs is None and low is None
+        n_rec = len(recorded)
+        assert cache.attn_counter == n_rec
+        window = np.stack(recorded[max(0, n_rec - hist):]).sum(axis=0)
+        assert np.array_equal(cache.low_counts(), window)
+        want_fr = np.where(cache.valid, window / min(n_rec, hist), -np.inf)
+        assert np.array_equal(cache.low_fraction(), want_fr)
 
 
 def test_scissorhands_equal_keys_never_low_and_dominant_key():
