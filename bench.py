@@ -35,10 +35,10 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_window_scores_snapkv_32k.json")
 SCORE_SOURCES = ["window_scores.hip", "kvc_device.h", "kvc_plan.h"]
 WORKLOADS = ["snapkv_32k", "tova_tiny", "tova_batched", "scissor_decode", "think_128k", "think_128k_kc",
-             "snapkv_think_32k"]
+             "snapkv_think_32k", "scissor_queue_decode"]
 DEFAULT_STEPS = {"snapkv_32k": (100, 10), "tova_tiny": (200, 20), "tova_batched": (20, 3),
                  "scissor_decode": (800, 0), "think_128k": (10, 2), "think_128k_kc": (10, 2),
-                 "snapkv_think_32k": (100, 10)}
+                 "snapkv_think_32k": (100, 10), "scissor_queue_decode": (800, 0)}
 
 
 def score_kernel_hash() -> str:
@@ -436,12 +436,129 @@ def wl_scissor_decode(c: Ctx) -> dict:
                         "hist_len": cfg.hist_len, "evict_every": cfg.evict_every, "n_evict": cfg.n_evict})
 
 
+def wl_scissor_queue_decode(c: Ctx) -> dict:
+    """Scissorhands with insertion: the prompt (the first P = 3840 slots,
+    protected) and the generated tokens share C = 4096 slots; each decode step
+    inserts its token (into the next free slot, then into the head of the
+    eviction queue, refilled with 64 slots whenever it runs out), attends with
+    the step's query and records."""
+    L, torch, cfg = c.L, c.torch, c.configs.SCISSOR_QUEUE
+    B, H, Hkv, C, D, P, m = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.keep, cfg.n_evict
+    nl = c.args.layers or cfg.layers
+    nsteps = c.args.steps
+    W = (C + 31) // 32
+    layers = []
+    for layer in range(nl):
+        qs = np.stack([c.synth.scissor_query(layer, t) for t in range(nsteps)])  # [T, B, H, 1, D]
+        kn, vn = c.synth.scissor_new_tokens(layer, nsteps)
+        cache = c.synth.scissor_cache(layer)
+        ly = dict(k0=c.up(cache), v0=c.up(cache[:, ::-1].copy()), q=c.up(qs), kn=c.up(kn), vn=c.up(vn))
+        ly["k"], ly["v"] = torch.empty_like(ly["k0"]), torch.empty_like(ly["v0"])
+        ly["valid"] = c.empty((B, Hkv, C), torch.uint8)
+        ly["hist"] = c.empty((cfg.hist_len, B * Hkv, W), torch.int32)
+        ly["counts"] = c.empty((B, Hkv, C), torch.int16)
+        ly["probs"] = c.empty((B, Hkv, C), torch.float32)
+        ly["queue"] = c.empty((B, Hkv, m), torch.int32)
+        ly["ws"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, C, D, 1), torch.uint8)
+        ly["rf_ws"] = c.empty(L.scissor_refill_ws_bytes(B, Hkv, C), torch.uint8)
+        layers.append(ly)
+    s0 = c.streams[0]
+    for i, ly in enumerate(layers):
+        st = c.streams[i % len(c.streams)]
+        ly["score"] = [L.bind_window_scores(ly["q"][t], ly["k"], ly["probs"], ly["ws"], st, valid=ly["valid"],
+                                            reduce=L.KVC_REDUCE_GROUP, causal=False) for t in range(nsteps)]
+        ly["kcall"] = L.bind_window_scores(ly["q"][0], ly["k"], ly["probs"], ly["ws"], s0, valid=ly["valid"],
+                                           reduce=L.KVC_REDUCE_GROUP, causal=False)
+        ly["record"], ly["record_step"] = L.bind_scissor_update(ly["valid"], ly["hist"], ly["counts"], st,
+                                                                probs=ly["probs"])
+        ly["refill"], ly["refill_step"] = L.bind_scissor_refill(ly["valid"], ly["counts"], cfg.hist_len, P,
+                                                                ly["queue"], ly["rf_ws"], st)
+        ly["fill"] = [L.bind_scissor_insert(ly["kn"][t], ly["vn"][t], ly["k"], ly["v"], ly["valid"], ly["hist"],
+                                            ly["counts"], st) for t in range(nsteps)]
+        ly["pop"] = [L.bind_scissor_insert(ly["kn"][t], ly["vn"][t], ly["k"], ly["v"], ly["valid"], ly["hist"],
+                                           ly["counts"], st, queue=ly["queue"]) for t in range(nsteps)]
+
+    state = {"t": 0, "ins": P, "qpos": m}
+
+    def reset():
+        for ly in layers:
+            ly["k"].copy_(ly["k0"])
+            ly["v"].copy_(ly["v0"])
+            ly["valid"].zero_()
+            ly["valid"][:, :, :P] = 1
+            ly["hist"].zero_()
+            ly["counts"].zero_()
+        torch.cuda.synchronize()
+        state.update(t=0, ins=P, qpos=m)
+
+    def step():
+        t, ins, qpos = state["t"], state["ins"], state["qpos"]
+        refill = ins >= C and qpos == m
+        for ly in layers:
+            if ins < C:
+                call, _, fill_pos = ly["fill"][t]
+                fill_pos.value = ins
+                call()
+            else:
+                if refill:
+                    ly["refill_step"].value = t - 1
+                    ly["refill"]()
+                call, j, _ = ly["pop"][t]
+                j.value = 0 if refill else qpos
+                call()
+            ly["score"][t]()
+            ly["record_step"].value = t
+            ly["record"]()
+        if ins >= C:
+            state["qpos"] = 1 if refill else qpos + 1
+        state.update(t=t + 1, ins=ins + 1)
+
+    # token-steps: valid slots per (b, g) at each step, times the batch
+    units = sum(B * min(P + t + 1, C) for t in range(nsteps))
+    k_bytes = B * Hkv * C * D * 2
+    # per step: the insertion (K and V rows written, one bit in every plane),
+    # K, Q, probabilities written and read, counts read and written, one
+    # bit-plane, validity
+    step_bytes = (2 * B * Hkv * D * 2 + B * Hkv * cfg.hist_len * 4 + k_bytes + B * H * D * 2 + 2 * B * Hkv * C * 4
+                  + 2 * B * Hkv * C * 2 + B * Hkv * W * 4 + B * Hkv * C)
+
+    def cpu(budget):
+        from oracle import kvc_oracle as O
+        G = H // Hkv
+        k64 = c.synth.stored_to_f64(c.synth.scissor_cache(0), "bf16")[0:1, 0:1]
+        kn, vn = c.synth.scissor_new_tokens(0, nsteps)
+        cache = O.ScissorhandsQueueCache(1, 1, C, D, cfg.hist_len, m, -1)
+        cache.prefill(k64[:, :, :P], k64[:, :, :P])
+        done = {"units": 0}
+
+        def one(n):
+            t = n % nsteps
+            q = c.synth.stored_to_f64(c.synth.scissor_query(0, t), "bf16")[0:1, 0:G]
+            kt = c.synth.stored_to_f64(kn[t], "bf16")[0:1, 0:1]
+            vt = c.synth.stored_to_f64(vn[t], "bf16")[0:1, 0:1]
+            O.scissorhands_queue_step(cache, q, kt, vt)
+            done["units"] += int(cache.valid.sum())
+        n, el = timed_oracle(one, budget)
+        return {"value": round(done["units"] / Hkv / el, 1), "unit": "token-steps/s", "cores": blas_threads(),
+                "kind": "oracle", "sample": f"{n} decode steps of one (batch, KV head) row of layer 0, C={C}, fp64 "
+                                            f"numpy oracle (insertion, probabilities, record, queue), {el:.1f} s"}
+    return dict(step=step, reset=reset, units_per_step=units * nl / nsteps, layers=nl, layer_bytes=step_bytes,
+                kernel=("kvc_window_scores (w=1, stored logits)", [ly["kcall"] for ly in layers],
+                        k_bytes + B * H * D * 2 + B * Hkv * C * 4, None),
+                cpu=cpu, metric=f"KV token-steps scored+recorded/s per layer ({cfg.name})", unit="token-steps/s",
+                dtype="bf16", workload=cfg.name,
+                config={"B": B, "H": H, "Hkv": Hkv, "C": C, "D": D, "decode_steps": nsteps, "prompt": P,
+                        "hist_len": cfg.hist_len, "queue": m})
+
+
 def build_workload(c: Ctx) -> dict:
     wl = c.args.workload
     if wl == "snapkv_32k":
         return wl_snapkv_32k(c)
     if wl == "snapkv_think_32k":
         return wl_snapkv_32k(c, then_think=True)
+    if wl == "scissor_queue_decode":
+        return wl_scissor_queue_decode(c)
     if wl == "tova_tiny":
         return wl_tova(c, c.configs.TOVA_TINY, c.synth.tova_tiny, "f32", c.torch.float32)
     if wl == "tova_batched":
@@ -459,7 +576,7 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is data-parallel per "
               f"(batch, KV head) and is not sharded here.", file=sys.stderr)
         sys.exit(2)
-    if args.workload == "scissor_decode" and not 1 <= args.steps <= 800:
+    if args.workload in ("scissor_decode", "scissor_queue_decode") and not 1 <= args.steps <= 800:
         print("the decode workload runs between 1 and 800 steps", file=sys.stderr)
         sys.exit(2)
     c = Ctx(args)

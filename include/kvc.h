@@ -159,6 +159,47 @@ kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
                               hipStream_t stream);
 
 /*
+ * kvc_scissor_refill — refill of the Scissorhands eviction queue.
+ *
+ * [COLD] PR description: instead of evicting in bulk, an eviction queue is
+ * updated periodically and one token is evicted per step from it; cache.py hunk:
+ * global_tokens = -1 keeps the prompt tokens.  The queue takes the m slots with
+ * the highest fraction of low attentions:
+ *   frac[b,g,c] = counts[b,g,c] / min(step+1, hist_len) at valid slots with
+ *                 c >= n_protect, -inf elsewhere (holes and the protected prefix);
+ *   queue[b,g,:] = kvc_topk_select(frac[b,g,:], m)  (ascending positions, lowest
+ *                 index first among equal fractions).
+ * `step` is the last recorded step.  At least m slots of every row must be
+ * valid and unprotected (else -inf entries, that is holes or protected slots,
+ * fill the rest of the queue).
+ *   valid [B, Hkv, C] uint8;  counts [B, Hkv, C] uint16 (kvc_scissor_update's state).
+ *   0 <= n_protect < C;  1 <= m <= C - n_protect;  queue out [B, Hkv, m] int32.
+ *   ws, ws_bytes  workspace (the fraction and the top-k's; see the conventions above).
+ */
+kvc_status kvc_scissor_refill(int32_t B, int32_t Hkv, int32_t C, int32_t hist_len, int64_t step,
+                              const uint8_t* valid, const uint16_t* counts, int32_t n_protect, int32_t m,
+                              int32_t* queue, void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * kvc_scissor_insert — a decode step's new token into the Scissorhands cache.
+ *
+ * [COLD] PR description: the eviction queue supplies one slot per step, so the
+ * new token replaces the evicted one and no hole is left.  The slot of row
+ * (b, g) is queue[b,g,j], or fill_pos for every row when queue is NULL (the
+ * cache is not full yet).  Then:
+ *   k_cache[b,g,slot,:] = k_new[b,g,:];  v_cache likewise (when v_new != NULL);
+ *   valid[b,g,slot] = 1;  counts[b,g,slot] = 0;  the slot's bit is cleared in
+ *   every history plane (the new token starts with an empty history).
+ * A slot outside [0, C) leaves its row unchanged.
+ *   k_new, v_new [B, Hkv, D];  k_cache, v_cache [B, Hkv, C, D] (16-byte aligned).
+ *   hist, counts, valid: kvc_scissor_update's state.  0 <= j < m; 0 <= fill_pos < C.
+ */
+kvc_status kvc_scissor_insert(int32_t B, int32_t Hkv, int32_t C, int32_t D, int32_t hist_len, kvc_dtype dt,
+                              const int32_t* queue, int32_t m, int32_t j, int32_t fill_pos, const void* k_new,
+                              const void* v_new, void* k_cache, void* v_cache, uint8_t* valid, uint32_t* hist,
+                              uint16_t* counts, hipStream_t stream);
+
+/*
  * kvc_channel_scores — ThinK per-channel key importance.
  *
  * [THINK] yuhuixu1993's factorised score (equal to the squared, summed

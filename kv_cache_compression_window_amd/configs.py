@@ -49,7 +49,12 @@ TOVA_BATCHED = Workload("tova_batched_b16_s8192", "tova", 16, 32, 8, 8192, 128, 
 SCISSOR_DECODE = Workload("scissorhands_decode_b8_c4096", "scissorhands", 8, 32, 8, 4096, 128, 1, 0,
                           "bf16", REDUCE_GROUP, 0, 0, steps=800, hist_len=400, evict_every=64,
                           n_evict=64, layers=8)
+SCISSOR_QUEUE = Workload("scissorhands_queue_decode_b8_c4096", "scissorhands_queue", 8, 32, 8, 4096, 128, 1, 3840,
+                         "bf16", REDUCE_GROUP, 0, 0, steps=800, hist_len=400, evict_every=64, n_evict=64, layers=8)
 THINK_128K = Workload("think_snapkv_128k_gqa32x8_w64", "think_snapkv", 1, 32, 8, 131072, 128, 64, 8192,
                       "bf16", REDUCE_GROUP, 1, 64, d_keep=64, layers=2)
 
 ALL = [TOVA_TINY, SNAPKV_32K, TOVA_BATCHED, SCISSOR_DECODE, THINK_128K]
+# Scissorhands with insertion and an eviction queue: keep = the protected prompt
+# length P (global_tokens = -1), n_evict = drop_amount (queue length)
+NEXT = [SCISSOR_QUEUE]

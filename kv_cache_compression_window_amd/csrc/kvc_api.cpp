@@ -110,6 +110,72 @@ kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
   return hip_status(kvc::launch_scissor(a, stream));
 }
 
+kvc_status kvc_scissor_refill(int32_t B, int32_t Hkv, int32_t C, int32_t hist_len, int64_t step,
+                              const uint8_t* valid, const uint16_t* counts, int32_t n_protect, int32_t m,
+                              int32_t* queue, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  if (!ws_bytes) return KVC_ERR_NULL;
+  if (B < 1 || Hkv < 1 || C < 1 || hist_len < 1 || hist_len > 65535 || step < 0) return KVC_ERR_SHAPE;
+  if ((int64_t)B * Hkv > 65535) return KVC_ERR_SHAPE;
+  if (n_protect < 0 || n_protect >= C || m < 1 || m > C - n_protect) return KVC_ERR_SHAPE;
+  size_t off_topk = 0;
+  const size_t need = kvc::scissor_refill_ws_bytes(B, Hkv, C, &off_topk);
+  if (!ws) {
+    *ws_bytes = need;
+    return KVC_OK;
+  }
+  if (*ws_bytes < need) return KVC_ERR_WORKSPACE;
+  if (!valid || !counts || !queue) return KVC_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(counts) & 1u) || misaligned4(queue) || misaligned16(ws)) return KVC_ERR_ALIGN;
+  kvc::ScissorRefillArgs a;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.C = C;
+  a.hist_len = hist_len;
+  a.step = step;
+  a.valid = valid;
+  a.counts = counts;
+  a.n_protect = n_protect;
+  a.m = m;
+  a.frac = static_cast<float*>(ws);
+  a.topk_ws = static_cast<unsigned char*>(ws) + off_topk;
+  a.queue = queue;
+  return hip_status(kvc::launch_scissor_refill(a, stream));
+}
+
+kvc_status kvc_scissor_insert(int32_t B, int32_t Hkv, int32_t C, int32_t D, int32_t hist_len, kvc_dtype dt,
+                              const int32_t* queue, int32_t m, int32_t j, int32_t fill_pos, const void* k_new,
+                              const void* v_new, void* k_cache, void* v_cache, uint8_t* valid, uint32_t* hist,
+                              uint16_t* counts, hipStream_t stream) {
+  if (dt != KVC_F32 && dt != KVC_BF16) return KVC_ERR_DTYPE;
+  if (B < 1 || Hkv < 1 || C < 1 || hist_len < 1 || hist_len > 65535) return KVC_ERR_SHAPE;
+  if ((int64_t)B * Hkv > 0x7fffffffLL) return KVC_ERR_SHAPE;
+  if (D != 64 && D != 128) return KVC_ERR_UNSUPPORTED;
+  if (queue ? (m < 1 || j < 0 || j >= m) : (fill_pos < 0 || fill_pos >= C)) return KVC_ERR_SHAPE;
+  if (!k_new || !k_cache || !valid || !hist || !counts) return KVC_ERR_NULL;
+  if (v_new && !v_cache) return KVC_ERR_NULL;
+  if (misaligned16(k_new) || misaligned16(k_cache) || (v_new && (misaligned16(v_new) || misaligned16(v_cache))) ||
+      misaligned4(hist) || (reinterpret_cast<uintptr_t>(counts) & 1u) || (queue && misaligned4(queue)))
+    return KVC_ERR_ALIGN;
+  kvc::ScissorInsertArgs a;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.C = C;
+  a.hist_len = hist_len;
+  a.row_bytes = D * (dt == KVC_BF16 ? 2 : 4);
+  a.queue = queue;
+  a.m = m;
+  a.j = j;
+  a.fill_pos = fill_pos;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_new ? v_cache : nullptr;
+  a.valid = valid;
+  a.hist = hist;
+  a.counts = counts;
+  return hip_status(kvc::launch_scissor_insert(a, stream));
+}
+
 kvc_status kvc_channel_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
                               float* chan_scores, void* ws, size_t* ws_bytes, hipStream_t stream) {
   if (!sh || !ws_bytes) return KVC_ERR_NULL;

@@ -79,4 +79,31 @@ struct ScissorArgs {
 };
 hipError_t launch_scissor(const ScissorArgs& a, hipStream_t st);
 
+// Scissorhands with insertion: the eviction queue's refill and the insertion.
+struct ScissorRefillArgs {
+  int B, Hkv, C, hist_len;
+  long long step;
+  const uint8_t* valid;
+  const uint16_t* counts;
+  int n_protect, m;
+  float* frac;    // [B*Hkv*C] workspace
+  void* topk_ws;  // top-k workspace
+  int32_t* queue; // [B, Hkv, m] out
+};
+hipError_t launch_scissor_refill(const ScissorRefillArgs& a, hipStream_t st);
+
+struct ScissorInsertArgs {
+  int B, Hkv, C, hist_len, row_bytes;
+  const int32_t* queue;  // [B, Hkv, m] or NULL (fill_pos for every row)
+  int m, j, fill_pos;
+  const void* k_new;     // [B, Hkv, D]
+  const void* v_new;     // [B, Hkv, D] or NULL
+  void* k_cache;         // [B, Hkv, C, D]
+  void* v_cache;
+  uint8_t* valid;
+  uint32_t* hist;
+  uint16_t* counts;
+};
+hipError_t launch_scissor_insert(const ScissorInsertArgs& a, hipStream_t st);
+
 }  // namespace kvc

@@ -120,4 +120,10 @@ inline size_t topk_ws_bytes(int rows, int n) {
   return p.bytes;
 }
 
+// kvc_scissor_refill: the fraction [B*Hkv*C] f32, then the top-k's workspace.
+inline size_t scissor_refill_ws_bytes(int B, int Hkv, int C, size_t* off_topk) {
+  *off_topk = align256((size_t)B * Hkv * C * sizeof(float));
+  return *off_topk + topk_ws_bytes(B * Hkv, C);
+}
+
 }  // namespace kvc

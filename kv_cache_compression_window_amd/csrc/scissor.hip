@@ -164,15 +164,43 @@ __global__ void scissor_evict_kernel(int C, int n_evict, const int32_t* __restri
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // The fraction from the current counts, without a record (sampled recording:
-// an eviction step need not be a recording step): counts / n_obs at valid
-// slots, -inf at holes, as the record kernels write it.
-__global__ __launch_bounds__(NTH) void scissor_frac_kernel(long long total, int n_obs,
+// an eviction step need not be a recording step; the eviction queue's refill):
+// counts / n_obs at valid slots, -inf at holes and at the first n_protect slots
+// of every row, as the record kernels write it.
+__global__ __launch_bounds__(NTH) void scissor_frac_kernel(long long total, int C, int n_obs, int n_protect,
                                                             const uint8_t* __restrict__ valid,
                                                             const uint16_t* __restrict__ counts,
                                                             float* __restrict__ frac_out) {
   const float inv_obs = 1.0f / (float)n_obs;
   for (long long i = (long long)blockIdx.x * NTH + threadIdx.x; i < total; i += (long long)gridDim.x * NTH)
-    frac_out[i] = valid[i] ? (float)counts[i] * inv_obs : kNegInf;
+    frac_out[i] = (valid[i] && (int)(i % C) >= n_protect) ? (float)counts[i] * inv_obs : kNegInf;
+}
+
+// A new token into one slot per (b, g) (Scissorhands with insertion): its K and
+// V rows, valid, a zero count and a cleared bit in every history plane.  The
+// slot is queue[bg*m + j], or fill_pos for every row without a queue; a slot
+// outside [0, C) is skipped.
+__global__ __launch_bounds__(NTH) void scissor_insert_kernel(int C, int W, int BHkv, int hist_len, int units,
+                                                              const int32_t* __restrict__ queue, int m, int j,
+                                                              int fill_pos, const uint4* __restrict__ k_new,
+                                                              const uint4* __restrict__ v_new,
+                                                              uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                                              uint8_t* __restrict__ valid, uint32_t* __restrict__ hist,
+                                                              uint16_t* __restrict__ counts) {
+  const size_t bg = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int slot = queue ? queue[bg * m + j] : fill_pos;
+  if (slot < 0 || slot >= C) return;
+  for (int u = tid; u < units; u += NTH) {
+    k_cache[(bg * C + slot) * units + u] = k_new[bg * units + u];
+    if (v_new) v_cache[(bg * C + slot) * units + u] = v_new[bg * units + u];
+  }
+  const uint32_t keep = ~(1u << (slot & 31));
+  for (int p = tid; p < hist_len; p += NTH) hist[((size_t)p * BHkv + bg) * W + (slot >> 5)] &= keep;
+  if (tid == 0) {
+    valid[bg * C + slot] = 1;
+    counts[bg * C + slot] = 0;
+  }
 }
 
 }  // namespace
@@ -195,10 +223,30 @@ hipError_t launch_scissor(const ScissorArgs& a, hipStream_t st) {
     const long long total = (long long)BHkv * a.C;
     const int obs = (int)(a.step + 1 < a.hist_len ? a.step + 1 : a.hist_len);
     const long long blocks = (total + NTH - 1) / NTH;
-    scissor_frac_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), NTH, 0, st>>>(total, obs, a.valid, a.counts,
-                                                                                    a.frac_out);
+    scissor_frac_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), NTH, 0, st>>>(total, a.C, obs, 0, a.valid,
+                                                                                    a.counts, a.frac_out);
   }
   if (a.evict_idx && a.n_evict > 0) scissor_evict_kernel<<<BHkv, 256, 0, st>>>(a.C, a.n_evict, a.evict_idx, a.valid);
+  return hipGetLastError();
+}
+
+hipError_t launch_scissor_refill(const ScissorRefillArgs& a, hipStream_t st) {
+  const long long total = (long long)a.B * a.Hkv * a.C;
+  const int obs = (int)(a.step + 1 < a.hist_len ? a.step + 1 : a.hist_len);
+  const long long blocks = (total + NTH - 1) / NTH;
+  scissor_frac_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), NTH, 0, st>>>(total, a.C, obs, a.n_protect, a.valid,
+                                                                                  a.counts, a.frac);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk(a.frac, a.B * a.Hkv, a.C, a.m, 0, a.queue, a.topk_ws, st);
+}
+
+hipError_t launch_scissor_insert(const ScissorInsertArgs& a, hipStream_t st) {
+  const int BHkv = a.B * a.Hkv;
+  scissor_insert_kernel<<<BHkv, NTH, 0, st>>>(a.C, (a.C + 31) / 32, BHkv, a.hist_len, a.row_bytes / 16, a.queue, a.m,
+                                              a.j, a.fill_pos, static_cast<const uint4*>(a.k_new),
+                                              static_cast<const uint4*>(a.v_new), static_cast<uint4*>(a.k_cache),
+                                              static_cast<uint4*>(a.v_cache), a.valid, a.hist, a.counts);
   return hipGetLastError();
 }
 

@@ -196,6 +196,13 @@ def scissor_query(layer: int, t: int, B: int = 8, H: int = 32, D: int = 128) -> 
     return bf16_bits(normal_f32((B, H, 1, D), [SEED_ROOT, W_SCISSOR, layer, T_Q, 1_000_000 + t]))
 
 
+def scissor_new_tokens(layer: int, steps: int, B: int = 8, Hkv: int = 8, D: int = 128):
+    """K and V of the token each decode step inserts: bf16 bits [steps,B,Hkv,D] ~ N(0,1)."""
+    k = bf16_bits(normal_f32((steps, B, Hkv, D), [SEED_ROOT, W_SCISSOR, layer, T_K, 2_000_000]))
+    v = bf16_bits(normal_f32((steps, B, Hkv, D), [SEED_ROOT, W_SCISSOR, layer, T_V, 2_000_000]))
+    return k, v
+
+
 def think_snapkv(layer: int = 0, B: int = 1, H: int = 32, Hkv: int = 8, S: int = 131072, D: int = 128,
                  w: int = 64, with_v: bool = True) -> Problem:
     """ThinK + SnapKV long-context layer: bf16 N(0,1) with per-channel scales

@@ -43,6 +43,14 @@ Readings where the pages are silent or garbled (each is used below):
       recordings so far.
   R27 SnapKV then ThinK: the channel scores use the kept keys only and the
       same window queries.
+  R28 Scissorhands with insertion: a decode step puts its token into the next
+      free slot while there is one, else into the head of the eviction queue;
+      the slot's history and count start empty; the step then attends with the
+      new token in the cache and records.
+  R29 the eviction queue is refilled when it is empty on a full cache, with
+      the top-k (O4) of the low-attention fraction, k = drop_amount,
+      ascending positions, popped front to back.
+  R30 the first global_tokens slots are never queued (-1: the prompt).
   R25 a compressed key cache keeps the kept channels in chan_idx order; the
       zero-back writes them in increasing j, so a repeated entry keeps the
       last j.
@@ -334,6 +342,87 @@ def scissorhands_step(cache: ScissorhandsCache, q_t: np.ndarray, k: np.ndarray, 
         low = cache.update_attn_history(probs)
     evicted = cache.evict(n_evict) if (t + 1) % evict_every == 0 else None
     return probs, low, evicted
+
+
+class ScissorhandsQueueCache(ScissorhandsCache):
+    """Scissorhands with insertion and an eviction queue ([COLD] PR
+    description: instead of bulk evictions, an eviction queue is refilled
+    periodically and one token is evicted per step; cache.py hunk:
+    global_tokens = -1 keeps the prompt).  The cache has C slots and holds K
+    and V.  Readings R28-R30:
+      * a decode step inserts its token into the next free slot while there is
+        one, else into the slot at the head of the eviction queue; the slot's
+        history and count start empty;
+      * when the queue is empty on a full cache it is refilled with the
+        drop_amount slots of the highest low-attention fraction (the top-k of
+        O4, ascending positions, popped front to back);
+      * the first global_tokens slots are never queued (-1: the prompt).
+    """
+
+    def __init__(self, B: int, Hkv: int, C: int, D: int, history_window_size: int, drop_amount: int,
+                 global_tokens: int):
+        super().__init__(B, Hkv, C, history_window_size)
+        self.valid[:] = False
+        self.k = np.zeros((B, Hkv, C, D))
+        self.v = np.zeros((B, Hkv, C, D))
+        self.drop_amount = drop_amount
+        self.global_tokens = global_tokens
+        self.insertions = 0
+        self.queue = np.zeros((B, Hkv, 0), dtype=np.int64)
+        self.queue_pos = 0
+
+    def prefill(self, k_prompt: np.ndarray, v_prompt: np.ndarray):
+        """The prompt fills the first P slots; global_tokens = -1 becomes P."""
+        P = k_prompt.shape[2]
+        self.k[:, :, :P] = k_prompt
+        self.v[:, :, :P] = v_prompt
+        self.valid[:, :, :P] = True
+        if self.insertions == 0 and self.global_tokens == -1:
+            self.global_tokens = P
+        self.insertions += P
+
+    def refill(self):
+        """The drop_amount evictable slots of the highest low-attention fraction."""
+        B, Hkv, C = self.valid.shape
+        frac = self.low_fraction()
+        frac[..., :self.global_tokens] = -np.inf
+        self.queue = topk_select(frac.reshape(B * Hkv, C), self.drop_amount).reshape(B, Hkv, self.drop_amount)
+        self.queue_pos = 0
+
+    def next_slots(self) -> np.ndarray:
+        """Slot of the next token per (b, g): the next free slot, else the head of the queue."""
+        B, Hkv, C = self.valid.shape
+        if self.insertions < C:
+            return np.full((B, Hkv), self.insertions, dtype=np.int64)
+        if self.queue_pos >= self.queue.shape[2]:
+            self.refill()
+        slots = self.queue[:, :, self.queue_pos].copy()
+        self.queue_pos += 1
+        return slots
+
+    def insert(self, slots: np.ndarray, k_new: np.ndarray, v_new: np.ndarray):
+        """Write the new token into its slots with an empty history."""
+        B, Hkv = slots.shape
+        for b in range(B):
+            for g in range(Hkv):
+                e = int(slots[b, g])
+                self.k[b, g, e] = k_new[b, g]
+                self.v[b, g, e] = v_new[b, g]
+                self.valid[b, g, e] = True
+                self.attn_history[b, g, e, :] = 0
+        self.insertions += 1
+
+
+def scissorhands_queue_step(cache: ScissorhandsQueueCache, q_t: np.ndarray, k_new: np.ndarray,
+                            v_new: np.ndarray):
+    """One decode step with insertion: place the new token (R28), attend with
+    the step's query over the valid slots (the new token included) and record
+    the low bits.  Returns (slots, probs, low bits)."""
+    slots = cache.next_slots()
+    cache.insert(slots, k_new, v_new)
+    probs = window_scores(q_t, cache.k, valid=cache.valid, reduce=REDUCE_GROUP, causal=False)
+    low = cache.update_attn_history(probs)
+    return slots, probs, low
 
 
 # ----------------------------------------------------------------------------

@@ -109,6 +109,44 @@ def test_scissor_validation(lib):
     assert f(8, 8, 4096, 400, 0, None, FAKE, None, None, None, None, 0, None) == 0
 
 
+def test_scissor_queue_validation(lib):
+    """Refill and insertion reject bad arguments before any launch."""
+    r = lib.LIB.kvc_scissor_refill
+    n = ctypes.c_size_t(1 << 30)
+    q = ctypes.c_size_t(0)
+    assert r(8, 8, 4096, 400, 10, None, None, 100, 64, None, None, ctypes.byref(q), None) == 0 and q.value > 0
+    assert q.value >= 8 * 8 * 4096 * 4  # the fraction lives in the workspace
+    assert r(8, 8, 4096, 400, 10, FAKE, FAKE, 100, 64, FAKE, FAKE, None, None) == 1
+    assert r(8, 8, 4096, 400, -1, FAKE, FAKE, 100, 64, FAKE, FAKE, ctypes.byref(n), None) == 2
+    assert r(8, 8, 4096, 400, 10, FAKE, FAKE, 4096, 1, FAKE, FAKE, ctypes.byref(n), None) == 2  # all protected
+    assert r(8, 8, 4096, 400, 10, FAKE, FAKE, 4000, 97, FAKE, FAKE, ctypes.byref(n), None) == 2  # m > C - n_protect
+    assert r(8, 8, 4096, 400, 10, FAKE, FAKE, 0, 0, FAKE, FAKE, ctypes.byref(n), None) == 2
+    assert r(8, 8, 4096, 400, 10, None, FAKE, 0, 64, FAKE, FAKE, ctypes.byref(n), None) == 1
+    assert r(8, 8, 4096, 400, 10, FAKE, ctypes.c_void_p(0x100001), 0, 64, FAKE, FAKE, ctypes.byref(n), None) == 4
+    small = ctypes.c_size_t(16)
+    assert r(8, 8, 4096, 400, 10, FAKE, FAKE, 0, 64, FAKE, FAKE, ctypes.byref(small), None) == 5
+
+    i = lib.LIB.kvc_scissor_insert
+    args = dict(B=8, Hkv=8, C=4096, D=128, hist=400, dt=1, queue=FAKE, m=64, j=3, fill=0, k_new=FAKE, v_new=FAKE,
+                k_cache=FAKE, v_cache=FAKE, valid=FAKE, hist_p=FAKE, counts=FAKE)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return i(a["B"], a["Hkv"], a["C"], a["D"], a["hist"], a["dt"], a["queue"], a["m"], a["j"], a["fill"],
+                 a["k_new"], a["v_new"], a["k_cache"], a["v_cache"], a["valid"], a["hist_p"], a["counts"], None)
+    assert call(D=96) == 6
+    assert call(dt=4) == 3
+    assert call(j=64) == 2
+    assert call(queue=None, fill=4096) == 2
+    assert call(queue=None, fill=-1) == 2
+    assert call(hist=0) == 2
+    assert call(k_new=None) == 1
+    assert call(v_cache=None) == 1
+    assert call(counts=None) == 1
+    assert call(k_cache=ODD) == 4
+    assert call(counts=ctypes.c_void_p(0x100001)) == 4
+
+
 def test_topk_validation(lib):
     f = lib.LIB.kvc_topk_select
     n = ctypes.c_size_t(1 << 20)

@@ -393,6 +393,85 @@ def test_scissorhands_sampled_lockstep_small():
                     assert np.array_equal(valid.cpu().numpy()[b, g], v_exp)
 
 
+def test_scissorhands_queue_lockstep_small():
+    """R28-R30 on the GPU: the prompt fills the first P slots, the next C - P
+    steps fill the rest, then every step takes its slot from the eviction queue,
+    refilled every m steps.  Teacher-forced: every refill's queue equals the
+    oracle's top-k on the GPU's counts, every insertion leaves the slot with the
+    new K/V rows, valid, a zero count and no history bit, and every step's low
+    bits match the oracle's on the GPU's state."""
+    say("scissorhands queue lockstep small")
+    B, H, Hkv, C, D, P, hist_len, m, steps = 2, 8, 2, 256, 128, 160, 6, 8, 140
+    G = H // Hkv
+    L = lib()
+    prob = synth.random_problem(5, B, Hkv, Hkv, C, D, 1, dtype="bf16", heavy_frac=0.05)
+    k_cache, v_cache = dev(prob.k, "bf16").clone(), dev(prob.v, "bf16").clone()
+    valid = torch.zeros((B, Hkv, C), dtype=torch.uint8, device="cuda")
+    valid[:, :, :P] = 1
+    W = (C + 31) // 32
+    hist = torch.zeros((hist_len, B * Hkv, W), dtype=torch.int32, device="cuda")
+    counts = torch.zeros((B, Hkv, C), dtype=torch.int16, device="cuda")
+    queue = torch.zeros((B, Hkv, m), dtype=torch.int32, device="cuda")
+    insertions, qpos = P, m
+    for t in range(steps):
+        new = synth.random_problem(3000 + t, B, Hkv, Hkv, 1, D, 1, dtype="bf16")
+        q = synth.random_problem(4000 + t, B, H, Hkv, 1, D, 1, dtype="bf16", with_v=False).q
+        k_new, v_new = dev(new.k[:, :, 0], "bf16"), dev(new.v[:, :, 0], "bf16")
+        if insertions < C:
+            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, fill_pos=insertions)
+            slots = np.full((B, Hkv), insertions)
+        else:
+            if qpos == m:
+                v_st = valid.cpu().numpy()
+                cnt_st = counts.cpu().numpy().view(np.uint16).astype(np.int64)
+                L.kvc_scissor_refill(t - 1, valid, counts, hist_len, P, m, queue=queue)
+                torch.cuda.synchronize()
+                frac = np.where(v_st.astype(bool), cnt_st / min(t, hist_len), -np.inf)
+                frac[..., :P] = -np.inf
+                want = O.topk_select(frac.reshape(B * Hkv, C), m).reshape(B, Hkv, m)
+                assert np.array_equal(queue.cpu().numpy(), want), f"step {t} queue"
+                qpos = 0
+            slots = queue.cpu().numpy()[:, :, qpos]
+            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, queue=queue, j=qpos)
+            qpos += 1
+        insertions += 1
+        torch.cuda.synchronize()
+        # the insertion
+        hist_ins = hist.cpu().numpy()
+        cnt_ins = counts.cpu().numpy().view(np.uint16)
+        v_ins = valid.cpu().numpy()
+        kc_bits = host_bits(k_cache)
+        vc_bits = host_bits(v_cache)
+        for b in range(B):
+            for g in range(Hkv):
+                e = int(slots[b, g])
+                assert e >= P
+                assert np.array_equal(kc_bits[b, g, e], new.k[b, g, 0]) and np.array_equal(vc_bits[b, g, e], new.v[b, g, 0])
+                assert v_ins[b, g, e] == 1 and cnt_ins[b, g, e] == 0
+                assert not unpack_planes(hist_ins, b * Hkv + g, C)[e].any()
+        assert np.array_equal(kc_bits[:, :, :P], prob.k[:, :, :P])  # the prompt is never replaced
+        # the step's attention with the new token in the cache, and its record
+        probs = L.kvc_window_scores(dev(q, "bf16"), k_cache, valid=valid, reduce=0, causal=False)
+        L.kvc_scissor_update(t, valid, hist, counts, probs=probs)
+        torch.cuda.synchronize()
+        k64 = synth.stored_to_f64(kc_bits, "bf16")
+        ref_p = O.window_scores(O_bf16(q), k64, valid=v_ins, reduce=0, causal=False)
+        check_scores(probs.cpu().numpy(), ref_p, f"step {t} probs")
+        hist_now = hist.cpu().numpy()
+        for b in range(B):
+            for g in range(Hkv):
+                bg = b * Hkv + g
+                cache = O.ScissorhandsCache(1, 1, C, hist_len)
+                cache.valid[0, 0] = v_ins[b, g].astype(bool)
+                cache.attn_history[0, 0] = unpack_planes(hist_ins, bg, C)
+                cache.attn_counter = t
+                low = cache.update_attn_history(ref_p[b, g][None, None])[0, 0]
+                got = unpack_planes(hist_now, bg, C)[:, t % hist_len].astype(bool)
+                near = np.abs(ref_p[b, g] * v_ins[b, g].sum() - 1.0) <= 1e-5
+                assert np.array_equal(got[~near], low[~near]), f"step {t} bg {bg} low bits"
+    assert insertions - P == steps and qpos > 0
+
+
 def O_bf16(bits):
     return synth.stored_to_f64(bits, "bf16")
 

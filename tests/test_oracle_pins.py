@@ -431,6 +431,54 @@ def test_scissorhands_sampled_recording(M):
         assert np.array_equal(cache.low_fraction(), want_fr)
 
 
+@pytest.mark.parametrize("global_tokens", [-1, 3])
+def test_scissorhands_queue_cache(global_tokens):
+    """R28-R30: the prompt fills the first P slots and the next C - P steps fill
+    the rest in order; after that every step replaces exactly one slot; the
+    drop_amount slots replaced after a refill are the bulk eviction set of O5
+    on the state at the refill (the pinned top-k rule); protected slots keep
+    their prompt keys; a replaced slot's history holds only the bits recorded
+    since its insertion."""
+    B, H, Hkv, C, D, P, hist, m, steps = 1, 4, 2, 24, 8, 10, 5, 4, 60
+    rs = np.random.default_rng(21)
+    cache = O.ScissorhandsQueueCache(B, Hkv, C, D, hist, m, global_tokens)
+    kp, vp = rs.standard_normal((B, Hkv, P, D)), rs.standard_normal((B, Hkv, P, D))
+    cache.prefill(kp, vp)
+    protect = P if global_tokens == -1 else global_tokens
+    assert cache.global_tokens == protect
+    since = {}  # (b, g, slot) -> step of its last insertion
+    pending = None
+    for t in range(steps):
+        if cache.insertions >= C and cache.queue_pos >= cache.queue.shape[2]:
+            # the refill about to happen takes O5's bulk eviction set of this state
+            ref = O.ScissorhandsCache(B, Hkv, C, hist)
+            ref.valid = cache.valid.copy()
+            ref.attn_history = cache.attn_history.copy()
+            ref.attn_counter = cache.attn_counter
+            frac = ref.low_fraction()
+            frac[..., :protect] = -np.inf
+            pending = O.topk_select(frac.reshape(B * Hkv, C), m).reshape(B, Hkv, m)
+        kn, vn = rs.standard_normal((B, Hkv, D)), rs.standard_normal((B, Hkv, D))
+        q = rs.standard_normal((B, H, 1, D))
+        slots, probs, low = O.scissorhands_queue_step(cache, q, kn, vn)
+        if t < C - P:
+            assert (slots == P + t).all()
+        else:
+            j = (t - (C - P)) % m
+            assert np.array_equal(slots, pending[:, :, j])
+            assert (slots >= protect).all()
+        for b in range(B):
+            for g in range(Hkv):
+                e = int(slots[b, g])
+                assert np.array_equal(cache.k[b, g, e], kn[b, g])
+                since[(b, g, e)] = t
+        assert np.array_equal(cache.k[:, :, :protect], kp[:, :, :protect])
+        assert cache.valid.all() == (t >= C - P - 1)
+        # a slot's count covers only the steps since its insertion
+        for (b, g, e), t0 in since.items():
+            assert cache.low_counts()[b, g, e] <= min(t - t0 + 1, hist)
+
+
 def test_scissorhands_equal_keys_never_low_and_dominant_key():
     """P8: all keys equal -> every probability is exactly 1/S_t, never low;
     one dominant key -> every other valid slot is low at every step, so its
