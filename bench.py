@@ -381,6 +381,12 @@ def wl_scissor_decode(c: Ctx) -> dict:
         ly["kcall"] = L.bind_window_scores(ly["q"][0], ly["k"], ly["probs"], ly["ws"], s0, valid=ly["valid"],
                                            reduce=L.KVC_REDUCE_GROUP, causal=False)
         ly["topk"] = L.bind_topk_select(ly["frac"], cfg.n_evict, 0, ly["ev"], ly["tk_ws"], st)
+        ly["record"], ly["record_step"] = L.bind_scissor_update(ly["valid"], ly["hist"], ly["counts"], st,
+                                                                probs=ly["probs"])
+        ly["record_frac"], ly["record_frac_step"] = L.bind_scissor_update(ly["valid"], ly["hist"], ly["counts"], st,
+                                                                          probs=ly["probs"], frac_out=ly["frac"])
+        ly["evict"], ly["evict_step"] = L.bind_scissor_update(ly["valid"], ly["hist"], ly["counts"], st,
+                                                              evict_idx=ly["ev"])
 
     state = {"t": 0}
 
@@ -397,11 +403,15 @@ def wl_scissor_decode(c: Ctx) -> dict:
         evict = (t + 1) % cfg.evict_every == 0
         for ly in layers:
             ly["score"][t]()
-            L.kvc_scissor_update(t, ly["valid"], ly["hist"], ly["counts"], probs=ly["probs"],
-                                 frac_out=ly["frac"] if evict else None, stream=ly["st"])
             if evict:
+                ly["record_frac_step"].value = t
+                ly["record_frac"]()
                 ly["topk"]()
-                L.kvc_scissor_update(t, ly["valid"], ly["hist"], ly["counts"], evict_idx=ly["ev"], stream=ly["st"])
+                ly["evict_step"].value = t
+                ly["evict"]()
+            else:
+                ly["record_step"].value = t
+                ly["record"]()
         state["t"] = t + 1
 
     # token-steps: valid slots per (b, g) at step t, times the batch

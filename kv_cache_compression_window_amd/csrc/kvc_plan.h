@@ -49,6 +49,15 @@ inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, WsPlan* p) {
   // four-wave streaming workgroups per CU on the (HBM-bound) stored-logits path
   const long long target = p->store ? 512 : 256LL * 8 / p->NW;
   long long nch = (target + bg - 1) / bg;
+  if (p->store) {
+    // stored-logits chunks of at least 1024 keys (a quarter of the row when that
+    // is shorter): fewer, longer workgroups overlap better with the work of
+    // other streams and lose little alone
+    long long min_keys = S / 4 < kTileKeys ? kTileKeys : S / 4;
+    if (min_keys > 1024) min_keys = 1024;
+    const long long by_len = S / min_keys < 1 ? 1 : S / min_keys;
+    if (nch > by_len) nch = by_len;
+  }
   const long long max_ch = (S + kTileKeys - 1) / kTileKeys;
   if (nch > max_ch) nch = max_ch;
   if (nch < 1) nch = 1;
