@@ -425,13 +425,17 @@ def wl_scissor_decode(c: Ctx) -> dict:
         from oracle import kvc_oracle as O
         k64 = c.synth.stored_to_f64(c.synth.scissor_cache(0), "bf16")[0:1, 0:1]
         G = H // Hkv
-        cache = O.ScissorhandsCache(1, 1, C, cfg.hist_len)
         done = {"units": 0}
 
         def one(n):
-            q = c.synth.stored_to_f64(c.synth.scissor_query(0, n % nsteps), "bf16")[0:1, 0:G]
+            # the workload's steps again and again, each pass from a full cache
+            t = n % nsteps
+            if t == 0:
+                done["cache"] = O.ScissorhandsCache(1, 1, C, cfg.hist_len)
+            cache = done["cache"]
+            q = c.synth.stored_to_f64(c.synth.scissor_query(0, t), "bf16")[0:1, 0:G]
             done["units"] += int(cache.valid.sum())
-            O.scissorhands_step(cache, q, k64, n, cfg.evict_every, cfg.n_evict)
+            O.scissorhands_step(cache, q, k64, t, cfg.evict_every, cfg.n_evict)
         n, el = timed_oracle(one, budget)
         # one (b, g) row is 1/Hkv of a sequence's work in a layer
         return {"value": round(done["units"] / Hkv / el, 1), "unit": "token-steps/s", "cores": blas_threads(),
