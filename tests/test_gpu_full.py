@@ -23,7 +23,7 @@ import torch
 
 from kv_cache_compression_window_amd import configs, synth
 from oracle import kvc_oracle as O
-from tests.gpu_util import check_gather, check_kept, check_scores, dev
+from tests.gpu_util import check_gather, check_kept, check_scores, dev, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -199,3 +199,140 @@ def test_c5_think_snapkv_128k_full():
     check_scores(sg, ref_s, "c5 scores")
     check_kept(idx.cpu().numpy(), sg, ref_s, cfg.keep, cfg.n_tail)
     check_gather(ko, vo, p.k, p.v, idx.cpu().numpy(), chg)
+
+
+def test_c5_kept_keys_compressed_full():
+    """The c5 layer with the kept keys stored with their 64 channels (bench
+    workload think_128k_kc): compressed K, V rows and pruned window queries,
+    bit-exact against the oracle on the GPU's kept positions and channels."""
+    cfg = configs.THINK_128K
+    say(cfg.name + " compressed keys")
+    p = synth.think_snapkv(0)
+    L = lib()
+    q, k, v = dev(p.q, "bf16"), dev(p.k, "bf16"), dev(p.v, "bf16")
+    cs = L.kvc_channel_scores(q, k)
+    ch = L.kvc_topk_select(cs.view(-1, p.D), cfg.d_keep).view(p.B, p.Hkv, cfg.d_keep)
+    s = L.kvc_window_scores(q, k, chan_idx=ch, reduce=L.KVC_REDUCE_GROUP, causal=True)
+    idx = L.kvc_topk_select(s.view(-1, p.S), cfg.keep, cfg.n_tail).view(p.B, p.Hkv, cfg.keep)
+    kc, vc = L.kvc_gather_compress(k, v, idx, ch)
+    qc = L.kvc_query_channels(q, ch)
+    torch.cuda.synchronize()
+    ig, chg = idx.cpu().numpy(), ch.cpu().numpy()
+    ref_kc, ref_vc = O.gather_compress(p.k, p.v, ig, chg)
+    assert np.array_equal(host_bits(kc), ref_kc) and np.array_equal(host_bits(vc), ref_vc)
+    assert np.array_equal(host_bits(qc), O.query_channels(p.q, chg))
+    # the zeros added back give the zero-filled cache of the think_128k workload
+    full = L.kvc_channel_expand(kc, ch, p.D)
+    k0, _ = L.kvc_gather_compact(k, None, idx, chan_idx=ch)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), k0.view(torch.int16))
+
+
+def test_c2_then_think_full():
+    """The c2 layer followed by ThinK on its 4096 kept keys (bench workload
+    snapkv_think_32k); the oracle follows the GPU's kept positions."""
+    cfg = configs.SNAPKV_32K
+    say(cfg.name + " then think")
+    p = synth.snapkv(0)
+    L = lib()
+    dk = 64
+    q, k, v = dev(p.q, "bf16"), dev(p.k, "bf16"), dev(p.v, "bf16")
+    s = L.kvc_window_scores(q, k, reduce=L.KVC_REDUCE_GROUP, causal=True)
+    idx = L.kvc_topk_select(s.view(-1, p.S), cfg.keep, cfg.n_tail).view(p.B, p.Hkv, cfg.keep)
+    ko, vo = L.kvc_gather_compact(k, v, idx)
+    cs = L.kvc_channel_scores(q, ko)
+    ch = L.kvc_topk_select(cs.view(-1, p.D), dk).view(p.B, p.Hkv, dk)
+    rows = torch.arange(cfg.keep, dtype=torch.int32, device="cuda").expand(p.B, p.Hkv, cfg.keep).contiguous()
+    kc, _ = L.kvc_gather_compress(ko, None, rows, ch)
+    torch.cuda.synchronize()
+    q64, k64 = p.q64(), p.k64()
+    ref_s, _ = O.snapkv(q64, k64, cfg.keep)
+    sg, ig = s.cpu().numpy(), idx.cpu().numpy()
+    check_scores(sg, ref_s, "c2 scores")
+    check_kept(ig, sg, ref_s, cfg.keep, cfg.n_tail)
+    ref_cs = O.channel_scores(q64, np.take_along_axis(k64, ig.astype(np.int64)[..., None], axis=2))
+    csg, chg = cs.cpu().numpy(), ch.cpu().numpy()
+    check_scores(csg, ref_cs, "channel scores of the kept keys")
+    check_kept(chg, csg, ref_cs, dk, 0)
+    k_kept, _ = O.gather_compact(p.k, None, ig)
+    ref_kc, _ = O.gather_compress(k_kept, None, np.broadcast_to(np.arange(cfg.keep), ig.shape), chg)
+    assert np.array_equal(host_bits(kc), ref_kc)
+
+
+def test_scissorhands_queue_decode_full_sampled():
+    """The Scissorhands decode with insertion at its bench size (B 8, C 4096, a
+    protected prompt of 3840, queue 64, 800 steps) on all 64 rows; three sampled
+    rows followed in teacher-forced lockstep: every refill's queue, every
+    insertion, every step's probabilities and low bits."""
+    cfg = configs.SCISSOR_QUEUE
+    say(cfg.name)
+    B, H, Hkv, C, D, P, m, hist_len = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.keep, cfg.n_evict, cfg.hist_len
+    G = H // Hkv
+    W = (C + 31) // 32
+    L = lib()
+    cache = synth.scissor_cache(0)
+    kn, vn = synth.scissor_new_tokens(0, cfg.steps)
+    k_cache, v_cache = dev(cache, "bf16"), dev(cache[:, ::-1].copy(), "bf16")
+    valid = torch.zeros((B, Hkv, C), dtype=torch.uint8, device="cuda")
+    valid[:, :, :P] = 1
+    hist = torch.zeros((hist_len, B * Hkv, W), dtype=torch.int32, device="cuda")
+    counts = torch.zeros((B, Hkv, C), dtype=torch.int16, device="cuda")
+    queue = torch.zeros((B, Hkv, m), dtype=torch.int32, device="cuda")
+    sample = [(0, 0), (3, 5), (7, 7)]
+    bgs = [b * Hkv + g for b, g in sample]
+    ins, qpos = P, m
+    for t in range(cfg.steps):
+        k_new, v_new = dev(kn[t], "bf16"), dev(vn[t], "bf16")
+        if ins < C:
+            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, fill_pos=ins)
+            slots = np.full((B, Hkv), ins)
+        else:
+            if qpos == m:
+                v_st = valid.cpu().numpy()
+                cnt_st = counts.cpu().numpy().view(np.uint16).astype(np.int64)
+                L.kvc_scissor_refill(t - 1, valid, counts, hist_len, P, m, queue=queue)
+                torch.cuda.synchronize()
+                qg = queue.cpu().numpy()
+                for b, g in sample:
+                    frac = np.where(v_st[b, g].astype(bool), cnt_st[b, g] / min(t, hist_len), -np.inf)
+                    frac[:P] = -np.inf
+                    assert np.array_equal(qg[b, g], O.topk_select(frac[None], m)[0]), f"step {t} queue ({b},{g})"
+                qpos = 0
+            slots = queue.cpu().numpy()[:, :, qpos]
+            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, queue=queue, j=qpos)
+            qpos += 1
+        ins += 1
+        torch.cuda.synchronize()
+        v_ins = valid.cpu().numpy()
+        h_ins = hist[:, bgs, :].cpu().numpy()
+        cnt_ins = counts.cpu().numpy().view(np.uint16)
+        q_t = synth.scissor_query(0, t)
+        probs = L.kvc_window_scores(dev(q_t, "bf16"), k_cache, valid=valid, reduce=L.KVC_REDUCE_GROUP, causal=False)
+        L.kvc_scissor_update(t, valid, hist, counts, probs=probs)
+        torch.cuda.synchronize()
+        pg = probs.cpu().numpy()
+        h_now = hist[:, bgs, :].cpu().numpy()
+        q64 = synth.stored_to_f64(q_t, "bf16")
+        for si, (b, g) in enumerate(sample):
+            e = int(slots[b, g])
+            assert e >= P
+            row_k = host_bits(k_cache[b, g, e])
+            assert np.array_equal(row_k, kn[t][b, g]), f"step {t} inserted K ({b},{g})"
+            assert v_ins[b, g, e] == 1 and cnt_ins[b, g, e] == 0
+            assert not unpack_rows(h_ins[:, si, :], C)[e].any()
+            k64 = synth.stored_to_f64(host_bits(k_cache[b:b + 1, g:g + 1]), "bf16")
+            ref_p = O.window_scores(q64[b:b + 1, g * G:(g + 1) * G], k64, valid=v_ins[b:b + 1, g:g + 1],
+                                    reduce=O.REDUCE_GROUP, causal=False)[0, 0]
+            check_scores(pg[b, g], ref_p, f"step {t} ({b},{g}) probs")
+            oc = O.ScissorhandsCache(1, 1, C, hist_len)
+            oc.valid[0, 0] = v_ins[b, g].astype(bool)
+            oc.attn_history[0, 0] = unpack_rows(h_ins[:, si, :], C)
+            oc.attn_counter = t
+            low = oc.update_attn_history(ref_p[None, None])[0, 0]
+            got = unpack_rows(h_now[:, si, :], C)[:, t % hist_len].astype(bool)
+            near = np.abs(ref_p * v_ins[b, g].sum() - 1.0) <= 1e-5
+            assert np.array_equal(got[~near], low[~near]), f"step {t} ({b},{g}) low bits"
+        if t % 100 == 0:
+            say(f"  step {t} ok")
+    # the prompt is never replaced
+    assert np.array_equal(host_bits(k_cache[:, :, :P].contiguous()), cache[:, :, :P])
