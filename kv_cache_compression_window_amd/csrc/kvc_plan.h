@@ -6,8 +6,9 @@
 
 namespace kvc {
 
-// Key granularity of the window-score chunks: the two-pass kernels use 128-key
-// tiles, the stored-logits kernel 64-key tiles; chunks are multiples of both.
+// Key granularity of the window-score chunks: chunks are multiples of 128 keys
+// (two 64-key tiles of the stream kernels, four 32-key blocks of the
+// stored-logits kernel).
 constexpr int kTileKeys = 128;
 
 // How kvc_window_scores runs a given shape.

@@ -13,27 +13,30 @@
 // i < w.  They are contiguous in q_win, so row r = (h - g*G)*w + i is at
 // q_win + ((b*Hkv + g)*R + r)*D.
 //
-// Two passes over the keys, each a 32x32x16 bf16 (or 32x32x2 fp32) MFMA
-// contraction of 32-row query blocks with 32-key blocks:
+// Rows per KV head R = G*w > 16: two passes over the keys, each a 32x32x16 bf16
+// (or 32x32x2 fp32) MFMA contraction of 32-row query blocks with 32-key blocks:
 //   stats   MFMA A = key block, B = query block.  Each lane holds 16 keys of one
 //           query row, so the row's running max and sum of exp2 stay in the lane.
-//           Writes (max, sum) per row and key chunk; the stored-logits variant
-//           also writes the scaled logits.
+//           Writes (max, sum) per row and key chunk.
 //   merge   combines the chunk partials into a base-2 log-normaliser per row.
 //   scores  MFMA A = query block, B = key block.  Each lane holds 16 rows of one
 //           key, so the column sums of exp2(l*c - lse2) stay in the lane; the
 //           partial sums of the waves are added in a fixed order in LDS.
-//   from_logits  (stored-logits path) normalises the stored logits and sums them.
 //   all_heads    (TOVA) sums the group sums over the KV heads and repeats them.
-// All sums run in a fixed order, so the results are deterministic.
-//
 // Multi-wave workgroups (one wave per 32 query rows, up to 256 rows per launch)
 // run a continuous stream of 32-key blocks: while the exp work of block b runs
 // on the VALU, the MFMAs of block b+1 run on the matrix cores and the K
-// fragments of block b+2 are read from LDS.  K tiles pass through a three-tile
-// LDS ring (the next tile is already resident when a tile ends) fed by one tile
-// of staging registers.  One-wave workgroups (at most 32 rows) keep a simple
-// two-stage loop: they serve the HBM-bound decode shapes.
+// fragments of block b+2 are read from LDS.  64-key K tiles pass through a
+// three-tile LDS ring (the next tile is already resident when a tile ends), fed
+// by up to three tiles of staging registers requested ahead.  One-wave
+// workgroups serve 16 < R <= 32 with a simple two-stage loop.
+//
+// R <= 16 (TOVA with w = 1, Scissorhands decode): the stored-logits path reads
+// the keys once.  The four-wave logits kernel streams the keys, writes the
+// scaled logits of the real rows and per-chunk (max, sum) partials; the finish
+// kernel merges the partials and sums the normalised probabilities (from_logits
+// and the separate merge serve more than 1024 merged rows).
+// All sums run in a fixed order, so the results are deterministic.
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
