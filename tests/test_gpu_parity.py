@@ -60,6 +60,9 @@ CASES = [
     ("chan_d1", 1, 32, 8, 500, 128, 64, "bf16", 0, 1, 0.0, 1, 1.0),
     ("chan_d65", 1, 32, 8, 400, 128, 64, "bf16", 0, 1, 0.0, 65, 1.0),
     ("chan_r320_chunks_holes", 1, 40, 8, 700, 128, 64, "bf16", 0, 1, 0.1, 48, 1.0),
+    # the row limit: 1024 window rows per KV head (four 256-row chunks accumulating)
+    ("rows_1024_max", 1, 16, 1, 1500, 128, 64, "bf16", 0, 1, 0.0, 0, 1.0),
+    ("rows_1024_allheads_holes", 2, 32, 2, 900, 64, 64, "bf16", 1, 1, 0.15, 0, 1.0),
 ]
 
 
@@ -105,7 +108,9 @@ def test_window_scores(case):
     # rows cut into 4096-position slices: one kept, all but one, nothing left to
     # select (k == n_tail), all kept, one value everywhere, -inf holes, odd length
     (3, 50000, 1, 0, 0), (2, 45000, 44999, 0, 0), (2, 40000, 100, 100, 0), (1, 40064, 40064, 64, 0),
-    (2, 50000, 7000, 5, 1), (3, 80000, 5000, 0, 401), (2, 65537, 8000, 3, 0)])
+    (2, 50000, 7000, 5, 1), (3, 80000, 5000, 0, 401), (2, 65537, 8000, 3, 0),
+    # every eligible position kept on a sliced row, and a tail as long as the budget
+    (2, 50000, 49999, 1, 0), (2, 50000, 64, 64, 0)])
 def test_topk(rows, n, k, n_tail, levels):
     say(f"topk rows={rows} n={n} k={k} tail={n_tail} levels={levels}")
     s = synth.random_scores(rows * 7 + n, rows, n, levels)
@@ -239,6 +244,22 @@ def test_gather(dt, D, chan):
     # K only
     ko2, vo2 = lib().kvc_gather_compact(dev(p.k, dt), None, dev(idx), chan_idx=None if ch is None else dev(ch))
     assert vo2 is None and torch.equal(ko.view(torch.uint8), ko2.view(torch.uint8))
+
+
+def test_gather_every_position_kept():
+    """n_keep = S with idx = 0..S-1: the compacted cache is the cache, bit for bit;
+    with every channel in chan_idx nothing is zeroed."""
+    say("gather every position kept")
+    B, Hkv, S, D = 2, 4, 1031, 128
+    p = synth.random_problem(11, B, Hkv, Hkv, S, D, 1, dtype="bf16")
+    idx = np.broadcast_to(np.arange(S, dtype=np.int32), (B, Hkv, S)).copy()
+    ch = np.broadcast_to(np.arange(D, dtype=np.int32), (B, Hkv, D)).copy()
+    L = lib()
+    ko, vo = L.kvc_gather_compact(dev(p.k, "bf16"), dev(p.v, "bf16"), dev(idx), chan_idx=dev(ch))
+    kc, _ = L.kvc_gather_compress(dev(p.k, "bf16"), None, dev(idx), dev(ch))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(ko), p.k) and np.array_equal(host_bits(vo), p.v)
+    assert np.array_equal(host_bits(kc), p.k)
 
 
 @pytest.mark.parametrize("dt,D,S,w,G", [("bf16", 128, 3001, 64, 4), ("f32", 64, 130, 3, 2), ("bf16", 64, 1, 1, 1)])
