@@ -225,6 +225,47 @@ __device__ inline void fold_stats(const f32x16_t& a, float c, float& m_run, floa
   m_run = live ? mn : m_run;
 }
 
+// The same fold without a running maximum, for the streaming statistics pass:
+// (m, z) is kept as a reference m and z = sum of exp2(l*c - m) over the keys so
+// far, which describes the same log-normaliser m + log2(z) whatever m is.  The
+// reference moves only when the new sum would leave [0, 2^64): an unset
+// reference (first allowed key), a key far above it, or a long run of large
+// terms.  Then the slice's maximum (or the old reference, if larger) becomes the
+// reference and the sum is rescaled; a sum still at 2^32 or more is brought into
+// [1, 2) by a power of two, moved exactly into the reference.  The common case
+// costs one fma, one exp2 and one add per logit.
+__device__ inline void fold_stats_ref(const f32x16_t& a, float c, float& m_ref, float& z_run) {
+  const float nm = -m_ref;
+  float zs[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) zs[v] = fast_exp2(fmaf(a[v], c, nm));
+#pragma unroll
+  for (int v = 4; v < 16; ++v) zs[v & 3] += fast_exp2(fmaf(a[v], c, nm));
+  const float znew = z_run + ((zs[0] + zs[1]) + (zs[2] + zs[3]));
+  if (znew < 0x1p64f) {  // false for +inf and NaN (unset reference)
+    z_run = znew;
+    return;
+  }
+  float tmax = fmaxf(a[0], a[1]);
+#pragma unroll
+  for (int v = 2; v < 16; v += 2) tmax = fmaxf(fmaxf(tmax, a[v]), a[v + 1]);
+  float mn = fmaxf(m_ref, tmax * c);
+  if (mn == kNegInf) return;  // every key so far masked: the sum stays 0
+  const float nmn = -mn;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) zs[v] = fast_exp2(fmaf(a[v], c, nmn));
+#pragma unroll
+  for (int v = 4; v < 16; ++v) zs[v & 3] += fast_exp2(fmaf(a[v], c, nmn));
+  float z = z_run * fast_exp2(m_ref - mn) + ((zs[0] + zs[1]) + (zs[2] + zs[3]));
+  if (!(z < 0x1p32f)) {
+    const int e = (int)((__float_as_uint(z) >> 23) & 0xFFu) - 127;  // z is finite and >= 2^32
+    z = __uint_as_float(__float_as_uint(z) - ((uint32_t)e << 23));
+    mn += (float)e;
+  }
+  m_ref = mn;
+  z_run = z;
+}
+
 // Mask the stats-layout slice: keys above `lim` or holes become -inf.  The keys
 // of registers 4*v4 .. 4*v4+3 are consecutive, so their validity bytes come in one
 // 32-bit LDS word.
@@ -385,7 +426,7 @@ __global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
   auto mfma = [&](const Frag<T, D>& kf) { return mma_block<T, D>(kf, qf); };
   auto epi = [&](f32x16_t& a, int t, int kb, bool masked) {
     if (masked) mask_stats(a, key0 + t * TK + kb * 32, lim, &lds_valid[t % 3][kb * 32], has_valid, half);
-    fold_stats(a, p.c, m_run, z_run);
+    fold_stats_ref(a, p.c, m_run, z_run);
   };
   stream_blocks<T, D, NW>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal, lds_k,
                           lds_valid, mfma, epi, [](int) {});
