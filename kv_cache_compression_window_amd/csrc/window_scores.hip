@@ -95,7 +95,14 @@ struct StreamNSTG {
   static constexpr int value = UPT <= 2 ? 3 : UPT <= 3 ? 2 : 1;
 };
 
+// Buffer descriptor word 3 for raw (unswizzled, stride 0) buffers on gfx9.
+constexpr int kRawBufferFlags = 0x00020000;
+
 // K tile staging: contiguous global rows -> registers -> padded LDS rows.
+// Loads go through a buffer descriptor whose base is the tile's first key and
+// whose size ends at key S, so the only per-tile address work is scalar and rows
+// past S read as zero (those keys are masked or discarded downstream).  The
+// vector offsets are per-thread constants.
 template <typename T, int D, int NT, int TK>
 struct Stager {
   using G_ = TileGeom<T, D>;
@@ -106,19 +113,18 @@ struct Stager {
   uint8_t pre_valid;
 
   // Every thread issues the same loads whatever the tile, so the compiler can
-  // count them: rows past key1 read row key1-1 instead (those keys are masked
-  // or discarded downstream), and without a validity mask the byte comes from
-  // the key data and is ignored.
-  __device__ inline void load(const unsigned char* kbase, const uint8_t* vrow, int base, int key1, int tid) {
+  // count them; without a validity mask the byte comes from the key data and is
+  // ignored.
+  __device__ inline void load(const unsigned char* kbase, const uint8_t* vrow, int base, int S, int tid) {
+    const int left = max(S - base, 0);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(kbase) + (size_t)base * G_::ROWB, (short)0, left * G_::ROWB, kRawBufferFlags);
 #pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int u = tid + i * NT;
-      const int row = u / G_::UPR, cu = u % G_::UPR;
-      const int key = min(base + row, key1 - 1);
-      pre[i] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * G_::ROWB + cu * 16);
-    }
-    const uint8_t* vsrc = vrow ? vrow : kbase;
-    pre_valid = vsrc[min(base + (tid % TK), key1 - 1)];
+    for (int i = 0; i < UPT; ++i) pre[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid + i * NT) * 16, 0, 0);
+    const __amdgpu_buffer_rsrc_t rv =
+        vrow ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vrow) + base, (short)0, left, kRawBufferFlags)
+             : rk;
+    pre_valid = __builtin_amdgcn_raw_buffer_load_b8(rv, tid % TK, 0, 0);
   }
   __device__ inline void store(unsigned char* lds_k, uint8_t* lds_v, int tid, bool has_valid) {
 #pragma unroll
@@ -317,21 +323,24 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
 
   static_assert(NSTG >= 1 && NSTG <= 3, "one to three staging sets");
   Stg s0, s1, s2;  // the staging sets (s1, s2 unused with fewer)
-  if (ntiles > 0) {
-    s0.load(kbase, vrow, key0, key1, tid);
-    s0.store(lds_k[0], lds_v[0], tid, has_valid);
+  {
+    // Tiles 0 and 1 are requested together (one memory round trip, together
+    // with the caller's query loads); the staging tiles only once the ring is
+    // filled, so that at the start of a pass, when every workgroup waits for
+    // its first tiles at once, no workgroup's prefetch delays another's start.
+    Stg s1st;
+    if (ntiles > 0) s0.load(kbase, vrow, key0, S, tid);
+    if (ntiles > 1) s1st.load(kbase, vrow, key0 + TK, S, tid);
+    if (ntiles > 0) s0.store(lds_k[0], lds_v[0], tid, has_valid);
+    if (ntiles > 1) s1st.store(lds_k[1], lds_v[1], tid, has_valid);
   }
-  if (ntiles > 1) {
-    s0.load(kbase, vrow, key0 + TK, key1, tid);
-    s0.store(lds_k[1], lds_v[1], tid, has_valid);
-  }
-  if (ntiles > 2) s0.load(kbase, vrow, key0 + 2 * TK, key1, tid);
-  if constexpr (NSTG > 1)
-    if (ntiles > 3) s1.load(kbase, vrow, key0 + 3 * TK, key1, tid);
-  if constexpr (NSTG > 2)
-    if (ntiles > 4) s2.load(kbase, vrow, key0 + 4 * TK, key1, tid);
   __syncthreads();
   if (ntiles <= 0) return;
+  if (ntiles > 2) s0.load(kbase, vrow, key0 + 2 * TK, S, tid);
+  if constexpr (NSTG > 1)
+    if (ntiles > 3) s1.load(kbase, vrow, key0 + 3 * TK, S, tid);
+  if constexpr (NSTG > 2)
+    if (ntiles > 4) s2.load(kbase, vrow, key0 + 4 * TK, S, tid);
 
   Frag<T, D> kf[2];
   read_frag<T, D>(kf[0], lds_k[0], col, half);
@@ -378,7 +387,7 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
     if (FULL || t + 2 < ntiles) st.store(lds_k[(t + 2) % 3], lds_v[(t + 2) % 3], tid, has_valid);
     __syncthreads();
     post(t);
-    if (FULL || t + 2 + NSTG < ntiles) st.load(kbase, vrow, base + (2 + NSTG) * TK, key1, tid);
+    if (FULL || t + 2 + NSTG < ntiles) st.load(kbase, vrow, base + (2 + NSTG) * TK, S, tid);
   };
   int t = 0;
   for (; t + 2 * NSTG + 1 < ntiles; t += NSTG) {  // steady state
@@ -540,14 +549,14 @@ __global__ __launch_bounds__(64) void ws_stats_wave_kernel(WsParams p) {
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
   Stager<T, D, 64, TK> stg;
   if (ntiles > 0) {
-    stg.load(kbase, vrow, key0, key1, tid);
+    stg.load(kbase, vrow, key0, p.S, tid);
     stg.store(lds_k[0], lds_valid[0], tid, has_valid);
   }
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int base = key0 + t * TK;
-    if (t + 1 < ntiles) stg.load(kbase, vrow, base + TK, key1, tid);
+    if (t + 1 < ntiles) stg.load(kbase, vrow, base + TK, p.S, tid);
     const bool masked = has_valid || (base + TK > p.S) || (p.causal && base + TK - 1 > p.S - p.w);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -607,14 +616,14 @@ __global__ __launch_bounds__(64) void ws_scores_wave_kernel(WsParams p) {
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
   Stager<T, D, 64, TK> stg;
   if (ntiles > 0) {
-    stg.load(kbase, vrow, key0, key1, tid);
+    stg.load(kbase, vrow, key0, p.S, tid);
     stg.store(lds_k[0], lds_valid[0], tid, has_valid);
   }
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int base = key0 + t * TK;
-    if (t + 1 < ntiles) stg.load(kbase, vrow, base + TK, key1, tid);
+    if (t + 1 < ntiles) stg.load(kbase, vrow, base + TK, p.S, tid);
     const bool causal_tile = p.causal && base + TK - 1 > p.S - p.w;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
