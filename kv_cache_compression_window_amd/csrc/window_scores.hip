@@ -100,9 +100,10 @@ constexpr int kRawBufferFlags = 0x00020000;
 
 // K tile staging: contiguous global rows -> registers -> padded LDS rows.
 // Loads go through a buffer descriptor whose base is the tile's first key and
-// whose size ends at key S, so the only per-tile address work is scalar and rows
-// past S read as zero (those keys are masked or discarded downstream).  The
-// vector offsets are per-thread constants.
+// whose size ends at key S (saturated at 2^32 - 1 bytes: a tile far from S
+// never reaches it), so the only per-tile address work is scalar and rows past
+// S read as zero (those keys are masked or discarded downstream).  The vector
+// offsets are per-thread constants.
 template <typename T, int D, int NT, int TK>
 struct Stager {
   using G_ = TileGeom<T, D>;
@@ -117,8 +118,10 @@ struct Stager {
   // ignored.
   __device__ inline void load(const unsigned char* kbase, const uint8_t* vrow, int base, int S, int tid) {
     const int left = max(S - base, 0);
+    const unsigned long long kbytes = (unsigned long long)left * G_::ROWB;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(kbase) + (size_t)base * G_::ROWB, (short)0, left * G_::ROWB, kRawBufferFlags);
+        const_cast<unsigned char*>(kbase) + (size_t)base * G_::ROWB, (short)0,
+        (int)(unsigned)(kbytes < 0xFFFFFFFFull ? kbytes : 0xFFFFFFFFull), kRawBufferFlags);
 #pragma unroll
     for (int i = 0; i < UPT; ++i) pre[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid + i * NT) * 16, 0, 0);
     const __amdgpu_buffer_rsrc_t rv =
