@@ -327,23 +327,27 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
   static_assert(NSTG >= 1 && NSTG <= 3, "one to three staging sets");
   Stg s0, s1, s2;  // the staging sets (s1, s2 unused with fewer)
   {
-    // Tiles 0 and 1 are requested together (one memory round trip, together
-    // with the caller's query loads); the staging tiles only once the ring is
-    // filled, so that at the start of a pass, when every workgroup waits for
-    // its first tiles at once, no workgroup's prefetch delays another's start.
-    Stg s1st;
-    if (ntiles > 0) s0.load(kbase, vrow, key0, S, tid);
-    if (ntiles > 1) s1st.load(kbase, vrow, key0 + TK, S, tid);
-    if (ntiles > 0) s0.store(lds_k[0], lds_v[0], tid, has_valid);
-    if (ntiles > 1) s1st.store(lds_k[1], lds_v[1], tid, has_valid);
+    // Tiles 0 and 1 (into the LDS ring) and tile 2 (into the first staging set,
+    // stored at the end of tile 0) are requested together, in one memory round
+    // trip with the caller's query loads; only tiles 0 and 1 are waited for
+    // before the first barrier.  The other staging tiles follow once the ring
+    // is filled: at the start of a pass every workgroup waits for its first
+    // tiles at once, and requesting more then only lengthens that burst.
+    // The loads are unconditional (a tile past S reads nothing: its descriptor
+    // is empty), so the compiler can count them exactly and the first tile
+    // waits only for what it uses.
+    Stg p0, p1;
+    p0.load(kbase, vrow, key0, S, tid);
+    p1.load(kbase, vrow, key0 + TK, S, tid);
+    __builtin_amdgcn_sched_barrier(0);  // tile 2 after tiles 0 and 1: their stores wait for them only
+    s0.load(kbase, vrow, key0 + 2 * TK, S, tid);
+    if (ntiles > 0) p0.store(lds_k[0], lds_v[0], tid, has_valid);
+    if (ntiles > 1) p1.store(lds_k[1], lds_v[1], tid, has_valid);
   }
   __syncthreads();
   if (ntiles <= 0) return;
-  if (ntiles > 2) s0.load(kbase, vrow, key0 + 2 * TK, S, tid);
-  if constexpr (NSTG > 1)
-    if (ntiles > 3) s1.load(kbase, vrow, key0 + 3 * TK, S, tid);
-  if constexpr (NSTG > 2)
-    if (ntiles > 4) s2.load(kbase, vrow, key0 + 4 * TK, S, tid);
+  if constexpr (NSTG > 1) s1.load(kbase, vrow, key0 + 3 * TK, S, tid);
+  if constexpr (NSTG > 2) s2.load(kbase, vrow, key0 + 4 * TK, S, tid);
 
   Frag<T, D> kf[2];
   read_frag<T, D>(kf[0], lds_k[0], col, half);
@@ -390,7 +394,7 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
     if (FULL || t + 2 < ntiles) st.store(lds_k[(t + 2) % 3], lds_v[(t + 2) % 3], tid, has_valid);
     __syncthreads();
     post(t);
-    if (FULL || t + 2 + NSTG < ntiles) st.load(kbase, vrow, base + (2 + NSTG) * TK, S, tid);
+    st.load(kbase, vrow, base + (2 + NSTG) * TK, S, tid);  // past S: an empty descriptor, nothing read
   };
   int t = 0;
   for (; t + 2 * NSTG + 1 < ntiles; t += NSTG) {  // steady state
