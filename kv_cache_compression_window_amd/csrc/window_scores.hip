@@ -100,10 +100,11 @@ constexpr int kRawBufferFlags = 0x00020000;
 
 // K tile staging: contiguous global rows -> registers -> padded LDS rows.
 // Loads go through a buffer descriptor whose base is the tile's first key and
-// whose size ends at key S (saturated at 2^32 - 1 bytes: a tile far from S
-// never reaches it), so the only per-tile address work is scalar and rows past
-// S read as zero (those keys are masked or discarded downstream).  The vector
-// offsets are per-thread constants.
+// whose size ends at `end`, the end of the workgroup's key chunk (saturated at
+// 2^32 - 1 bytes), so the only per-tile address work is scalar, rows past the
+// chunk read nothing (zero: past S those keys are masked, and tiles never
+// straddle an inner chunk boundary), and a tile wholly past the chunk costs no
+// memory traffic.  The vector offsets are per-thread constants.
 template <typename T, int D, int NT, int TK>
 struct Stager {
   using G_ = TileGeom<T, D>;
@@ -116,8 +117,8 @@ struct Stager {
   // Every thread issues the same loads whatever the tile, so the compiler can
   // count them; without a validity mask the byte comes from the key data and is
   // ignored.
-  __device__ inline void load(const unsigned char* kbase, const uint8_t* vrow, int base, int S, int tid) {
-    const int left = max(S - base, 0);
+  __device__ inline void load(const unsigned char* kbase, const uint8_t* vrow, int base, int end, int tid) {
+    const int left = max(end - base, 0);
     const unsigned long long kbytes = (unsigned long long)left * G_::ROWB;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(kbase) + (size_t)base * G_::ROWB, (short)0,
@@ -333,21 +334,21 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
     // before the first barrier.  The other staging tiles follow once the ring
     // is filled: at the start of a pass every workgroup waits for its first
     // tiles at once, and requesting more then only lengthens that burst.
-    // The loads are unconditional (a tile past S reads nothing: its descriptor
-    // is empty), so the compiler can count them exactly and the first tile
-    // waits only for what it uses.
+    // The loads are unconditional (a tile past the chunk reads nothing: its
+    // descriptor is empty), so the compiler can count them exactly and the
+    // first tile waits only for what it uses.
     Stg p0, p1;
-    p0.load(kbase, vrow, key0, S, tid);
-    p1.load(kbase, vrow, key0 + TK, S, tid);
+    p0.load(kbase, vrow, key0, key1, tid);
+    p1.load(kbase, vrow, key0 + TK, key1, tid);
     __builtin_amdgcn_sched_barrier(0);  // tile 2 after tiles 0 and 1: their stores wait for them only
-    s0.load(kbase, vrow, key0 + 2 * TK, S, tid);
+    s0.load(kbase, vrow, key0 + 2 * TK, key1, tid);
     if (ntiles > 0) p0.store(lds_k[0], lds_v[0], tid, has_valid);
     if (ntiles > 1) p1.store(lds_k[1], lds_v[1], tid, has_valid);
   }
   __syncthreads();
   if (ntiles <= 0) return;
-  if constexpr (NSTG > 1) s1.load(kbase, vrow, key0 + 3 * TK, S, tid);
-  if constexpr (NSTG > 2) s2.load(kbase, vrow, key0 + 4 * TK, S, tid);
+  if constexpr (NSTG > 1) s1.load(kbase, vrow, key0 + 3 * TK, key1, tid);
+  if constexpr (NSTG > 2) s2.load(kbase, vrow, key0 + 4 * TK, key1, tid);
 
   Frag<T, D> kf[2];
   read_frag<T, D>(kf[0], lds_k[0], col, half);
@@ -394,7 +395,7 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
     if (FULL || t + 2 < ntiles) st.store(lds_k[(t + 2) % 3], lds_v[(t + 2) % 3], tid, has_valid);
     __syncthreads();
     post(t);
-    st.load(kbase, vrow, base + (2 + NSTG) * TK, S, tid);  // past S: an empty descriptor, nothing read
+    st.load(kbase, vrow, base + (2 + NSTG) * TK, key1, tid);  // past the chunk: an empty descriptor, nothing read
   };
   int t = 0;
   for (; t + 2 * NSTG + 1 < ntiles; t += NSTG) {  // steady state
@@ -556,14 +557,14 @@ __global__ __launch_bounds__(64) void ws_stats_wave_kernel(WsParams p) {
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
   Stager<T, D, 64, TK> stg;
   if (ntiles > 0) {
-    stg.load(kbase, vrow, key0, p.S, tid);
+    stg.load(kbase, vrow, key0, key1, tid);
     stg.store(lds_k[0], lds_valid[0], tid, has_valid);
   }
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int base = key0 + t * TK;
-    if (t + 1 < ntiles) stg.load(kbase, vrow, base + TK, p.S, tid);
+    if (t + 1 < ntiles) stg.load(kbase, vrow, base + TK, key1, tid);
     const bool masked = has_valid || (base + TK > p.S) || (p.causal && base + TK - 1 > p.S - p.w);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -623,14 +624,14 @@ __global__ __launch_bounds__(64) void ws_scores_wave_kernel(WsParams p) {
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
   Stager<T, D, 64, TK> stg;
   if (ntiles > 0) {
-    stg.load(kbase, vrow, key0, p.S, tid);
+    stg.load(kbase, vrow, key0, key1, tid);
     stg.store(lds_k[0], lds_valid[0], tid, has_valid);
   }
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int base = key0 + t * TK;
-    if (t + 1 < ntiles) stg.load(kbase, vrow, base + TK, p.S, tid);
+    if (t + 1 < ntiles) stg.load(kbase, vrow, base + TK, key1, tid);
     const bool causal_tile = p.causal && base + TK - 1 > p.S - p.w;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
