@@ -63,6 +63,11 @@ CASES = [
     # the row limit: 1024 window rows per KV head (four 256-row chunks accumulating)
     ("rows_1024_max", 1, 16, 1, 1500, 128, 64, "bf16", 0, 1, 0.0, 0, 1.0),
     ("rows_1024_allheads_holes", 2, 32, 2, 900, 64, 64, "bf16", 1, 1, 0.15, 0, 1.0),
+    # logits spanning hundreds of base-2 units (queries scaled by 20 and 30): the
+    # statistics pass moves its reference many times and most probabilities
+    # underflow (the score tolerance's absolute floor covers those)
+    ("fold_extreme_q30", 1, 32, 8, 3000, 128, 64, "bf16", 0, 1, 0.0, 0, 30.0),
+    ("fold_extreme_r128_holes_allheads", 1, 16, 4, 2000, 128, 32, "bf16", 1, 1, 0.1, 0, 20.0),
 ]
 
 
