@@ -88,11 +88,18 @@ struct StreamTK {
 };
 
 // Tiles of staging registers of the stream kernels: K tiles are requested that
-// many tiles ahead of the LDS ring, within about 24 registers per thread.
-template <typename T, int D, int NW>
+// many tiles ahead of the LDS ring, within about 24 registers per thread.  SHORT
+// (a workgroup streams at most kShortChunkTiles tiles): two sets instead of
+// three.  Measured on MI355X at 16 tiles per workgroup (SnapKV 32k) the third set
+// costs 4% of a score call, at 64 (ThinK 128k) it gains 3%: a short chunk spends
+// a larger share of its time in the start-up burst, which more requests only
+// lengthen, and a long one gains from the deeper prefetch.
+constexpr int kShortChunkTiles = 16;
+
+template <typename T, int D, int NW, bool SHORT>
 struct StreamNSTG {
   static constexpr int UPT = StreamTK<T, D, NW>::value * D * (int)sizeof(T) / 16 / (NW * 64);
-  static constexpr int value = UPT <= 2 ? 3 : UPT <= 3 ? 2 : 1;
+  static constexpr int value = UPT <= 2 ? (SHORT ? 2 : 3) : UPT <= 3 ? 2 : 1;
 };
 
 // Buffer descriptor word 3 for raw (unswizzled, stride 0) buffers on gfx9.
@@ -312,14 +319,14 @@ using bool_t = std::integral_constant<bool, B>;
 // staging registers), tile loop with the three-tile LDS ring, and the block
 // stream.  `mfma(kf)` runs the contraction of one block, `epi(acc, t, kb,
 // masked)` its VALU work, `post(t)` runs after the barrier ending tile t.
-template <typename T, int D, int NW, typename Mma, typename Epi, typename Post>
+template <typename T, int D, int NW, bool SHORT, typename Mma, typename Epi, typename Post>
 __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* vrow, int key0, int key1,
                                      int ntiles, bool has_valid, int tid, int col, int half, int S, int w,
                                      int causal, unsigned char (*lds_k)[StreamTK<T, D, NW>::value * TileGeom<T, D>::LSTRIDE],
                                      uint8_t (*lds_v)[StreamTK<T, D, NW>::value], Mma mfma, Epi epi, Post post) {
   constexpr int NT = NW * 64;
   constexpr int TK = StreamTK<T, D, NW>::value;
-  constexpr int NSTG = StreamNSTG<T, D, NW>::value;
+  constexpr int NSTG = StreamNSTG<T, D, NW, SHORT>::value;
   constexpr int KB = TK / 32;
   static_assert(KB % 2 == 0, "fragment double buffer alternates within a tile");
   using G_ = TileGeom<T, D>;
@@ -412,7 +419,7 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
   }
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool SHORT>
 __global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
   using G_ = TileGeom<T, D>;
   constexpr int NT = NW * 64;
@@ -445,7 +452,7 @@ __global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
     if (masked) mask_stats(a, key0 + t * TK + kb * 32, lim, &lds_valid[t % 3][kb * 32], has_valid, half);
     fold_stats_ref(a, p.c, m_run, z_run);
   };
-  stream_blocks<T, D, NW>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal, lds_k,
+  stream_blocks<T, D, NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal, lds_k,
                           lds_valid, mfma, epi, [](int) {});
 
   const float m2 = __shfl_xor(m_run, 32);
@@ -454,7 +461,7 @@ __global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
   if (half == 0) p.part[(size_t)chunk * p.rows_total + bg * p.Rpad + r] = make_float2(m_run, z_run);
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool SHORT>
 __global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
   using G_ = TileGeom<T, D>;
   constexpr int NT = NW * 64;
@@ -520,7 +527,7 @@ __global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
       }
     }
   };
-  stream_blocks<T, D, NW>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal, lds_k,
+  stream_blocks<T, D, NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal, lds_k,
                           lds_valid, mfma, epi, post);
 }
 
@@ -910,16 +917,22 @@ void launch_pass(const WsParams& p, const WsPlan& plan, dim3 grid, hipStream_t s
       else ws_stats_wave_kernel<T, D, false><<<grid, 64, 0, st>>>(p);
       break;
     case 2:
-      if (scores_pass) ws_scores_stream_kernel<T, D, 2><<<grid, 128, 0, st>>>(p);
-      else ws_stats_stream_kernel<T, D, 2><<<grid, 128, 0, st>>>(p);
+      if (scores_pass) ws_scores_stream_kernel<T, D, 2, false><<<grid, 128, 0, st>>>(p);
+      else ws_stats_stream_kernel<T, D, 2, false><<<grid, 128, 0, st>>>(p);
       break;
     case 4:
-      if (scores_pass) ws_scores_stream_kernel<T, D, 4><<<grid, 256, 0, st>>>(p);
-      else ws_stats_stream_kernel<T, D, 4><<<grid, 256, 0, st>>>(p);
+      if (scores_pass) ws_scores_stream_kernel<T, D, 4, false><<<grid, 256, 0, st>>>(p);
+      else ws_stats_stream_kernel<T, D, 4, false><<<grid, 256, 0, st>>>(p);
       break;
     default:
-      if (scores_pass) ws_scores_stream_kernel<T, D, 8><<<grid, 512, 0, st>>>(p);
-      else ws_stats_stream_kernel<T, D, 8><<<grid, 512, 0, st>>>(p);
+      // eight waves: the staging depth follows the number of tiles per workgroup
+      if (plan.CH <= kShortChunkTiles * StreamTK<T, D, 8>::value) {
+        if (scores_pass) ws_scores_stream_kernel<T, D, 8, true><<<grid, 512, 0, st>>>(p);
+        else ws_stats_stream_kernel<T, D, 8, true><<<grid, 512, 0, st>>>(p);
+      } else {
+        if (scores_pass) ws_scores_stream_kernel<T, D, 8, false><<<grid, 512, 0, st>>>(p);
+        else ws_stats_stream_kernel<T, D, 8, false><<<grid, 512, 0, st>>>(p);
+      }
       break;
   }
 }

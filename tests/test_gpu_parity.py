@@ -68,6 +68,9 @@ CASES = [
     # underflow (the score tolerance's absolute floor covers those)
     ("fold_extreme_q30", 1, 32, 8, 3000, 128, 64, "bf16", 0, 1, 0.0, 0, 30.0),
     ("fold_extreme_r128_holes_allheads", 1, 16, 4, 2000, 128, 32, "bf16", 1, 1, 0.1, 0, 20.0),
+    # eight waves with 18 tiles per workgroup (the three-staging-set kernels; the
+    # cases above stream at most 16)
+    ("w8_long_chunks_s36000", 1, 32, 8, 36000, 128, 64, "bf16", 0, 1, 0.0, 0, 1.0),
 ]
 
 
