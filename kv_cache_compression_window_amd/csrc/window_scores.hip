@@ -847,26 +847,35 @@ __global__ __launch_bounds__(256) void ws_finish_logits_kernel(WsParams p, int a
 }
 
 // Per row: combine the chunk partials into lse2 = M + log2(sum over chunks of
-// z_c * exp2(m_c - M)), M the largest chunk maximum, summed in chunk order.
-// One thread per row, so each chunk's partials are read coalesced across the
-// rows.  Rows past R (padding) and rows with no allowed key get +inf, so their
-// probabilities are 0.
-__global__ __launch_bounds__(64) void ws_merge_kernel(const float2* __restrict__ part, float* __restrict__ lse,
-                                                      int rows_total, int Rpad, int R, int nchunks) {
-  const int row = blockIdx.x * 64 + threadIdx.x;
-  if (row >= rows_total) return;
-  const float2* pr = part + row;
-  float m = kNegInf;
-#pragma unroll 8
-  for (int c = 0; c < nchunks; ++c) m = fmaxf(m, pr[(size_t)c * rows_total].x);
-  float z = 0.0f;
-  if (m != kNegInf) {
-#pragma unroll 8
-    for (int c = 0; c < nchunks; ++c) {
-      const float2 pc = pr[(size_t)c * rows_total];
-      z += pc.y * fast_exp2(pc.x - m);  // an empty chunk (-inf, 0) adds 0
+// z_c * exp2(m_c - M)), M the largest chunk reference.  Eight lanes per row:
+// lane j folds chunks j, j+8, ... (requested together, so a row costs one
+// memory round trip for up to 32 chunks), then a butterfly over the eight lanes
+// merges the lane results in a fixed order.  Rows past R (padding) and rows with
+// no allowed key get +inf, so their probabilities are 0.
+constexpr int kMergeLanes = 8;
+
+__global__ __launch_bounds__(256) void ws_merge_kernel(const float2* __restrict__ part, float* __restrict__ lse,
+                                                       int rows_total, int Rpad, int R, int nchunks) {
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int row = gid / kMergeLanes, j = gid % kMergeLanes;
+  const bool ok = row < rows_total;
+  float m = kNegInf, z = 0.0f;
+  for (int c0 = 0; c0 < nchunks; c0 += 4 * kMergeLanes) {
+    float2 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = c0 + j + i * kMergeLanes;
+      v[i] = (ok && c < nchunks) ? part[(size_t)c * rows_total + row] : make_float2(kNegInf, 0.0f);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lse2_merge(m, z, v[i].x, v[i].y);
   }
+#pragma unroll
+  for (int off = 1; off < kMergeLanes; off <<= 1) {
+    const float m2 = __shfl_xor(m, off), z2 = __shfl_xor(z, off);
+    lse2_merge(m, z, m2, z2);  // commutative, so every lane of the row ends with the same value
+  }
+  if (!ok || j != 0) return;
   const int r = row % Rpad;
   lse[row] = (r >= R || m == kNegInf || !(z > 0.0f)) ? kPosInf : m + log2f(z);
 }
@@ -993,8 +1002,8 @@ hipError_t launch_window_scores(const WsArgs& a, const WsPlan& plan, hipStream_t
     p.row0 = c * rows_per_launch;
     run(false);
   }
-  ws_merge_kernel<<<(p.rows_total + 63) / 64, 64, 0, st>>>(p.part, p.lse, p.rows_total, plan.Rpad, plan.R,
-                                                           plan.nchunks);
+  ws_merge_kernel<<<(p.rows_total * kMergeLanes + 255) / 256, 256, 0, st>>>(p.part, p.lse, p.rows_total, plan.Rpad,
+                                                                            plan.R, plan.nchunks);
   const float scale_all = 1.0f / (float)(a.H * a.w);
   if (plan.store) {
     const dim3 g2((a.S + 255) / 256, a.reduce ? 1 : a.Hkv, a.B);
