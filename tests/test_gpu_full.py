@@ -336,3 +336,31 @@ def test_scissorhands_queue_decode_full_sampled():
             say(f"  step {t} ok")
     # the prompt is never replaced
     assert np.array_equal(host_bits(k_cache[:, :, :P].contiguous()), cache[:, :, :P])
+
+
+def test_window_scores_key_rows_past_4gib():
+    """Key rows longer than 2^32 bytes (17 M keys of one KV head, 4.35 GB): the
+    K tiles are loaded through buffer descriptors whose 32-bit size saturates
+    there.  Every key is the same vector, so each window row's probabilities are
+    uniform over the keys its causal mask allows (the closed form of the
+    all-keys-equal case, pinned in the oracle tests): score_j = (1/w) * sum over
+    the window positions i that allow key j of 1 / (S - w + i + 1).  A key read
+    wrongly (as zero, or from another row) changes its logit and the sums."""
+    L = lib()
+    B, H, Hkv, S, D, w = 1, 32, 1, 17_000_000, 128, 8
+    g = torch.Generator(device="cpu").manual_seed(20261202)
+    q = torch.randn(B, H, w, D, generator=g).to(torch.bfloat16).cuda()
+    krow = torch.randn(D, generator=g).to(torch.bfloat16).cuda()
+    k = krow.view(1, 1, 1, D).expand(B, Hkv, S, D).contiguous()
+    assert k.numel() * k.element_size() > 2 ** 32
+    say(f"window scores, S={S} keys of one KV head, {k.numel() * 2 / 2**30:.2f} GiB of K")
+    s = L.kvc_window_scores(q, k, reduce=L.KVC_REDUCE_GROUP, causal=True)
+    torch.cuda.synchronize()
+    got = s[0, 0].cpu().numpy()
+    del k
+    exp = np.zeros(S)
+    for i in range(w):
+        n_i = S - w + i + 1
+        exp[:n_i] += 1.0 / n_i
+    exp /= w
+    check_scores(got, exp, "key rows past 4 GiB")
