@@ -196,6 +196,49 @@ __device__ inline void load_query(Frag<T, D>& qf, const WsParams& p, size_t bg, 
   }
 }
 
+// Query fragments of the 32 rows rowblk .. rowblk+31 of (b, g), through the
+// wave's LDS slot.  The rows are contiguous in q_win, so the wave reads them with
+// coalesced 16-byte loads (each instruction covers 1 KB of consecutive rows, not
+// one 16-byte piece of each of 64 rows), writes them to padded LDS rows and reads
+// its fragment back; the wave's LDS operations run in order.  Rows past R are
+// zero; channels not in the keep mask are zeroed.
+template <typename T, int D>
+__device__ inline void load_query_rows(Frag<T, D>& qf, const WsParams& p, size_t bg, int rowblk, int lane, int half,
+                                       const uint32_t* keep, unsigned char* slot) {
+  using M = Mfma<T>;
+  using G_ = TileGeom<T, D>;
+  constexpr int UPL = 32 * G_::ROWB / 16 / 64;  // 16-byte units per lane
+  const unsigned char* src =
+      reinterpret_cast<const unsigned char*>(p.q) + (bg * p.R + (size_t)rowblk) * (size_t)G_::ROWB;
+  u32x4_t d[UPL];
+#pragma unroll
+  for (int u = 0; u < UPL; ++u) {
+    const int off = u * 1024 + lane * 16;
+    d[u] = (rowblk + off / G_::ROWB < p.R) ? *reinterpret_cast<const u32x4_t*>(src + off) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int u = 0; u < UPL; ++u) {
+    const int off = u * 1024 + lane * 16;
+    *reinterpret_cast<u32x4_t*>(slot + (off / G_::ROWB) * G_::LSTRIDE + off % G_::ROWB) = d[u];
+  }
+  __builtin_amdgcn_wave_barrier();
+  read_frag<T, D>(qf, slot, lane & 31, half);
+  __builtin_amdgcn_wave_barrier();
+  if (keep) {
+#pragma unroll
+    for (int s = 0; s < G_::NSTEP; ++s) {
+#pragma unroll
+      for (int e = 0; e < M::KPL; ++e) {
+        const int dch = half * G_::HALF + s * M::KPL + e;
+        if (!((keep[dch >> 5] >> (dch & 31)) & 1u)) {
+          if constexpr (M::KPL == 1) qf.o[s] = 0.0f;
+          else qf.o[s][e] = (__bf16)0.0f;
+        }
+      }
+    }
+  }
+}
+
 // Bit mask of the kept key channels of (b, g) (ThinK), built in LDS.
 template <int D, int NT>
 __device__ inline const uint32_t* build_keep(uint32_t* lds_keep, const WsParams& p, size_t bg, int tid) {
@@ -427,6 +470,9 @@ __global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
 
   __shared__ __attribute__((aligned(16))) unsigned char lds_k[3][TK * G_::LSTRIDE];
   __shared__ __attribute__((aligned(16))) uint8_t lds_valid[3][TK];
+  // query staging slots (bf16 only: fp32 rows would not fit next to the ring)
+  constexpr bool QLDS = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_q[QLDS ? NW : 1][QLDS ? 32 * G_::LSTRIDE : 16];
   __shared__ uint32_t lds_keep[D / 32];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
@@ -441,7 +487,8 @@ __global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
   const uint32_t* keep = build_keep<D, NT>(lds_keep, p, bg, tid);
   const int r = p.row0 + wave * 32 + col;  // this lane's query row
   Frag<T, D> qf;
-  load_query<T, D>(qf, p, bg, r, half, keep);
+  if constexpr (QLDS) load_query_rows<T, D>(qf, p, bg, p.row0 + wave * 32, lane, half, keep, lds_q[wave]);
+  else load_query<T, D>(qf, p, bg, r, half, keep);
   int lim = p.S - 1;
   if (p.causal && r < p.R) lim = min(p.S - 1, p.S - p.w + r % p.w);
   float m_run = kNegInf, z_run = 0.0f;
@@ -470,6 +517,9 @@ __global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_k[3][TK * G_::LSTRIDE];
   __shared__ __attribute__((aligned(16))) uint8_t lds_valid[3][TK];
   __shared__ float lds_red[3][2 * NW][TK];
+  // query staging slots (bf16 only: fp32 rows would not fit next to the ring)
+  constexpr bool QLDS = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_q[QLDS ? NW : 1][QLDS ? 32 * G_::LSTRIDE : 16];
   __shared__ uint32_t lds_keep[D / 32];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
@@ -484,7 +534,8 @@ __global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
   const uint32_t* keep = build_keep<D, NT>(lds_keep, p, bg, tid);
   const int rowblk = p.row0 + wave * 32;
   Frag<T, D> qf;
-  load_query<T, D>(qf, p, bg, rowblk + col, half, keep);
+  if constexpr (QLDS) load_query_rows<T, D>(qf, p, bg, rowblk, lane, half, keep, lds_q[wave]);
+  else load_query<T, D>(qf, p, bg, rowblk + col, half, keep);
   float nb[16];
   load_neg_lse(nb, p, bg, rowblk, half);
 
