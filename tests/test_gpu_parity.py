@@ -133,6 +133,23 @@ def test_topk(rows, n, k, n_tail, levels):
     assert np.array_equal(ig, O.topk_select(s.astype(np.float64), k, n_tail))
 
 
+def test_topk_two_values():
+    """Two distinct values, m of the larger per row: k = m takes the top value's
+    bin whole (the radix passes stop at the first digit); k = m - 5 and m + 5
+    leave ties at the threshold on either side of it."""
+    say("topk two values")
+    rng = np.random.default_rng(4242)
+    for n, m in ((3000, 700), (30001, 4000), (70000, 9000)):
+        rows = 3
+        s = np.full((rows, n), 0.25, np.float32)
+        for r in range(rows):
+            s[r, rng.choice(n, size=m, replace=False)] = np.float32(0.75)
+        for k, tail in ((m, 0), (m - 5, 0), (m + 5, 0), (m, 3)):
+            idx = lib().kvc_topk_select(dev(s), k, tail)
+            torch.cuda.synchronize()
+            assert np.array_equal(idx.cpu().numpy().astype(np.int64), O.topk_select(s.astype(np.float64), k, tail))
+
+
 def test_topk_signed_zeros():
     """Mixed-sign scores with exact +0 and -0 (equal, so the lower index wins)."""
     say("topk signed zeros")
