@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--streams", type=int, default=3,
                     help="layers are spread round-robin over this many streams in the timed region")
     ap.add_argument("--kernel-reps", type=int, default=20,
-                    help="passes over the layers in which each call of the dominant kernel is timed alone")
+                    help="passes over the layers, each timed as one run of back-to-back calls of the dominant kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -629,21 +629,22 @@ def main():
     wall = time.perf_counter() - t_wall
     elapsed_ms = start.elapsed_time(end)
 
-    # the dominant kernel timed alone: in each of kernel-reps passes over the
-    # layers every call runs on one stream between two HIP events recorded on it
+    # the dominant kernel timed alone: kernel-reps passes over the layers, each
+    # pass one run of back-to-back calls on one stream between two HIP events
+    # recorded on it, so that the average is the calls' own duration and not the
+    # latency of an event and a dispatch per call
     label, kcalls, kbytes, traffic = wl["kernel"]
     st0 = c.streams[0]
     st0.wait_stream(cur)
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.kernel_reps * len(kcalls))]
-    for r in range(args.kernel_reps):
-        for i, f in enumerate(kcalls):
-            a, b = kev[r * len(kcalls) + i]
-            a.record(st0)
+           for _ in range(args.kernel_reps)]
+    for a, b in kev:
+        a.record(st0)
+        for f in kcalls:
             f()
-            b.record(st0)
+        b.record(st0)
     torch.cuda.synchronize()
-    k_us = float(np.mean([a.elapsed_time(b) for (a, b) in kev])) * 1e3
+    k_us = float(np.mean([a.elapsed_time(b) for (a, b) in kev])) / len(kcalls) * 1e3
 
     units = wl["units_per_step"] * args.steps
     value = units / (elapsed_ms * 1e-3)
