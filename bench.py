@@ -431,7 +431,7 @@ def wl_scissor_decode(c: Ctx) -> dict:
             # the workload's steps again and again, each pass from a full cache
             t = n % nsteps
             if t == 0:
-                done["cache"] = O.ScissorhandsCache(1, 1, C, cfg.hist_len)
+                done["cache"] = O.LowAttentionState(1, 1, C, cfg.hist_len)
             cache = done["cache"]
             q = c.synth.stored_to_f64(c.synth.scissor_query(0, t), "bf16")[0:1, 0:G]
             done["units"] += int(cache.valid.sum())
@@ -471,6 +471,7 @@ def wl_scissor_queue_decode(c: Ctx) -> dict:
         ly["valid"] = c.empty((B, Hkv, C), torch.uint8)
         ly["hist"] = c.empty((cfg.hist_len, B * Hkv, W), torch.int32)
         ly["counts"] = c.empty((B, Hkv, C), torch.int16)
+        ly["since"] = c.empty((B, Hkv, C), torch.int64)
         ly["probs"] = c.empty((B, Hkv, C), torch.float32)
         ly["queue"] = c.empty((B, Hkv, m), torch.int32)
         ly["ws"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, C, D, 1), torch.uint8)
@@ -485,12 +486,12 @@ def wl_scissor_queue_decode(c: Ctx) -> dict:
                                            reduce=L.KVC_REDUCE_GROUP, causal=False)
         ly["record"], ly["record_step"] = L.bind_scissor_update(ly["valid"], ly["hist"], ly["counts"], st,
                                                                 probs=ly["probs"])
-        ly["refill"], ly["refill_step"] = L.bind_scissor_refill(ly["valid"], ly["counts"], cfg.hist_len, P,
-                                                                ly["queue"], ly["rf_ws"], st)
+        ly["refill"], ly["refill_step"] = L.bind_scissor_refill(ly["valid"], ly["counts"], ly["since"], cfg.hist_len,
+                                                                P, ly["queue"], ly["rf_ws"], st)
         ly["fill"] = [L.bind_scissor_insert(ly["kn"][t], ly["vn"][t], ly["k"], ly["v"], ly["valid"], ly["hist"],
-                                            ly["counts"], st) for t in range(nsteps)]
+                                            ly["counts"], ly["since"], st) for t in range(nsteps)]
         ly["pop"] = [L.bind_scissor_insert(ly["kn"][t], ly["vn"][t], ly["k"], ly["v"], ly["valid"], ly["hist"],
-                                           ly["counts"], st, queue=ly["queue"]) for t in range(nsteps)]
+                                           ly["counts"], ly["since"], st, queue=ly["queue"]) for t in range(nsteps)]
 
     state = {"t": 0, "ins": P, "qpos": m}
 
@@ -502,6 +503,7 @@ def wl_scissor_queue_decode(c: Ctx) -> dict:
             ly["valid"][:, :, :P] = 1
             ly["hist"].zero_()
             ly["counts"].zero_()
+            ly["since"].zero_()
         torch.cuda.synchronize()
         state.update(t=0, ins=P, qpos=m)
 
@@ -510,15 +512,17 @@ def wl_scissor_queue_decode(c: Ctx) -> dict:
         refill = ins >= C and qpos == m
         for ly in layers:
             if ins < C:
-                call, _, fill_pos = ly["fill"][t]
+                call, _, fill_pos, rec = ly["fill"][t]
                 fill_pos.value = ins
+                rec.value = t
                 call()
             else:
                 if refill:
                     ly["refill_step"].value = t - 1
                     ly["refill"]()
-                call, j, _ = ly["pop"][t]
+                call, j, _, rec = ly["pop"][t]
                 j.value = 0 if refill else qpos
+                rec.value = t
                 call()
             ly["score"][t]()
             ly["record_step"].value = t
@@ -541,7 +545,7 @@ def wl_scissor_queue_decode(c: Ctx) -> dict:
         G = H // Hkv
         k64 = c.synth.stored_to_f64(c.synth.scissor_cache(0), "bf16")[0:1, 0:1]
         kn, vn = c.synth.scissor_new_tokens(0, nsteps)
-        cache = O.ScissorhandsQueueCache(1, 1, C, D, cfg.hist_len, m, -1)
+        cache = O.ScissorhandsQueue(1, 1, C, D, cfg.hist_len, m, -1)
         cache.prefill(k64[:, :, :P], k64[:, :, :P])
         done = {"units": 0}
 

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 typedef enum {
   KVC_OK = 0,
@@ -120,65 +120,73 @@ kvc_status kvc_window_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_wi
 /*
  * kvc_scissor_update — Scissorhands low-attention history (record and evict).
  *
- * [COLD] cache.py hunks: a slot has low attention when its probability is below
- * uniform attention 1/keys.  The indicator goes into the circular history slot
- * (counter % history_window_size), which overwrites the oldest entry.  [COLD] PR
- * description: every m steps, per head, evict the tokens with the highest
- * fraction of unimportant attentions.  Bulk eviction leaves empty slots.
+ * [COLD] cache.py hunks: a slot counts as unimportant at a step when its
+ * probability is below that of uniform attention over the cache (1/keys), and
+ * the newest indicator overwrites the oldest of a circular window of steps.
+ * [COLD] PR description: every m steps each head evicts the tokens that were
+ * unimportant on the largest share of their observed steps; bulk eviction
+ * leaves empty slots.  [COLD] review thread: a token's share counts only the
+ * steps on which it was observed (both the numerator and the denominator).
  *
  * State (caller-owned device buffers, which persist across steps):
  *   valid  [B, Hkv, C] uint8, 1 = occupied slot, 0 = hole.
  *   hist   [hist_len][B*Hkv][ceil(C/32)] uint32 bit-planes.  Bit (c % 32) of word
- *          c/32 in plane p holds the indicator recorded at the last step t with
- *          t % hist_len == p.  Zero it before step 0.
+ *          c/32 in plane p holds the indicator recorded at the last recording r
+ *          with r % hist_len == p.  Zero it before the first recording.
  *   counts [B, Hkv, C] uint16, the number of set bits of slot c over the planes.
- *          Zero it before step 0.
+ *          Zero it before the first recording.
+ *   since  [B, Hkv, C] int64 or NULL: the number of recordings made before the
+ *          slot's current token arrived (kvc_scissor_insert writes it; 0 for
+ *          tokens present from the start).  NULL means 0 for every slot.
  *
- * When probs != NULL (record step `step`, counted from 0):
+ * When probs != NULL (recording number `step`, counted from 0):
  *   S_t = number of valid slots of (b, g);
  *   low = valid[c] and probs[c] < 1/S_t (compared exactly: probs is widened to double);
  *   plane = step % hist_len: counts += low - old bit;  bit <- low.
- *   If frac_out != NULL, it then writes
- *   frac_out[b,g,c] = counts / min(step+1, hist_len) at valid slots and -inf at holes.
- * When probs == NULL and frac_out != NULL, frac_out is written the same way from
- * the current counts, with `step` the last recorded step.  This serves sampled
- * recording ([COLD] review thread: Scissorhands checks and records the attention
- * only every M steps): record with step = the number of recordings so far, and
- * ask for the fraction at an eviction step that records nothing.
+ * If frac_out != NULL, it is written after the record (or from the current
+ * counts when probs == NULL, `step` then being the last recording's number):
+ *   n_obs = min(step + 1 - since[c], hist_len)  (the slot's own observations)
+ *   frac_out[b,g,c] = counts / n_obs (correctly rounded; 0 when n_obs <= 0) at
+ *   valid slots and -inf at holes.
+ * Sampled recording ([COLD] review thread: the paper checks the attention every
+ * M steps only): record with step = the number of recordings so far, and ask
+ * for the fraction alone at an eviction step that records nothing.
  * When evict_idx != NULL (after the record, if both are given):
  *   valid[b, g, evict_idx[b,g,e]] = 0 for e < n_evict.  The indices must be in
  *   [0, C) (e.g. kvc_topk_select over frac_out with k = n_evict).
  *
  *   probs     [B, Hkv, C] float32 group-mean probabilities of this step (the
  *             kvc_window_scores output with w = 1, KVC_REDUCE_GROUP and valid), or NULL.
- *   hist_len  1..65535 (400 in [COLD]).  step >= 0.
+ *   hist_len  1..65535 (400 in [COLD]).  step >= 0.  since 8-byte aligned.
  */
 kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_len, int64_t step,
                               const float* probs, uint8_t* valid, uint32_t* hist, uint16_t* counts,
-                              float* frac_out, const int32_t* evict_idx, int32_t n_evict,
+                              const int64_t* since, float* frac_out, const int32_t* evict_idx, int32_t n_evict,
                               hipStream_t stream);
 
 /*
  * kvc_scissor_refill — refill of the Scissorhands eviction queue.
  *
  * [COLD] PR description: instead of evicting in bulk, an eviction queue is
- * updated periodically and one token is evicted per step from it; cache.py hunk:
- * global_tokens = -1 keeps the prompt tokens.  The queue takes the m slots with
- * the highest fraction of low attentions:
- *   frac[b,g,c] = counts[b,g,c] / min(step+1, hist_len) at valid slots with
- *                 c >= n_protect, -inf elsewhere (holes and the protected prefix);
+ * rebuilt periodically and supplies one slot per step; cache.py hunk: a
+ * setting keeps the prompt tokens for good.  The queue takes the m slots of
+ * the largest low-attention fraction, each over its own observations:
+ *   frac[b,g,c] = counts / min(step + 1 - since[c], hist_len) (0 with no
+ *                 observation) at valid slots with c >= n_protect, -inf
+ *                 elsewhere (holes and the protected prefix);
  *   queue[b,g,:] = kvc_topk_select(frac[b,g,:], m)  (ascending positions, lowest
  *                 index first among equal fractions).
- * `step` is the last recorded step.  At least m slots of every row must be
+ * `step` is the last recording's number.  At least m slots of every row must be
  * valid and unprotected (else -inf entries, that is holes or protected slots,
  * fill the rest of the queue).
- *   valid [B, Hkv, C] uint8;  counts [B, Hkv, C] uint16 (kvc_scissor_update's state).
+ *   valid [B, Hkv, C] uint8;  counts [B, Hkv, C] uint16;  since [B, Hkv, C] int64
+ *         or NULL (kvc_scissor_update's state).
  *   0 <= n_protect < C;  1 <= m <= C - n_protect;  queue out [B, Hkv, m] int32.
  *   ws, ws_bytes  workspace (the fraction and the top-k's; see the conventions above).
  */
 kvc_status kvc_scissor_refill(int32_t B, int32_t Hkv, int32_t C, int32_t hist_len, int64_t step,
-                              const uint8_t* valid, const uint16_t* counts, int32_t n_protect, int32_t m,
-                              int32_t* queue, void* ws, size_t* ws_bytes, hipStream_t stream);
+                              const uint8_t* valid, const uint16_t* counts, const int64_t* since, int32_t n_protect,
+                              int32_t m, int32_t* queue, void* ws, size_t* ws_bytes, hipStream_t stream);
 
 /*
  * kvc_scissor_insert — a decode step's new token into the Scissorhands cache.
@@ -188,16 +196,20 @@ kvc_status kvc_scissor_refill(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
  * (b, g) is queue[b,g,j], or fill_pos for every row when queue is NULL (the
  * cache is not full yet).  Then:
  *   k_cache[b,g,slot,:] = k_new[b,g,:];  v_cache likewise (when v_new != NULL);
- *   valid[b,g,slot] = 1;  counts[b,g,slot] = 0;  the slot's bit is cleared in
- *   every history plane (the new token starts with an empty history).
+ *   valid[b,g,slot] = 1;  counts[b,g,slot] = 0;  since[b,g,slot] = rec;  the
+ *   slot's bit is cleared in every history plane (the new token starts with no
+ *   observation).
  * A slot outside [0, C) leaves its row unchanged.
+ *   rec       the number of recordings made before this token (>= 0); the next
+ *             kvc_scissor_update record is the first to observe it.
  *   k_new, v_new [B, Hkv, D];  k_cache, v_cache [B, Hkv, C, D] (16-byte aligned).
- *   hist, counts, valid: kvc_scissor_update's state.  0 <= j < m; 0 <= fill_pos < C.
+ *   hist, counts, valid, since: kvc_scissor_update's state (since required,
+ *   8-byte aligned).  0 <= j < m; 0 <= fill_pos < C.
  */
 kvc_status kvc_scissor_insert(int32_t B, int32_t Hkv, int32_t C, int32_t D, int32_t hist_len, kvc_dtype dt,
-                              const int32_t* queue, int32_t m, int32_t j, int32_t fill_pos, const void* k_new,
-                              const void* v_new, void* k_cache, void* v_cache, uint8_t* valid, uint32_t* hist,
-                              uint16_t* counts, hipStream_t stream);
+                              const int32_t* queue, int32_t m, int32_t j, int32_t fill_pos, int64_t rec,
+                              const void* k_new, const void* v_new, void* k_cache, void* v_cache, uint8_t* valid,
+                              uint32_t* hist, uint16_t* counts, int64_t* since, hipStream_t stream);
 
 /*
  * kvc_channel_scores — ThinK per-channel key importance.

@@ -47,15 +47,15 @@ def _load():
     SH = ctypes.POINTER(KvcShape)
     sig = {
         "kvc_window_scores": [SH, I32, P, P, P, P, I32, I32, I32, P, P, SZP, P],
-        "kvc_scissor_update": [I32, I32, I32, I32, I64, P, P, P, P, P, P, I32, P],
+        "kvc_scissor_update": [I32, I32, I32, I32, I64, P, P, P, P, P, P, P, I32, P],
         "kvc_channel_scores": [SH, I32, P, P, P, P, SZP, P],
         "kvc_topk_select": [P, I32, I32, I32, I32, P, P, SZP, P],
         "kvc_gather_compact": [SH, I32, P, P, P, I32, P, I32, P, P, P],
         "kvc_gather_compress": [SH, I32, P, P, P, I32, P, I32, P, P, P],
         "kvc_channel_expand": [I32, I32, I32, I32, I32, P, P, I32, P, P],
         "kvc_query_channels": [I32, I32, I32, I32, I32, I32, P, P, I32, P, P],
-        "kvc_scissor_refill": [I32, I32, I32, I32, I64, P, P, I32, I32, P, P, SZP, P],
-        "kvc_scissor_insert": [I32, I32, I32, I32, I32, I32, P, I32, I32, I32, P, P, P, P, P, P, P, P],
+        "kvc_scissor_refill": [I32, I32, I32, I32, I64, P, P, P, I32, I32, P, P, SZP, P],
+        "kvc_scissor_insert": [I32, I32, I32, I32, I32, I32, P, I32, I32, I32, I64, P, P, P, P, P, P, P, P, P],
         "kvc_status_string": [I32],
         "kvc_abi_version": [],
     }
@@ -149,29 +149,32 @@ def kvc_window_scores(q, k, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, 
     return scores
 
 
-def kvc_scissor_update(step, valid, hist, counts, probs=None, frac_out=None, evict_idx=None, stream=None):
-    """Record step `step` (probs given) and/or evict (evict_idx given).  valid [B,Hkv,C]
-    uint8, hist [hist_len, B*Hkv, ceil(C/32)] int32 bit-planes, counts [B,Hkv,C] int16
-    (read as uint16)."""
+def kvc_scissor_update(step, valid, hist, counts, probs=None, frac_out=None, evict_idx=None, since=None,
+                       stream=None):
+    """Record recording number `step` (probs given), write the fraction (frac_out
+    given) and/or evict (evict_idx given).  valid [B,Hkv,C] uint8, hist
+    [hist_len, B*Hkv, ceil(C/32)] int32 bit-planes, counts [B,Hkv,C] int16 (read as
+    uint16), since [B,Hkv,C] int64 or None (every slot observed from the start)."""
     _need(valid, "valid", 3)
     B, Hkv, C = valid.shape
     hist_len = hist.shape[0]
     n_evict = 0 if evict_idx is None else evict_idx.shape[2]
     _check("kvc_scissor_update", LIB.kvc_scissor_update(B, Hkv, C, hist_len, int(step), _ptr(probs), _ptr(valid),
-                                                        _ptr(hist), _ptr(counts), _ptr(frac_out), _ptr(evict_idx),
-                                                        n_evict, _stream(stream)))
+                                                        _ptr(hist), _ptr(counts), _ptr(since), _ptr(frac_out),
+                                                        _ptr(evict_idx), n_evict, _stream(stream)))
 
 
 def scissor_refill_ws_bytes(B, Hkv, C) -> int:
     n = ctypes.c_size_t(0)
-    _check("kvc_scissor_refill", LIB.kvc_scissor_refill(B, Hkv, C, 1, 0, None, None, 0, 1, None, None,
+    _check("kvc_scissor_refill", LIB.kvc_scissor_refill(B, Hkv, C, 1, 0, None, None, None, 0, 1, None, None,
                                                         ctypes.byref(n), None))
     return n.value
 
 
-def kvc_scissor_refill(step, valid, counts, hist_len, n_protect, m, queue=None, ws=None, stream=None):
-    """queue [B,Hkv,m] int32: the m slots of the highest low-attention fraction
-    (counts / min(step+1, hist_len)), never a hole or one of the first n_protect."""
+def kvc_scissor_refill(step, valid, counts, hist_len, n_protect, m, queue=None, ws=None, since=None, stream=None):
+    """queue [B,Hkv,m] int32: the m slots of the largest low-attention fraction
+    (counts over each slot's own observations, min(step+1-since, hist_len)), never a
+    hole or one of the first n_protect."""
     _need(valid, "valid", 3)
     B, Hkv, C = valid.shape
     if queue is None:
@@ -179,22 +182,23 @@ def kvc_scissor_refill(step, valid, counts, hist_len, n_protect, m, queue=None, 
     ws = _workspace(scissor_refill_ws_bytes(B, Hkv, C), valid.device, ws)
     n = ctypes.c_size_t(ws.numel() * ws.element_size())
     _check("kvc_scissor_refill", LIB.kvc_scissor_refill(B, Hkv, C, hist_len, int(step), _ptr(valid), _ptr(counts),
-                                                        n_protect, m, _ptr(queue), _ptr(ws), ctypes.byref(n),
-                                                        _stream(stream)))
+                                                        _ptr(since), n_protect, m, _ptr(queue), _ptr(ws),
+                                                        ctypes.byref(n), _stream(stream)))
     return queue
 
 
-def kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, queue=None, j=0, fill_pos=0,
-                       stream=None):
+def kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, since, rec, queue=None, j=0,
+                       fill_pos=0, stream=None):
     """The new token k_new/v_new [B,Hkv,D] into slot queue[:,:,j] (or fill_pos) of
-    k_cache/v_cache [B,Hkv,C,D]; the slot becomes valid with an empty history."""
+    k_cache/v_cache [B,Hkv,C,D]; the slot becomes valid with no observation
+    (since [B,Hkv,C] int64 <- rec, the recordings made before it)."""
     _need(k_cache, "k_cache", 4)
     B, Hkv, C, D = k_cache.shape
     m = 0 if queue is None else queue.shape[2]
     _check("kvc_scissor_insert", LIB.kvc_scissor_insert(B, Hkv, C, D, hist.shape[0], _dtype_code(k_cache),
-                                                        _ptr(queue), m, j, fill_pos, _ptr(k_new), _ptr(v_new),
-                                                        _ptr(k_cache), _ptr(v_cache), _ptr(valid), _ptr(hist),
-                                                        _ptr(counts), _stream(stream)))
+                                                        _ptr(queue), m, j, fill_pos, int(rec), _ptr(k_new),
+                                                        _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(valid),
+                                                        _ptr(hist), _ptr(counts), _ptr(since), _stream(stream)))
 
 
 def channel_scores_ws_bytes(B, H, Hkv, S, D, w) -> int:
@@ -377,42 +381,43 @@ def bind_query_channels(q, chan_idx, q_c, stream):
     return call
 
 
-def bind_scissor_update(valid, hist, counts, stream, probs=None, frac_out=None, evict_idx=None):
+def bind_scissor_update(valid, hist, counts, stream, probs=None, frac_out=None, evict_idx=None, since=None):
     """Pre-bound kvc_scissor_update; returns (call, step) with step a ctypes.c_int64
     whose value the caller sets before each call."""
     B, Hkv, C = valid.shape
     step = ctypes.c_int64(0)
     n_evict = 0 if evict_idx is None else evict_idx.shape[2]
-    args = (B, Hkv, C, hist.shape[0], step, _ptr(probs), _ptr(valid), _ptr(hist), _ptr(counts), _ptr(frac_out),
-            _ptr(evict_idx), n_evict, ctypes.c_void_p(stream.cuda_stream))
+    args = (B, Hkv, C, hist.shape[0], step, _ptr(probs), _ptr(valid), _ptr(hist), _ptr(counts), _ptr(since),
+            _ptr(frac_out), _ptr(evict_idx), n_evict, ctypes.c_void_p(stream.cuda_stream))
     call = _bound("kvc_scissor_update", args)
-    call.keep_alive = (valid, hist, counts, probs, frac_out, evict_idx, step)
+    call.keep_alive = (valid, hist, counts, probs, frac_out, evict_idx, since, step)
     return call, step
 
 
-def bind_scissor_refill(valid, counts, hist_len, n_protect, queue, ws, stream):
+def bind_scissor_refill(valid, counts, since, hist_len, n_protect, queue, ws, stream):
     """Pre-bound kvc_scissor_refill; returns (call, step)."""
     B, Hkv, C = valid.shape
     step = ctypes.c_int64(0)
     n = ctypes.c_size_t(ws.numel() * ws.element_size())
-    args = (B, Hkv, C, hist_len, step, _ptr(valid), _ptr(counts), n_protect, queue.shape[2], _ptr(queue), _ptr(ws),
-            ctypes.byref(n), ctypes.c_void_p(stream.cuda_stream))
+    args = (B, Hkv, C, hist_len, step, _ptr(valid), _ptr(counts), _ptr(since), n_protect, queue.shape[2],
+            _ptr(queue), _ptr(ws), ctypes.byref(n), ctypes.c_void_p(stream.cuda_stream))
     call = _bound("kvc_scissor_refill", args)
-    call.keep_alive = (valid, counts, queue, ws, step, n)
+    call.keep_alive = (valid, counts, since, queue, ws, step, n)
     return call, step
 
 
-def bind_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, stream, queue=None):
-    """Pre-bound kvc_scissor_insert; returns (call, j, fill_pos), the last two
-    ctypes.c_int32 values the caller sets before each call."""
+def bind_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, since, stream, queue=None):
+    """Pre-bound kvc_scissor_insert; returns (call, j, fill_pos, rec), ctypes values
+    the caller sets before each call (rec: the recordings made before the token)."""
     B, Hkv, C, D = k_cache.shape
-    j, fill_pos = ctypes.c_int32(0), ctypes.c_int32(0)
+    j, fill_pos, rec = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int64(0)
     m = 0 if queue is None else queue.shape[2]
-    args = (B, Hkv, C, D, hist.shape[0], _dtype_code(k_cache), _ptr(queue), m, j, fill_pos, _ptr(k_new), _ptr(v_new),
-            _ptr(k_cache), _ptr(v_cache), _ptr(valid), _ptr(hist), _ptr(counts), ctypes.c_void_p(stream.cuda_stream))
+    args = (B, Hkv, C, D, hist.shape[0], _dtype_code(k_cache), _ptr(queue), m, j, fill_pos, rec, _ptr(k_new),
+            _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(valid), _ptr(hist), _ptr(counts), _ptr(since),
+            ctypes.c_void_p(stream.cuda_stream))
     call = _bound("kvc_scissor_insert", args)
-    call.keep_alive = (k_new, v_new, k_cache, v_cache, valid, hist, counts, queue, j, fill_pos)
-    return call, j, fill_pos
+    call.keep_alive = (k_new, v_new, k_cache, v_cache, valid, hist, counts, since, queue, j, fill_pos, rec)
+    return call, j, fill_pos, rec
 
 
 def bind_channel_scores(q, k, out, ws, stream):

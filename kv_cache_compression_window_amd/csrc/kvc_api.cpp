@@ -83,7 +83,8 @@ kvc_status kvc_window_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_wi
 
 kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_len, int64_t step,
                               const float* probs, uint8_t* valid, uint32_t* hist, uint16_t* counts,
-                              float* frac_out, const int32_t* evict_idx, int32_t n_evict, hipStream_t stream) {
+                              const int64_t* since, float* frac_out, const int32_t* evict_idx, int32_t n_evict,
+                              hipStream_t stream) {
   if (B < 1 || Hkv < 1 || C < 1 || hist_len < 1 || hist_len > 65535 || step < 0) return KVC_ERR_SHAPE;
   if ((int64_t)B * Hkv > 0x7fffffffLL) return KVC_ERR_SHAPE;
   if (n_evict < 0 || n_evict > C) return KVC_ERR_SHAPE;
@@ -93,6 +94,7 @@ kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
   if (probs && (misaligned4(probs) || misaligned4(hist))) return KVC_ERR_ALIGN;
   if ((probs || frac_out) && (reinterpret_cast<uintptr_t>(counts) & 1u)) return KVC_ERR_ALIGN;
   if (frac_out && misaligned4(frac_out)) return KVC_ERR_ALIGN;
+  if (since && (reinterpret_cast<uintptr_t>(since) & 7u)) return KVC_ERR_ALIGN;
   kvc::ScissorArgs a;
   a.B = B;
   a.Hkv = Hkv;
@@ -103,6 +105,7 @@ kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
   a.valid = valid;
   a.hist = hist;
   a.counts = counts;
+  a.since = since;
   a.frac_out = frac_out;
   a.evict_idx = evict_idx;
   a.n_evict = evict_idx ? n_evict : 0;
@@ -111,8 +114,8 @@ kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
 }
 
 kvc_status kvc_scissor_refill(int32_t B, int32_t Hkv, int32_t C, int32_t hist_len, int64_t step,
-                              const uint8_t* valid, const uint16_t* counts, int32_t n_protect, int32_t m,
-                              int32_t* queue, void* ws, size_t* ws_bytes, hipStream_t stream) {
+                              const uint8_t* valid, const uint16_t* counts, const int64_t* since, int32_t n_protect,
+                              int32_t m, int32_t* queue, void* ws, size_t* ws_bytes, hipStream_t stream) {
   if (!ws_bytes) return KVC_ERR_NULL;
   if (B < 1 || Hkv < 1 || C < 1 || hist_len < 1 || hist_len > 65535 || step < 0) return KVC_ERR_SHAPE;
   if ((int64_t)B * Hkv > 65535) return KVC_ERR_SHAPE;
@@ -125,7 +128,9 @@ kvc_status kvc_scissor_refill(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
   }
   if (*ws_bytes < need) return KVC_ERR_WORKSPACE;
   if (!valid || !counts || !queue) return KVC_ERR_NULL;
-  if ((reinterpret_cast<uintptr_t>(counts) & 1u) || misaligned4(queue) || misaligned16(ws)) return KVC_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(counts) & 1u) || misaligned4(queue) || misaligned16(ws) ||
+      (reinterpret_cast<uintptr_t>(since) & 7u))
+    return KVC_ERR_ALIGN;
   kvc::ScissorRefillArgs a;
   a.B = B;
   a.Hkv = Hkv;
@@ -134,6 +139,7 @@ kvc_status kvc_scissor_refill(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
   a.step = step;
   a.valid = valid;
   a.counts = counts;
+  a.since = since;
   a.n_protect = n_protect;
   a.m = m;
   a.frac = static_cast<float*>(ws);
@@ -143,18 +149,20 @@ kvc_status kvc_scissor_refill(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
 }
 
 kvc_status kvc_scissor_insert(int32_t B, int32_t Hkv, int32_t C, int32_t D, int32_t hist_len, kvc_dtype dt,
-                              const int32_t* queue, int32_t m, int32_t j, int32_t fill_pos, const void* k_new,
-                              const void* v_new, void* k_cache, void* v_cache, uint8_t* valid, uint32_t* hist,
-                              uint16_t* counts, hipStream_t stream) {
+                              const int32_t* queue, int32_t m, int32_t j, int32_t fill_pos, int64_t rec,
+                              const void* k_new, const void* v_new, void* k_cache, void* v_cache, uint8_t* valid,
+                              uint32_t* hist, uint16_t* counts, int64_t* since, hipStream_t stream) {
   if (dt != KVC_F32 && dt != KVC_BF16) return KVC_ERR_DTYPE;
   if (B < 1 || Hkv < 1 || C < 1 || hist_len < 1 || hist_len > 65535) return KVC_ERR_SHAPE;
   if ((int64_t)B * Hkv > 0x7fffffffLL) return KVC_ERR_SHAPE;
   if (D != 64 && D != 128) return KVC_ERR_UNSUPPORTED;
   if (queue ? (m < 1 || j < 0 || j >= m) : (fill_pos < 0 || fill_pos >= C)) return KVC_ERR_SHAPE;
-  if (!k_new || !k_cache || !valid || !hist || !counts) return KVC_ERR_NULL;
+  if (rec < 0) return KVC_ERR_SHAPE;
+  if (!k_new || !k_cache || !valid || !hist || !counts || !since) return KVC_ERR_NULL;
   if (v_new && !v_cache) return KVC_ERR_NULL;
   if (misaligned16(k_new) || misaligned16(k_cache) || (v_new && (misaligned16(v_new) || misaligned16(v_cache))) ||
-      misaligned4(hist) || (reinterpret_cast<uintptr_t>(counts) & 1u) || (queue && misaligned4(queue)))
+      misaligned4(hist) || (reinterpret_cast<uintptr_t>(counts) & 1u) || (queue && misaligned4(queue)) ||
+      (reinterpret_cast<uintptr_t>(since) & 7u))
     return KVC_ERR_ALIGN;
   kvc::ScissorInsertArgs a;
   a.B = B;
@@ -173,6 +181,8 @@ kvc_status kvc_scissor_insert(int32_t B, int32_t Hkv, int32_t C, int32_t D, int3
   a.valid = valid;
   a.hist = hist;
   a.counts = counts;
+  a.rec = rec;
+  a.since = since;
   return hip_status(kvc::launch_scissor_insert(a, stream));
 }
 

@@ -73,6 +73,7 @@ struct ScissorArgs {
   uint8_t* valid;
   uint32_t* hist;
   uint16_t* counts;
+  const int64_t* since;  // [B, Hkv, C] recordings before each slot's token, or NULL (all 0)
   float* frac_out;
   const int32_t* evict_idx;
   int n_evict;
@@ -85,6 +86,7 @@ struct ScissorRefillArgs {
   long long step;
   const uint8_t* valid;
   const uint16_t* counts;
+  const int64_t* since;  // or NULL (all 0)
   int n_protect, m;
   float* frac;    // [B*Hkv*C] workspace
   void* topk_ws;  // top-k workspace
@@ -103,6 +105,8 @@ struct ScissorInsertArgs {
   uint8_t* valid;
   uint32_t* hist;
   uint16_t* counts;
+  long long rec;    // recordings made before the new token
+  int64_t* since;   // [B, Hkv, C]
 };
 hipError_t launch_scissor_insert(const ScissorInsertArgs& a, hipStream_t st);
 

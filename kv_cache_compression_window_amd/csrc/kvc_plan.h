@@ -32,6 +32,7 @@ struct WsPlan {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kMaxRows = 1024;  // G*w limit per KV head
+constexpr int kMergeLanes = 8;  // lanes of the merge kernel per (b, g, row)
 
 inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, WsPlan* p) {
   const int G = H / Hkv;
@@ -39,13 +40,15 @@ inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, WsPlan* p) {
   if (R > kMaxRows) return false;
   p->R = (int)R;
   p->store = R <= 16;
+  const long long bg = (long long)B * Hkv;
   // one wave per 32 query rows, up to 8 waves; beyond 256 rows the rows are
   // processed in chunks of 256 by successive launches
   const int nrb = (int)((R + 31) / 32);
   p->NW = nrb <= 1 ? 1 : nrb == 2 ? 2 : nrb <= 4 ? 4 : 8;
   p->nrch = (nrb + p->NW - 1) / p->NW;
   p->Rpad = p->nrch * p->NW * 32;
-  const long long bg = (long long)B * Hkv;
+  // the merge kernel indexes rows and lanes in 32-bit integers
+  if (bg * p->Rpad * kMergeLanes > 0x7fffffffLL) return false;
   // workgroups to aim for: about eight waves per CU on the two-pass path, two
   // four-wave streaming workgroups per CU on the (HBM-bound) stored-logits path
   const long long target = p->store ? 512 : 256LL * 8 / p->NW;

@@ -2,10 +2,11 @@
 //
 // Source: "Implement Scissorhands KV-cache compression & SnapKV prompt
 // compression" (cold-compress PR 11).  The cache.py hunks mark a slot low when
-// its attention is below uniform attention 1/keys.  The circular slot
-// counter % history_window_size holds the newest indicator.  The PR description
-// evicts per head the tokens with the highest fraction of unimportant
-// attentions, and bulk eviction leaves holes.
+// its attention is below that of uniform attention over the cache, and keep the
+// indicators of a circular window of recent steps.  The PR description ranks
+// each head's tokens by the share of their observed steps with low attention
+// and evicts the largest (bulk eviction leaves holes); the review thread counts
+// a token's share over the steps on which it was observed.
 //
 // The history is kept as bit-planes (one plane per circular slot, one bit per
 // cache slot) plus a running count per slot.  A step reads and writes one plane
@@ -19,11 +20,22 @@ namespace {
 
 constexpr int NTH = 256;
 
-__global__ __launch_bounds__(NTH) void scissor_record_kernel(int C, int W, int BHkv, int plane, int n_obs,
-                                                              const float* __restrict__ probs,
+// Low-attention fraction of one slot: its low count over its own observations,
+// the recordings since its token arrived (since = recordings made before it),
+// at most hist_len of them; 0 without an observation.  n_rec is the number of
+// recordings made so far.  Correctly rounded, so equal ratios give equal floats.
+__device__ inline float slot_fraction(int cnt, long long n_rec, long long since, int hist_len) {
+  long long obs = n_rec - since;
+  if (obs > hist_len) obs = hist_len;
+  return obs > 0 ? (float)((double)cnt / (double)obs) : 0.0f;
+}
+
+__global__ __launch_bounds__(NTH) void scissor_record_kernel(int C, int W, int BHkv, int plane, long long n_rec,
+                                                              int hist_len, const float* __restrict__ probs,
                                                               const uint8_t* __restrict__ valid,
                                                               uint32_t* __restrict__ hist,
                                                               uint16_t* __restrict__ counts,
+                                                              const int64_t* __restrict__ since,
                                                               float* __restrict__ frac_out) {
   __shared__ int red[NTH / 64];
   const size_t bg = blockIdx.x;
@@ -41,7 +53,6 @@ __global__ __launch_bounds__(NTH) void scissor_record_kernel(int C, int W, int B
 #pragma unroll
   for (int wv = 0; wv < NTH / 64; ++wv) S_t += red[wv];
   const double uniform = S_t > 0 ? 1.0 / (double)S_t : 0.0;
-  const float inv_obs = 1.0f / (float)n_obs;
 
   uint32_t* prow = hist + ((size_t)plane * BHkv + bg) * W;
   for (int c0 = 0; c0 < C; c0 += NTH) {
@@ -55,7 +66,8 @@ __global__ __launch_bounds__(NTH) void scissor_record_kernel(int C, int W, int B
     if (in) {
       const int cnew = (int)counts[bg * C + c] + (int)low - (int)old_bit;
       counts[bg * C + c] = (uint16_t)cnew;
-      if (frac_out) frac_out[bg * C + c] = v ? (float)cnew * inv_obs : kNegInf;
+      if (frac_out)
+        frac_out[bg * C + c] = v ? slot_fraction(cnew, n_rec, since ? since[bg * C + c] : 0, hist_len) : kNegInf;
     }
     // all lanes have read the old word before it is overwritten (ballot above
     // and the wave's single instruction stream order the reads first)
@@ -82,11 +94,13 @@ __device__ inline int nonzero_bytes(const uint4& u) {
 // thread t owns the 32-slot words t, t + NTH, ... of its (b, g) row, loads the
 // validity, probabilities, counts and old history word of a word with
 // independent 16-byte loads, and writes the new word itself.
-__global__ __launch_bounds__(NTH) void scissor_record_words_kernel(int C, int W, int BHkv, int plane, int n_obs,
+__global__ __launch_bounds__(NTH) void scissor_record_words_kernel(int C, int W, int BHkv, int plane,
+                                                                    long long n_rec, int hist_len,
                                                                     const float* __restrict__ probs,
                                                                     const uint8_t* __restrict__ valid,
                                                                     uint32_t* __restrict__ hist,
                                                                     uint16_t* __restrict__ counts,
+                                                                    const int64_t* __restrict__ since,
                                                                     float* __restrict__ frac_out) {
   __shared__ int red[NTH / 64];
   const size_t bg = blockIdx.x;
@@ -103,7 +117,6 @@ __global__ __launch_bounds__(NTH) void scissor_record_words_kernel(int C, int W,
 #pragma unroll
   for (int wv = 0; wv < NTH / 64; ++wv) S_t += red[wv];
   const double uniform = S_t > 0 ? 1.0 / (double)S_t : 0.0;
-  const float inv_obs = 1.0f / (float)n_obs;
 
   uint32_t* prow = hist + ((size_t)plane * BHkv + bg) * W;
   const float4* p4 = reinterpret_cast<const float4*>(probs + bg * C);
@@ -140,7 +153,7 @@ __global__ __launch_bounds__(NTH) void scissor_record_words_kernel(int C, int W,
       const int cold = (int)((cw[j >> 1] >> sh) & 0xFFFFu);
       const int cnew = cold + (int)low - (int)((old >> j) & 1u);
       cw[j >> 1] = (cw[j >> 1] & ~(0xFFFFu << sh)) | ((uint32_t)cnew << sh);
-      fr[j] = v ? (float)cnew * inv_obs : kNegInf;
+      if (f4) fr[j] = v ? slot_fraction(cnew, n_rec, since ? since[bg * C + 32 * wd + j] : 0, hist_len) : kNegInf;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) c4[4 * wd + i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
@@ -165,28 +178,32 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 // The fraction from the current counts, without a record (sampled recording:
 // an eviction step need not be a recording step; the eviction queue's refill):
-// counts / n_obs at valid slots, -inf at holes and at the first n_protect slots
-// of every row, as the record kernels write it.
-__global__ __launch_bounds__(NTH) void scissor_frac_kernel(long long total, int C, int n_obs, int n_protect,
-                                                            const uint8_t* __restrict__ valid,
+// the slot's fraction at valid slots, -inf at holes and at the first n_protect
+// slots of every row, as the record kernels write it.
+__global__ __launch_bounds__(NTH) void scissor_frac_kernel(long long total, int C, long long n_rec, int hist_len,
+                                                            int n_protect, const uint8_t* __restrict__ valid,
                                                             const uint16_t* __restrict__ counts,
+                                                            const int64_t* __restrict__ since,
                                                             float* __restrict__ frac_out) {
-  const float inv_obs = 1.0f / (float)n_obs;
   for (long long i = (long long)blockIdx.x * NTH + threadIdx.x; i < total; i += (long long)gridDim.x * NTH)
-    frac_out[i] = (valid[i] && (int)(i % C) >= n_protect) ? (float)counts[i] * inv_obs : kNegInf;
+    frac_out[i] = (valid[i] && (int)(i % C) >= n_protect)
+                      ? slot_fraction(counts[i], n_rec, since ? since[i] : 0, hist_len)
+                      : kNegInf;
 }
 
 // A new token into one slot per (b, g) (Scissorhands with insertion): its K and
-// V rows, valid, a zero count and a cleared bit in every history plane.  The
-// slot is queue[bg*m + j], or fill_pos for every row without a queue; a slot
-// outside [0, C) is skipped.
+// V rows, valid, a zero count, a cleared bit in every history plane, and `rec`
+// (the recordings made before it) as the start of its observations.  The slot
+// is queue[bg*m + j], or fill_pos for every row without a queue; a slot outside
+// [0, C) is skipped.
 __global__ __launch_bounds__(NTH) void scissor_insert_kernel(int C, int W, int BHkv, int hist_len, int units,
                                                               const int32_t* __restrict__ queue, int m, int j,
                                                               int fill_pos, const uint4* __restrict__ k_new,
                                                               const uint4* __restrict__ v_new,
                                                               uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
                                                               uint8_t* __restrict__ valid, uint32_t* __restrict__ hist,
-                                                              uint16_t* __restrict__ counts) {
+                                                              uint16_t* __restrict__ counts, long long rec,
+                                                              int64_t* __restrict__ since) {
   const size_t bg = blockIdx.x;
   const int tid = threadIdx.x;
   const int slot = queue ? queue[bg * m + j] : fill_pos;
@@ -200,6 +217,7 @@ __global__ __launch_bounds__(NTH) void scissor_insert_kernel(int C, int W, int B
   if (tid == 0) {
     valid[bg * C + slot] = 1;
     counts[bg * C + slot] = 0;
+    since[bg * C + slot] = rec;
   }
 }
 
@@ -208,23 +226,22 @@ __global__ __launch_bounds__(NTH) void scissor_insert_kernel(int C, int W, int B
 hipError_t launch_scissor(const ScissorArgs& a, hipStream_t st) {
   const int BHkv = a.B * a.Hkv;
   const int W = (a.C + 31) / 32;
+  const long long n_rec = a.step + 1;  // recordings made, the one at `step` included
   if (a.probs) {
     const int plane = (int)(a.step % a.hist_len);
-    const int64_t obs = a.step + 1 < a.hist_len ? a.step + 1 : a.hist_len;
     const bool words = a.C % 32 == 0 && aligned16(a.probs) && aligned16(a.valid) && aligned16(a.counts) &&
                        (!a.frac_out || aligned16(a.frac_out));
     if (words)
-      scissor_record_words_kernel<<<BHkv, NTH, 0, st>>>(a.C, W, BHkv, plane, (int)obs, a.probs, a.valid, a.hist,
-                                                        a.counts, a.frac_out);
+      scissor_record_words_kernel<<<BHkv, NTH, 0, st>>>(a.C, W, BHkv, plane, n_rec, a.hist_len, a.probs, a.valid,
+                                                        a.hist, a.counts, a.since, a.frac_out);
     else
-      scissor_record_kernel<<<BHkv, NTH, 0, st>>>(a.C, W, BHkv, plane, (int)obs, a.probs, a.valid, a.hist,
-                                                  a.counts, a.frac_out);
+      scissor_record_kernel<<<BHkv, NTH, 0, st>>>(a.C, W, BHkv, plane, n_rec, a.hist_len, a.probs, a.valid, a.hist,
+                                                  a.counts, a.since, a.frac_out);
   } else if (a.frac_out) {
     const long long total = (long long)BHkv * a.C;
-    const int obs = (int)(a.step + 1 < a.hist_len ? a.step + 1 : a.hist_len);
     const long long blocks = (total + NTH - 1) / NTH;
-    scissor_frac_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), NTH, 0, st>>>(total, a.C, obs, 0, a.valid,
-                                                                                    a.counts, a.frac_out);
+    scissor_frac_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), NTH, 0, st>>>(
+        total, a.C, n_rec, a.hist_len, 0, a.valid, a.counts, a.since, a.frac_out);
   }
   if (a.evict_idx && a.n_evict > 0) scissor_evict_kernel<<<BHkv, 256, 0, st>>>(a.C, a.n_evict, a.evict_idx, a.valid);
   return hipGetLastError();
@@ -232,10 +249,9 @@ hipError_t launch_scissor(const ScissorArgs& a, hipStream_t st) {
 
 hipError_t launch_scissor_refill(const ScissorRefillArgs& a, hipStream_t st) {
   const long long total = (long long)a.B * a.Hkv * a.C;
-  const int obs = (int)(a.step + 1 < a.hist_len ? a.step + 1 : a.hist_len);
   const long long blocks = (total + NTH - 1) / NTH;
-  scissor_frac_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), NTH, 0, st>>>(total, a.C, obs, a.n_protect, a.valid,
-                                                                                  a.counts, a.frac);
+  scissor_frac_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), NTH, 0, st>>>(
+      total, a.C, a.step + 1, a.hist_len, a.n_protect, a.valid, a.counts, a.since, a.frac);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topk(a.frac, a.B * a.Hkv, a.C, a.m, 0, a.queue, a.topk_ws, st);
@@ -246,7 +262,8 @@ hipError_t launch_scissor_insert(const ScissorInsertArgs& a, hipStream_t st) {
   scissor_insert_kernel<<<BHkv, NTH, 0, st>>>(a.C, (a.C + 31) / 32, BHkv, a.hist_len, a.row_bytes / 16, a.queue, a.m,
                                               a.j, a.fill_pos, static_cast<const uint4*>(a.k_new),
                                               static_cast<const uint4*>(a.v_new), static_cast<uint4*>(a.k_cache),
-                                              static_cast<uint4*>(a.v_cache), a.valid, a.hist, a.counts);
+                                              static_cast<uint4*>(a.v_cache), a.valid, a.hist, a.counts, a.rec,
+                                              a.since);
   return hipGetLastError();
 }
 

@@ -903,7 +903,6 @@ __global__ __launch_bounds__(256) void ws_finish_logits_kernel(WsParams p, int a
 // memory round trip for up to 32 chunks), then a butterfly over the eight lanes
 // merges the lane results in a fixed order.  Rows past R (padding) and rows with
 // no allowed key get +inf, so their probabilities are 0.
-constexpr int kMergeLanes = 8;
 
 __global__ __launch_bounds__(256) void ws_merge_kernel(const float2* __restrict__ part, float* __restrict__ lse,
                                                        int rows_total, int Rpad, int R, int nchunks) {

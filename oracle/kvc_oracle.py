@@ -31,7 +31,10 @@ Readings where the pages are silent or garbled (each is used below):
   R11 Scissorhands' "keys" is the number of valid cache slots S_t.
   R12 the low test compares the group-mean probability with 1/S_t, strictly.
   R13 Scissorhands records every step.
-  R14 the low-attention fraction is count / min(steps recorded, history).
+  R14 the low-attention fraction of a slot is its low count over its own
+      observations: the recordings since its token arrived, at most the last
+      `history` of them.  Without insertion that is min(recordings, history)
+      for every slot.
   R15 evicted slots become holes (no insertion), excluded from later softmaxes.
   R16 ThinK's norms sum over positions (window rows for q, all S keys for
       k); only that reading agrees with the materialised channel_attn form.
@@ -44,13 +47,14 @@ Readings where the pages are silent or garbled (each is used below):
   R27 SnapKV then ThinK: the channel scores use the kept keys only and the
       same window queries.
   R28 Scissorhands with insertion: a decode step puts its token into the next
-      free slot while there is one, else into the head of the eviction queue;
-      the slot's history and count start empty; the step then attends with the
-      new token in the cache and records.
-  R29 the eviction queue is refilled when it is empty on a full cache, with
+      never-used slot while there is one, else into the head of the eviction
+      queue; the token starts with no observation; the step then attends with
+      the new token in the cache and records.
+  R29 the eviction queue is rebuilt when it is empty on a full cache, with
       the top-k (O4) of the low-attention fraction, k = drop_amount,
       ascending positions, popped front to back.
-  R30 the first global_tokens slots are never queued (-1: the prompt).
+  R30 the first n_protect slots are never queued; a negative setting protects
+      the prompt, whatever its length.
   R25 a compressed key cache keeps the kept channels in chan_idx order; the
       zero-back writes them in increasing j, so a repeated entry keeps the
       last j.
@@ -113,20 +117,6 @@ def softmax_rows(logits: np.ndarray, allowed: np.ndarray) -> np.ndarray:
     z = e.sum(axis=-1, keepdims=True)
     with np.errstate(invalid="ignore", divide="ignore"):
         return np.where(z > 0, e / np.where(z > 0, z, 1.0), 0.0)
-
-
-def window_probs(q, k, valid=None, chan_keep=None, causal=True) -> np.ndarray:
-    """Window attention probabilities [B, H, w, S] (for small problems)."""
-    B, H, w, _ = q.shape
-    Hkv, S = k.shape[1], k.shape[2]
-    G = H // Hkv
-    out = np.zeros((B, H, w, S))
-    for b in range(B):
-        for g in range(Hkv):
-            vbg = None if valid is None else valid[b, g]
-            allowed = window_allowed(S, w, vbg, causal)
-            out[b, g * G:(g + 1) * G] = softmax_rows(window_logits(q, k, b, g, chan_keep), allowed[None])
-    return out
 
 
 def window_scores(q, k, valid=None, chan_keep=None, reduce=REDUCE_GROUP, causal=True) -> np.ndarray:
@@ -278,122 +268,171 @@ def query_channels(q: np.ndarray, chan_idx: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
-# O5: Scissorhands low-attention history and bulk eviction
+# O5: Scissorhands low-attention counting, bulk eviction and the eviction queue
 # ----------------------------------------------------------------------------
 
-class ScissorhandsCache:
-    """One layer's Scissorhands state in the page's own layout ([COLD]
-    cache.py hunks): attn_history[b, g, slot, step % history] holds the
-    low-attention indicator, attn_counter counts recorded steps.
+class LowAttentionState:
+    """One layer's Scissorhands bookkeeping, kept as its plain definition.
+
+    Source: "Implement Scissorhands KV-cache compression & SnapKV prompt
+    compression" (cold-compress PR 11).  The cache.py review hunks call a slot
+    unimportant at a step when its attention falls below that of uniform
+    attention over the cache, and keep those indicators for a bounded number
+    of recent steps.  The PR description ranks the tokens of each head by the
+    share of their observed steps on which they were unimportant, and the
+    review thread counts per token both the unimportant steps (the numerator)
+    and the observed steps (the denominator).
+
+    State per (batch, KV head, slot):
+      valid  the slot holds a token (bulk eviction leaves holes, R15);
+      since  index of the first recording that saw the slot's current token:
+             0 for tokens present before the first recording, the number of
+             recordings made before its insertion otherwise (R28).
+    and every recorded indicator array by recording index; only the last
+    `history` recordings can ever count, so older ones are dropped.
+
+    For one slot, with n recordings made so far, the recordings that count are
+    those with index r in [max(since, n - history), n) (R14):
+      count        how many of them found the slot low;
+      observations how many there are;
+      fraction     count / observations (0 without an observation), -inf at holes.
     """
 
-    def __init__(self, B: int, Hkv: int, C: int, history_window_size: int = 400):
+    def __init__(self, B: int, Hkv: int, C: int, history: int = 400):
+        self.history = history
         self.valid = np.ones((B, Hkv, C), dtype=bool)
-        self.attn_history = np.zeros((B, Hkv, C, history_window_size), dtype=np.int8)
-        self.attn_counter = 0
-        self.history_window_size = history_window_size
+        self.since = np.zeros((B, Hkv, C), dtype=np.int64)
+        self.recordings: dict[int, np.ndarray] = {}
+        self.n = 0
 
-    def update_attn_history(self, attn: np.ndarray) -> np.ndarray:
-        """[COLD] update_attn_history: a slot is low when its group-mean
-        probability is below uniform attention 1/keys (R11, R12); the
-        indicator goes into the circular slot attn_counter % history."""
-        keys = self.valid.sum(axis=-1, keepdims=True)
-        with np.errstate(divide="ignore"):
-            uniform = np.where(keys > 0, 1.0 / np.maximum(keys, 1), 0.0)
-        attn_is_low = self.valid & (attn < uniform)
-        self.attn_history[..., self.attn_counter % self.history_window_size] = attn_is_low
-        self.attn_counter += 1
-        return attn_is_low
+    @classmethod
+    def from_recordings(cls, valid, since, recordings: dict, n: int, history: int) -> "LowAttentionState":
+        """A state given explicitly: `recordings` maps recording index -> low
+        indicators [B, Hkv, C] (indices below n - history are ignored)."""
+        valid = np.asarray(valid, dtype=bool)
+        st = cls(*valid.shape, history)
+        st.valid = valid.copy()
+        st.since = np.asarray(since, dtype=np.int64).copy()
+        st.n = int(n)
+        st.recordings = {int(r): np.asarray(v, dtype=bool).copy() for r, v in recordings.items()
+                         if n - history <= r < n}
+        return st
 
-    def low_counts(self) -> np.ndarray:
-        return self.attn_history.sum(axis=-1, dtype=np.int64)
+    def record(self, probs: np.ndarray) -> np.ndarray:
+        """Record one step's group-mean probabilities [B, Hkv, C]: a valid slot
+        is low when its probability is below 1/S_t, S_t the number of valid
+        slots of its (batch, KV head) (R11, R12; strictly below)."""
+        n_valid = self.valid.sum(axis=-1, keepdims=True)
+        uniform = np.where(n_valid > 0, 1.0 / np.maximum(n_valid, 1), 0.0)
+        low = self.valid & (np.asarray(probs) < uniform)
+        self.recordings[self.n] = low.copy()
+        self.n += 1
+        self.recordings.pop(self.n - 1 - self.history, None)
+        return low
 
-    def low_fraction(self) -> np.ndarray:
-        """Fraction of recorded steps with low attention (R14); -inf at holes."""
-        n_obs = min(self.attn_counter, self.history_window_size)
-        frac = self.low_counts() / float(max(n_obs, 1))
+    def _first_counted(self) -> np.ndarray:
+        return np.maximum(self.since, self.n - self.history)
+
+    def counts(self) -> np.ndarray:
+        lo = self._first_counted()
+        c = np.zeros(self.valid.shape, dtype=np.int64)
+        for r, low in self.recordings.items():
+            c += low & (r >= lo)
+        return c
+
+    def observations(self) -> np.ndarray:
+        return np.maximum(self.n - self._first_counted(), 0)
+
+    def fraction(self) -> np.ndarray:
+        obs = self.observations()
+        frac = np.where(obs > 0, self.counts() / np.maximum(obs, 1), 0.0)
         return np.where(self.valid, frac, -np.inf)
 
     def evict(self, n_evict: int) -> np.ndarray:
-        """[COLD] PR description: evict, per head, the tokens with the highest
-        fraction of unimportant attentions; bulk eviction leaves empty slots
-        (R15).  Returns the evicted indices [B, Hkv, n_evict] (ascending)."""
+        """Bulk eviction ([COLD] PR description): per (batch, KV head), the
+        n_evict valid slots of the largest fraction (O4: the lowest index first
+        among equals) become holes.  Returns them [B, Hkv, n_evict] ascending."""
         B, Hkv, C = self.valid.shape
-        idx = topk_select(self.low_fraction().reshape(B * Hkv, C), n_evict).reshape(B, Hkv, n_evict)
+        idx = topk_select(self.fraction().reshape(B * Hkv, C), n_evict).reshape(B, Hkv, n_evict)
         for b in range(B):
             for g in range(Hkv):
                 self.valid[b, g, idx[b, g]] = False
         return idx
 
+    def occupy(self, slots: np.ndarray):
+        """A new token in slot slots[b, g] of each row: valid, observed from the
+        next recording on."""
+        B, Hkv = slots.shape
+        for b in range(B):
+            for g in range(Hkv):
+                e = int(slots[b, g])
+                self.valid[b, g, e] = True
+                self.since[b, g, e] = self.n
 
-def scissorhands_step(cache: ScissorhandsCache, q_t: np.ndarray, k: np.ndarray, t: int,
+
+def scissorhands_step(state: LowAttentionState, q_t: np.ndarray, k: np.ndarray, t: int,
                       evict_every: int, n_evict: int, record_every: int = 1):
-    """One decode step: group-mean attention of the step's query over the
-    valid slots, record it, and every evict_every steps evict n_evict slots
-    per (batch, KV head).  With record_every = M > 1 the attention is checked
-    and recorded only at the steps t with t % M == 0 ([COLD] review thread:
-    Scissorhands records every M steps), so the history and the fraction's
-    denominator count recorded steps (R26).  Returns (probs, low bits,
-    evicted indices or None); probs and low are None at a step that records
-    nothing."""
+    """One decode step: the step's group-mean attention over the valid slots is
+    recorded, and every evict_every steps n_evict slots per (batch, KV head)
+    are evicted.  With record_every = M > 1 the attention is checked and
+    recorded only at the steps t with t % M == 0 ([COLD] review thread: the
+    paper checks the attention every M steps only), so the window and the
+    observations count recordings (R26).  Returns (probs, low bits, evicted
+    indices or None); probs and low are None at a step that records nothing."""
     probs = low = None
     if t % record_every == 0:
-        probs = window_scores(q_t, k, valid=cache.valid, reduce=REDUCE_GROUP, causal=False)
-        low = cache.update_attn_history(probs)
-    evicted = cache.evict(n_evict) if (t + 1) % evict_every == 0 else None
+        probs = window_scores(q_t, k, valid=state.valid, reduce=REDUCE_GROUP, causal=False)
+        low = state.record(probs)
+    evicted = state.evict(n_evict) if (t + 1) % evict_every == 0 else None
     return probs, low, evicted
 
 
-class ScissorhandsQueueCache(ScissorhandsCache):
-    """Scissorhands with insertion and an eviction queue ([COLD] PR
-    description: instead of bulk evictions, an eviction queue is refilled
-    periodically and one token is evicted per step; cache.py hunk:
-    global_tokens = -1 keeps the prompt).  The cache has C slots and holds K
-    and V.  Readings R28-R30:
-      * a decode step inserts its token into the next free slot while there is
-        one, else into the slot at the head of the eviction queue; the slot's
-        history and count start empty;
-      * when the queue is empty on a full cache it is refilled with the
-        drop_amount slots of the highest low-attention fraction (the top-k of
-        O4, ascending positions, popped front to back);
-      * the first global_tokens slots are never queued (-1: the prompt).
+class ScissorhandsQueue(LowAttentionState):
+    """Scissorhands with insertion and an eviction queue ([COLD] PR description:
+    the queue is rebuilt periodically and supplies one slot per step, so no
+    hole is left; cache.py hunk: a setting keeps the prompt tokens for good).
+    The cache has C slots holding K and V.  Readings R28-R30:
+      * a step's token goes to the next never-used slot while there is one,
+        else to the slot at the head of the queue; it starts unobserved;
+      * an empty queue on a full cache is rebuilt from the drop_amount slots of
+        the largest fraction (O4: ascending positions, popped front to back);
+      * the first n_protect slots are never queued; a negative setting
+        protects the prompt, whatever its length.
     """
 
-    def __init__(self, B: int, Hkv: int, C: int, D: int, history_window_size: int, drop_amount: int,
-                 global_tokens: int):
-        super().__init__(B, Hkv, C, history_window_size)
+    def __init__(self, B: int, Hkv: int, C: int, D: int, history: int, drop_amount: int, protect: int):
+        super().__init__(B, Hkv, C, history)
         self.valid[:] = False
         self.k = np.zeros((B, Hkv, C, D))
         self.v = np.zeros((B, Hkv, C, D))
         self.drop_amount = drop_amount
-        self.global_tokens = global_tokens
-        self.insertions = 0
+        self.protect = protect
+        self.n_protect = max(protect, 0)
+        self.filled = 0
         self.queue = np.zeros((B, Hkv, 0), dtype=np.int64)
         self.queue_pos = 0
 
     def prefill(self, k_prompt: np.ndarray, v_prompt: np.ndarray):
-        """The prompt fills the first P slots; global_tokens = -1 becomes P."""
+        """The prompt takes the first P slots (observed from the first recording)."""
         P = k_prompt.shape[2]
         self.k[:, :, :P] = k_prompt
         self.v[:, :, :P] = v_prompt
         self.valid[:, :, :P] = True
-        if self.insertions == 0 and self.global_tokens == -1:
-            self.global_tokens = P
-        self.insertions += P
+        self.filled = P
+        if self.protect < 0:
+            self.n_protect = P
 
     def refill(self):
-        """The drop_amount evictable slots of the highest low-attention fraction."""
         B, Hkv, C = self.valid.shape
-        frac = self.low_fraction()
-        frac[..., :self.global_tokens] = -np.inf
+        frac = self.fraction()
+        frac[..., :self.n_protect] = -np.inf
         self.queue = topk_select(frac.reshape(B * Hkv, C), self.drop_amount).reshape(B, Hkv, self.drop_amount)
         self.queue_pos = 0
 
     def next_slots(self) -> np.ndarray:
-        """Slot of the next token per (b, g): the next free slot, else the head of the queue."""
         B, Hkv, C = self.valid.shape
-        if self.insertions < C:
-            return np.full((B, Hkv), self.insertions, dtype=np.int64)
+        if self.filled < C:
+            return np.full((B, Hkv), self.filled, dtype=np.int64)
         if self.queue_pos >= self.queue.shape[2]:
             self.refill()
         slots = self.queue[:, :, self.queue_pos].copy()
@@ -401,27 +440,24 @@ class ScissorhandsQueueCache(ScissorhandsCache):
         return slots
 
     def insert(self, slots: np.ndarray, k_new: np.ndarray, v_new: np.ndarray):
-        """Write the new token into its slots with an empty history."""
         B, Hkv = slots.shape
         for b in range(B):
             for g in range(Hkv):
                 e = int(slots[b, g])
                 self.k[b, g, e] = k_new[b, g]
                 self.v[b, g, e] = v_new[b, g]
-                self.valid[b, g, e] = True
-                self.attn_history[b, g, e, :] = 0
-        self.insertions += 1
+        self.occupy(slots)
+        self.filled += 1
 
 
-def scissorhands_queue_step(cache: ScissorhandsQueueCache, q_t: np.ndarray, k_new: np.ndarray,
-                            v_new: np.ndarray):
+def scissorhands_queue_step(cache: ScissorhandsQueue, q_t: np.ndarray, k_new: np.ndarray, v_new: np.ndarray):
     """One decode step with insertion: place the new token (R28), attend with
-    the step's query over the valid slots (the new token included) and record
-    the low bits.  Returns (slots, probs, low bits)."""
+    the step's query over the valid slots, the new token included, and record.
+    Returns (slots, probs, low bits)."""
     slots = cache.next_slots()
     cache.insert(slots, k_new, v_new)
     probs = window_scores(q_t, cache.k, valid=cache.valid, reduce=REDUCE_GROUP, causal=False)
-    low = cache.update_attn_history(probs)
+    low = cache.record(probs)
     return slots, probs, low
 
 

@@ -80,3 +80,40 @@ def check_gather(k_out, v_out, k_host, v_host, idx_gpu, chan_host=None):
     assert np.array_equal(host_bits(k_out).view(np.uint8), np.ascontiguousarray(ko).view(np.uint8)), "K gather"
     if v_out is not None:
         assert np.array_equal(host_bits(v_out).view(np.uint8), np.ascontiguousarray(vo).view(np.uint8)), "V gather"
+
+
+def unpack_planes(hist: np.ndarray, bg: int, C: int) -> np.ndarray:
+    """[C, hist_len] 0/1 matrix of the bit-planes of row bg of a
+    [hist_len, rows, ceil(C/32)] int32 history."""
+    words = np.ascontiguousarray(hist[:, bg, :]).astype(np.uint32)  # [hist_len, W]
+    bits = np.unpackbits(words.view(np.uint8).reshape(words.shape[0], -1), bitorder="little", axis=1)
+    return bits[:, :C].T.astype(np.int8)
+
+
+def unpack_all_planes(hist: np.ndarray, C: int) -> np.ndarray:
+    """[rows, C, hist_len] 0/1 matrix of every row's bit-planes."""
+    words = np.ascontiguousarray(hist).astype(np.uint32)  # [hist_len, rows, W]
+    hl, rows, W = words.shape
+    bits = np.unpackbits(words.view(np.uint8).reshape(hl, rows, W * 4), bitorder="little", axis=2)
+    return np.ascontiguousarray(bits[:, :, :C].transpose(1, 2, 0))
+
+
+def oracle_state(valid, planes: np.ndarray, n_rec: int, hist_len: int, since=None) -> "O.LowAttentionState":
+    """The oracle's Scissorhands state taken from the GPU's: validity [..., C],
+    planes [..., C, hist_len] (recording r lives in plane r % hist_len), the
+    recordings made so far and the per-slot observation start (None: 0)."""
+    valid = np.asarray(valid, dtype=bool)
+    shape = valid.shape
+    valid3 = valid.reshape((-1,) + shape[-1:])[None] if valid.ndim != 3 else valid
+    planes = np.asarray(planes).reshape(valid3.shape + (hist_len,))
+    recs = {r: planes[..., r % hist_len] for r in range(max(0, n_rec - hist_len), n_rec)}
+    since = np.zeros(valid3.shape, dtype=np.int64) if since is None else np.asarray(since).reshape(valid3.shape)
+    return O.LowAttentionState.from_recordings(valid3, since, recs, n_rec, hist_len)
+
+
+def low_bits_agree(got: np.ndarray, low: np.ndarray, probs: np.ndarray, valid: np.ndarray) -> bool:
+    """The GPU's low bits equal the oracle's except where the probability lies
+    within a relative 1e-5 of 1/S_t (both sides decide from fp32 vs fp64 sums)."""
+    n_valid = np.asarray(valid).sum(axis=-1, keepdims=True)
+    near = np.abs(probs * n_valid - 1.0) <= GAP
+    return bool(np.array_equal(np.asarray(got, dtype=bool)[~near], np.asarray(low, dtype=bool)[~near]))

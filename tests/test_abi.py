@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.abi_version() == 2
+    assert lib.abi_version() == 3
     for code in range(8):
         s = lib.LIB.kvc_status_string(code).decode()
         assert s and s != "unknown status"
@@ -68,6 +68,9 @@ def test_window_scores_validation(lib):
     assert ws_call(lib, S(1, 32, 8, 63, 128, 64)) == 2         # w > S
     assert ws_call(lib, S(1, 32, 8, 4096, 96, 64)) == 6        # D
     assert ws_call(lib, S(1, 64, 8, 4096, 128, 256)) == 6      # G*w > 1024
+    # (b, g, padded row) x merge lanes past 2^31 - 1: 4096 x 1024 x 64 x 8 = 2^31
+    assert ws_call(lib, S(4096, 1024, 1024, 4096, 128, 64)) == 6
+    assert ws_call(lib, S(2048, 1024, 1024, 4096, 128, 64), ws=None) == 0  # 2^30 is still fine (size query)
     assert ws_call(lib, ok, chan=FAKE, d_keep=0) == 2
     assert ws_call(lib, ok, chan=FAKE, d_keep=129) == 2
     assert ws_call(lib, ok, q=None) == 1
@@ -92,21 +95,27 @@ def test_window_scores_workspace_grows_with_rows(lib):
 
 def test_scissor_validation(lib):
     f = lib.LIB.kvc_scissor_update
-    assert f(0, 8, 4096, 400, 0, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 2
-    assert f(8, 8, 4096, 0, 0, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 2
-    assert f(8, 8, 4096, 70000, 0, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 2
-    assert f(8, 8, 4096, 400, -1, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 2
-    assert f(8, 8, 4096, 400, 0, FAKE, None, FAKE, FAKE, None, None, 0, None) == 1
-    assert f(8, 8, 4096, 400, 0, FAKE, FAKE, None, FAKE, None, None, 0, None) == 1
-    assert f(8, 8, 4096, 400, 0, FAKE, FAKE, FAKE, None, None, None, 0, None) == 1
-    assert f(8, 8, 4096, 400, 0, None, FAKE, None, None, None, FAKE, 4097, None) == 2
-    assert f(8, 8, 4096, 400, 0, ctypes.c_void_p(0x100002), FAKE, FAKE, FAKE, None, None, 0, None) == 4
+
+    def up(B=8, Hkv=8, C=4096, hist=400, step=0, probs=FAKE, valid=FAKE, hist_p=FAKE, counts=FAKE, since=None,
+           frac=None, ev=None, n_ev=0):
+        return f(B, Hkv, C, hist, step, probs, valid, hist_p, counts, since, frac, ev, n_ev, None)
+    assert up(B=0) == 2
+    assert up(hist=0) == 2
+    assert up(hist=70000) == 2
+    assert up(step=-1) == 2
+    assert up(valid=None) == 1
+    assert up(hist_p=None) == 1
+    assert up(counts=None) == 1
+    assert up(probs=None, hist_p=None, counts=None, ev=FAKE, n_ev=4097) == 2
+    assert up(probs=ctypes.c_void_p(0x100002)) == 4
     # the fraction alone (sampled recording) needs the counts, 2-byte aligned, and a 4-byte aligned output
-    assert f(8, 8, 4096, 400, 3, None, FAKE, None, None, FAKE, None, 0, None) == 1
-    assert f(8, 8, 4096, 400, 3, None, FAKE, None, ctypes.c_void_p(0x100001), FAKE, None, 0, None) == 4
-    assert f(8, 8, 4096, 400, 3, None, FAKE, None, FAKE, ctypes.c_void_p(0x100002), None, 0, None) == 4
+    assert up(step=3, probs=None, hist_p=None, counts=None, frac=FAKE) == 1
+    assert up(step=3, probs=None, hist_p=None, counts=ctypes.c_void_p(0x100001), frac=FAKE) == 4
+    assert up(step=3, probs=None, hist_p=None, frac=ctypes.c_void_p(0x100002)) == 4
+    # the per-slot observation start is 8-byte aligned
+    assert up(step=3, probs=None, hist_p=None, frac=FAKE, since=ctypes.c_void_p(0x100004)) == 4
     # nothing to do is not an error
-    assert f(8, 8, 4096, 400, 0, None, FAKE, None, None, None, None, 0, None) == 0
+    assert up(probs=None, hist_p=None, counts=None) == 0
 
 
 def test_scissor_queue_validation(lib):
@@ -114,37 +123,45 @@ def test_scissor_queue_validation(lib):
     r = lib.LIB.kvc_scissor_refill
     n = ctypes.c_size_t(1 << 30)
     q = ctypes.c_size_t(0)
-    assert r(8, 8, 4096, 400, 10, None, None, 100, 64, None, None, ctypes.byref(q), None) == 0 and q.value > 0
+
+    def rf(step=10, valid=FAKE, counts=FAKE, since=FAKE, prot=0, m=64, queue=FAKE, ws=FAKE, nb=n):
+        return r(8, 8, 4096, 400, step, valid, counts, since, prot, m, queue, ws,
+                 None if nb is None else ctypes.byref(nb), None)
+    assert rf(valid=None, counts=None, since=None, prot=100, queue=None, ws=None, nb=q) == 0 and q.value > 0
     assert q.value >= 8 * 8 * 4096 * 4  # the fraction lives in the workspace
-    assert r(8, 8, 4096, 400, 10, FAKE, FAKE, 100, 64, FAKE, FAKE, None, None) == 1
-    assert r(8, 8, 4096, 400, -1, FAKE, FAKE, 100, 64, FAKE, FAKE, ctypes.byref(n), None) == 2
-    assert r(8, 8, 4096, 400, 10, FAKE, FAKE, 4096, 1, FAKE, FAKE, ctypes.byref(n), None) == 2  # all protected
-    assert r(8, 8, 4096, 400, 10, FAKE, FAKE, 4000, 97, FAKE, FAKE, ctypes.byref(n), None) == 2  # m > C - n_protect
-    assert r(8, 8, 4096, 400, 10, FAKE, FAKE, 0, 0, FAKE, FAKE, ctypes.byref(n), None) == 2
-    assert r(8, 8, 4096, 400, 10, None, FAKE, 0, 64, FAKE, FAKE, ctypes.byref(n), None) == 1
-    assert r(8, 8, 4096, 400, 10, FAKE, ctypes.c_void_p(0x100001), 0, 64, FAKE, FAKE, ctypes.byref(n), None) == 4
-    small = ctypes.c_size_t(16)
-    assert r(8, 8, 4096, 400, 10, FAKE, FAKE, 0, 64, FAKE, FAKE, ctypes.byref(small), None) == 5
+    assert rf(prot=100, nb=None) == 1
+    assert rf(step=-1, prot=100) == 2
+    assert rf(prot=4096, m=1) == 2  # all protected
+    assert rf(prot=4000, m=97) == 2  # m > C - n_protect
+    assert rf(m=0) == 2
+    assert rf(valid=None) == 1
+    assert rf(counts=ctypes.c_void_p(0x100001)) == 4
+    assert rf(since=ctypes.c_void_p(0x100004)) == 4
+    assert rf(nb=ctypes.c_size_t(16)) == 5
 
     i = lib.LIB.kvc_scissor_insert
-    args = dict(B=8, Hkv=8, C=4096, D=128, hist=400, dt=1, queue=FAKE, m=64, j=3, fill=0, k_new=FAKE, v_new=FAKE,
-                k_cache=FAKE, v_cache=FAKE, valid=FAKE, hist_p=FAKE, counts=FAKE)
+    args = dict(B=8, Hkv=8, C=4096, D=128, hist=400, dt=1, queue=FAKE, m=64, j=3, fill=0, rec=7, k_new=FAKE,
+                v_new=FAKE, k_cache=FAKE, v_cache=FAKE, valid=FAKE, hist_p=FAKE, counts=FAKE, since=FAKE)
 
     def call(**kw):
         a = {**args, **kw}
         return i(a["B"], a["Hkv"], a["C"], a["D"], a["hist"], a["dt"], a["queue"], a["m"], a["j"], a["fill"],
-                 a["k_new"], a["v_new"], a["k_cache"], a["v_cache"], a["valid"], a["hist_p"], a["counts"], None)
+                 a["rec"], a["k_new"], a["v_new"], a["k_cache"], a["v_cache"], a["valid"], a["hist_p"], a["counts"],
+                 a["since"], None)
     assert call(D=96) == 6
     assert call(dt=4) == 3
     assert call(j=64) == 2
     assert call(queue=None, fill=4096) == 2
     assert call(queue=None, fill=-1) == 2
     assert call(hist=0) == 2
+    assert call(rec=-1) == 2
     assert call(k_new=None) == 1
     assert call(v_cache=None) == 1
     assert call(counts=None) == 1
+    assert call(since=None) == 1
     assert call(k_cache=ODD) == 4
     assert call(counts=ctypes.c_void_p(0x100001)) == 4
+    assert call(since=ctypes.c_void_p(0x100004)) == 4
 
 
 def test_topk_validation(lib):

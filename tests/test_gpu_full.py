@@ -23,7 +23,8 @@ import torch
 
 from kv_cache_compression_window_amd import configs, synth
 from oracle import kvc_oracle as O
-from tests.gpu_util import check_gather, check_kept, check_scores, dev, host_bits
+from tests.gpu_util import (check_gather, check_kept, check_scores, dev, host_bits, low_bits_agree,
+                             oracle_state, unpack_all_planes, unpack_planes)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,17 +101,15 @@ def test_c3_tova_batched_full():
     check_gather(ko, vo, p.k, p.v, ig)
 
 
-def unpack_rows(planes: np.ndarray, C: int) -> np.ndarray:
-    """planes [hist_len, W] uint32 of one row -> [C, hist_len] 0/1."""
-    words = planes.astype(np.uint32)
-    bits = np.unpackbits(words.view(np.uint8).reshape(words.shape[0], -1), bitorder="little", axis=1)
-    return bits[:, :C].T.astype(np.int8)
-
-
 def test_c4_scissorhands_decode_full_sampled():
+    """c4 at full size: all 800 steps on all 64 (b, g) rows.  Three rows are
+    followed in teacher-forced lockstep at every step (probabilities, low bits,
+    counts); at each of the 12 eviction steps every row is checked:
+    probabilities, low bits, counts, fractions, the eviction set and the
+    validity after it."""
     cfg = configs.SCISSOR_DECODE
     say(cfg.name)
-    B, H, Hkv, C, D = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D
+    B, H, Hkv, C, D, hl = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.hist_len
     G = H // Hkv
     L = lib()
     kb = synth.scissor_cache(0)
@@ -119,14 +118,13 @@ def test_c4_scissorhands_decode_full_sampled():
     sample = [(0, 0), (3, 5), (7, 7)]
     W = (C + 31) // 32
     valid = torch.ones((B, Hkv, C), dtype=torch.uint8, device="cuda")
-    hist = torch.zeros((cfg.hist_len, B * Hkv, W), dtype=torch.int32, device="cuda")
+    hist = torch.zeros((hl, B * Hkv, W), dtype=torch.int32, device="cuda")
     counts = torch.zeros((B, Hkv, C), dtype=torch.int16, device="cuda")
     frac = torch.empty((B, Hkv, C), dtype=torch.float32, device="cuda")
     bgs = [b * Hkv + g for b, g in sample]
     for t in range(cfg.steps):
         qb = synth.scissor_query(0, t)
         v_before = valid.cpu().numpy()
-        h_before = hist[:, bgs, :].cpu().numpy()
         probs = L.kvc_window_scores(dev(qb, "bf16"), kd, valid=valid, reduce=L.KVC_REDUCE_GROUP, causal=False)
         evict = (t + 1) % cfg.evict_every == 0
         L.kvc_scissor_update(t, valid, hist, counts, probs=probs, frac_out=frac if evict else None)
@@ -143,35 +141,73 @@ def test_c4_scissorhands_decode_full_sampled():
             ref_p = O.window_scores(q64[b:b + 1, g * G:(g + 1) * G], k64[b:b + 1, g:g + 1],
                                     valid=v_before[b:b + 1, g:g + 1], reduce=O.REDUCE_GROUP, causal=False)[0, 0]
             check_scores(pg[b, g], ref_p, f"c4 step {t} ({b},{g}) probs")
-            # the oracle adopts the GPU's state, then takes the step
-            cache = O.ScissorhandsCache(1, 1, C, cfg.hist_len)
-            cache.valid[0, 0] = v_before[b, g].astype(bool)
-            cache.attn_history[0, 0] = unpack_rows(h_before[:, si, :], C)
-            cache.attn_counter = t
-            low = cache.update_attn_history(ref_p[None, None])[0, 0]
-            planes = unpack_rows(h_now[:, si, :], C)
-            got = planes[:, t % cfg.hist_len].astype(bool)
-            n_valid = int(v_before[b, g].sum())
-            near = np.abs(ref_p * n_valid - 1.0) <= 1e-5
-            assert np.array_equal(got[~near], low[~near]), f"step {t} ({b},{g}) low bits"
+            planes = unpack_planes(h_now, si, C)
+            # the oracle takes the step on the GPU's state: the low test needs only validity and probabilities
+            low = oracle_state(v_before[b, g], planes, t, hl).record(ref_p[None, None])[0, 0]
+            assert low_bits_agree(planes[:, t % hl], low, ref_p, v_before[b, g]), f"step {t} ({b},{g}) low bits"
             assert np.array_equal(cnt[b, g], planes.sum(axis=1)), f"step {t} ({b},{g}) counts"
-            assert cnt[b, g].max() <= min(t + 1, cfg.hist_len)
-            if evict:
-                cache.attn_history[0, 0] = planes
-                fr = cache.low_fraction()[0, 0]
-                fg = frac.cpu().numpy()[b, g]
-                assert np.array_equal(np.isinf(fg), np.isinf(fr))
-                fin = np.isfinite(fr)
-                assert np.allclose(fg[fin], fr[fin], rtol=1e-6, atol=0)
-                want = O.topk_select(fr[None], cfg.n_evict)[0]
-                assert np.array_equal(idx.cpu().numpy()[b, g], want), f"step {t} ({b},{g}) evictions"
-                v_exp = v_before[b, g].copy()
-                v_exp[want] = 0
-                assert np.array_equal(valid.cpu().numpy()[b, g], v_exp)
-        if t % 100 == 0:
-            say(f"  step {t} ok")
+            assert cnt[b, g].max() <= min(t + 1, hl)
+        if evict:
+            # every row at the eviction steps
+            ref_all = O.window_scores(q64, k64, valid=v_before, reduce=O.REDUCE_GROUP, causal=False)
+            check_scores(pg, ref_all, f"c4 step {t} probs (all rows)")
+            planes_all = unpack_all_planes(hist.cpu().numpy(), C).reshape(B, Hkv, C, hl)
+            low_all = O.LowAttentionState.from_recordings(v_before, np.zeros((B, Hkv, C), np.int64), {}, t,
+                                                          hl).record(ref_all)
+            assert low_bits_agree(planes_all[..., t % hl], low_all, ref_all, v_before), f"step {t} low bits"
+            assert np.array_equal(cnt, planes_all.sum(axis=-1, dtype=np.int64)), f"step {t} counts"
+            fr = oracle_state(v_before, planes_all, t + 1, hl).fraction()
+            assert np.array_equal(frac.cpu().numpy(), fr.astype(np.float32)), f"step {t} fractions"
+            want = O.topk_select(fr.reshape(B * Hkv, C), cfg.n_evict).reshape(B, Hkv, cfg.n_evict)
+            assert np.array_equal(idx.cpu().numpy(), want), f"step {t} evictions"
+            v_exp = v_before.copy()
+            np.put_along_axis(v_exp, want, 0, axis=2)
+            assert np.array_equal(valid.cpu().numpy(), v_exp), f"step {t} validity after eviction"
+            say(f"  eviction at step {t}: all 64 rows ok")
     # 12 evictions of 64 slots per row
     assert int(valid.sum().item()) == B * Hkv * (C - (cfg.steps // cfg.evict_every) * cfg.n_evict)
+
+
+def test_c4_scissorhands_resume():
+    """Checkpoint and resume of the decode state: 400 steps, a copy of the state
+    buffers (validity, bit-planes, counts) through host memory into fresh
+    buffers, 400 more steps; the result is bit-identical to 800 uninterrupted
+    steps."""
+    cfg = configs.SCISSOR_DECODE
+    say("c4 resume")
+    B, Hkv, C, hl = cfg.B, cfg.Hkv, cfg.S, cfg.hist_len
+    L = lib()
+    kd = dev(synth.scissor_cache(0), "bf16")
+    qs = [dev(synth.scissor_query(0, t), "bf16") for t in range(cfg.steps)]
+    W = (C + 31) // 32
+
+    def fresh():
+        return (torch.ones((B, Hkv, C), dtype=torch.uint8, device="cuda"),
+                torch.zeros((hl, B * Hkv, W), dtype=torch.int32, device="cuda"),
+                torch.zeros((B, Hkv, C), dtype=torch.int16, device="cuda"))
+
+    def run(state, t0, t1):
+        valid, hist, counts = state
+        frac = torch.empty((B, Hkv, C), dtype=torch.float32, device="cuda")
+        for t in range(t0, t1):
+            probs = L.kvc_window_scores(qs[t], kd, valid=valid, reduce=L.KVC_REDUCE_GROUP, causal=False)
+            evict = (t + 1) % cfg.evict_every == 0
+            L.kvc_scissor_update(t, valid, hist, counts, probs=probs, frac_out=frac if evict else None)
+            if evict:
+                L.kvc_scissor_update(t, valid, hist, counts, evict_idx=L.kvc_topk_select(frac, cfg.n_evict))
+        torch.cuda.synchronize()
+
+    full = fresh()
+    run(full, 0, cfg.steps)
+    first = fresh()
+    half = cfg.steps // 2
+    run(first, 0, half)
+    snap = [x.cpu().clone() for x in first]
+    del first
+    resumed = tuple(x.cuda() for x in snap)
+    run(resumed, half, cfg.steps)
+    for a, b, name in zip(full, resumed, ("valid", "hist", "counts")):
+        assert torch.equal(a.cpu(), b.cpu()), name
 
 
 def test_c5_think_snapkv_128k_full():
@@ -261,9 +297,11 @@ def test_c2_then_think_full():
 
 def test_scissorhands_queue_decode_full_sampled():
     """The Scissorhands decode with insertion at its bench size (B 8, C 4096, a
-    protected prompt of 3840, queue 64, 800 steps) on all 64 rows; three sampled
-    rows followed in teacher-forced lockstep: every refill's queue, every
-    insertion, every step's probabilities and low bits."""
+    protected prompt of 3840, queue 64, 800 steps) on all 64 rows: every refill's
+    queue on every row equals the oracle's top-k of the fractions of the GPU's
+    state, each slot over its own observations (R14); three sampled rows
+    followed in teacher-forced lockstep at every step: every insertion, the
+    step's probabilities and low bits."""
     cfg = configs.SCISSOR_QUEUE
     say(cfg.name)
     B, H, Hkv, C, D, P, m, hist_len = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.keep, cfg.n_evict, cfg.hist_len
@@ -277,35 +315,36 @@ def test_scissorhands_queue_decode_full_sampled():
     valid[:, :, :P] = 1
     hist = torch.zeros((hist_len, B * Hkv, W), dtype=torch.int32, device="cuda")
     counts = torch.zeros((B, Hkv, C), dtype=torch.int16, device="cuda")
+    since = torch.zeros((B, Hkv, C), dtype=torch.int64, device="cuda")
     queue = torch.zeros((B, Hkv, m), dtype=torch.int32, device="cuda")
     sample = [(0, 0), (3, 5), (7, 7)]
     bgs = [b * Hkv + g for b, g in sample]
-    ins, qpos = P, m
+    ins, qpos, refills = P, m, 0
     for t in range(cfg.steps):
         k_new, v_new = dev(kn[t], "bf16"), dev(vn[t], "bf16")
         if ins < C:
-            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, fill_pos=ins)
+            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, since, t, fill_pos=ins)
             slots = np.full((B, Hkv), ins)
         else:
             if qpos == m:
-                v_st = valid.cpu().numpy()
-                cnt_st = counts.cpu().numpy().view(np.uint16).astype(np.int64)
-                L.kvc_scissor_refill(t - 1, valid, counts, hist_len, P, m, queue=queue)
+                v_st, since_st = valid.cpu().numpy(), since.cpu().numpy()
+                planes_st = unpack_all_planes(hist.cpu().numpy(), C).reshape(B, Hkv, C, hist_len)
+                L.kvc_scissor_refill(t - 1, valid, counts, hist_len, P, m, queue=queue, since=since)
                 torch.cuda.synchronize()
-                qg = queue.cpu().numpy()
-                for b, g in sample:
-                    frac = np.where(v_st[b, g].astype(bool), cnt_st[b, g] / min(t, hist_len), -np.inf)
-                    frac[:P] = -np.inf
-                    assert np.array_equal(qg[b, g], O.topk_select(frac[None], m)[0]), f"step {t} queue ({b},{g})"
-                qpos = 0
+                fr = oracle_state(v_st, planes_st, t, hist_len, since_st).fraction()
+                fr[..., :P] = -np.inf
+                want = O.topk_select(fr.reshape(B * Hkv, C), m).reshape(B, Hkv, m)
+                assert np.array_equal(queue.cpu().numpy(), want), f"step {t} queue"
+                qpos, refills = 0, refills + 1
             slots = queue.cpu().numpy()[:, :, qpos]
-            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, queue=queue, j=qpos)
+            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, since, t, queue=queue, j=qpos)
             qpos += 1
         ins += 1
         torch.cuda.synchronize()
         v_ins = valid.cpu().numpy()
         h_ins = hist[:, bgs, :].cpu().numpy()
         cnt_ins = counts.cpu().numpy().view(np.uint16)
+        since_ins = since.cpu().numpy()
         q_t = synth.scissor_query(0, t)
         probs = L.kvc_window_scores(dev(q_t, "bf16"), k_cache, valid=valid, reduce=L.KVC_REDUCE_GROUP, causal=False)
         L.kvc_scissor_update(t, valid, hist, counts, probs=probs)
@@ -318,22 +357,19 @@ def test_scissorhands_queue_decode_full_sampled():
             assert e >= P
             row_k = host_bits(k_cache[b, g, e])
             assert np.array_equal(row_k, kn[t][b, g]), f"step {t} inserted K ({b},{g})"
-            assert v_ins[b, g, e] == 1 and cnt_ins[b, g, e] == 0
-            assert not unpack_rows(h_ins[:, si, :], C)[e].any()
+            assert v_ins[b, g, e] == 1 and cnt_ins[b, g, e] == 0 and since_ins[b, g, e] == t
+            assert not unpack_planes(h_ins, si, C)[e].any()
             k64 = synth.stored_to_f64(host_bits(k_cache[b:b + 1, g:g + 1]), "bf16")
             ref_p = O.window_scores(q64[b:b + 1, g * G:(g + 1) * G], k64, valid=v_ins[b:b + 1, g:g + 1],
                                     reduce=O.REDUCE_GROUP, causal=False)[0, 0]
             check_scores(pg[b, g], ref_p, f"step {t} ({b},{g}) probs")
-            oc = O.ScissorhandsCache(1, 1, C, hist_len)
-            oc.valid[0, 0] = v_ins[b, g].astype(bool)
-            oc.attn_history[0, 0] = unpack_rows(h_ins[:, si, :], C)
-            oc.attn_counter = t
-            low = oc.update_attn_history(ref_p[None, None])[0, 0]
-            got = unpack_rows(h_now[:, si, :], C)[:, t % hist_len].astype(bool)
-            near = np.abs(ref_p * v_ins[b, g].sum() - 1.0) <= 1e-5
-            assert np.array_equal(got[~near], low[~near]), f"step {t} ({b},{g}) low bits"
+            st = oracle_state(v_ins[b, g], unpack_planes(h_ins, si, C), t, hist_len, since_ins[b, g])
+            low = st.record(ref_p[None, None])[0, 0]
+            got = unpack_planes(h_now, si, C)[:, t % hist_len]
+            assert low_bits_agree(got, low, ref_p, v_ins[b, g]), f"step {t} ({b},{g}) low bits"
         if t % 100 == 0:
             say(f"  step {t} ok")
+    assert refills > 0
     # the prompt is never replaced
     assert np.array_equal(host_bits(k_cache[:, :, :P].contiguous()), cache[:, :, :P])
 

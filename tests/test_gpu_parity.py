@@ -13,7 +13,7 @@ import torch
 
 from kv_cache_compression_window_amd import synth
 from oracle import kvc_oracle as O
-from tests.gpu_util import check_gather, check_kept, check_scores, dev, host_bits
+from tests.gpu_util import low_bits_agree, oracle_state, unpack_planes, check_gather, check_kept, check_scores, dev, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -300,13 +300,6 @@ def test_channel_scores(dt, D, S, w, G):
     assert torch.equal(cs, cs2)
 
 
-def unpack_planes(hist: np.ndarray, bg: int, C: int) -> np.ndarray:
-    """[C, hist_len] 0/1 matrix of the bit-planes of row bg."""
-    words = hist[:, bg, :].astype(np.uint32)  # [hist_len, W]
-    bits = np.unpackbits(words.view(np.uint8).reshape(words.shape[0], -1), bitorder="little", axis=1)
-    return bits[:, :C].T.astype(np.int8)
-
-
 def test_scissorhands_lockstep_small():
     """Teacher-forced lockstep: after every step the oracle adopts the GPU's state
     and checks the step's low bits (except within 1e-5 of the threshold), counts,
@@ -325,7 +318,6 @@ def test_scissorhands_lockstep_small():
     for t in range(steps):
         q = synth.random_problem(1000 + t, B, H, Hkv, 1, D, 1, dtype="bf16", with_v=False).q
         v_before = valid.cpu().numpy().copy()
-        hist_before = hist.cpu().numpy().copy()
         probs = L.kvc_window_scores(dev(q, "bf16"), kd, valid=valid, reduce=0, causal=False)
         evict = (t + 1) % every == 0
         L.kvc_scissor_update(t, valid, hist, counts, probs=probs, frac_out=frac if evict else None)
@@ -342,24 +334,16 @@ def test_scissorhands_lockstep_small():
         for b in range(B):
             for g in range(Hkv):
                 bg = b * Hkv + g
-                cache = O.ScissorhandsCache(1, 1, C, hist_len)
-                cache.valid[0, 0] = v_before[b, g].astype(bool)
-                cache.attn_history[0, 0] = unpack_planes(hist_before, bg, C)
-                cache.attn_counter = t
-                low = cache.update_attn_history(ref_p[b, g][None, None])[0, 0]
-                got = unpack_planes(hist_now, bg, C)[:, t % hist_len].astype(bool)
-                n_valid = v_before[b, g].sum()
-                near = np.abs(ref_p[b, g] * n_valid - 1.0) <= 1e-5
-                assert np.array_equal(got[~near], low[~near]), f"step {t} bg {bg} low bits"
+                planes = unpack_planes(hist_now, bg, C)
+                low = oracle_state(v_before[b, g], planes, t, hist_len).record(ref_p[b, g][None, None])[0, 0]
+                got = planes[:, t % hist_len]
+                assert low_bits_agree(got, low, ref_p[b, g], v_before[b, g]), f"step {t} bg {bg} low bits"
                 # the GPU's counts are the popcount of its own planes
-                assert np.array_equal(cnt[b, g], unpack_planes(hist_now, bg, C).sum(axis=1))
+                assert np.array_equal(cnt[b, g], planes.sum(axis=1))
                 if evict:
-                    cache.attn_history[0, 0] = unpack_planes(hist_now, bg, C)
-                    fr = cache.low_fraction()[0, 0]
+                    fr = oracle_state(v_before[b, g], planes, t + 1, hist_len).fraction()[0, 0]
                     fg = frac.cpu().numpy()[b, g]
-                    assert np.array_equal(np.isinf(fg), np.isinf(fr))
-                    fin = np.isfinite(fr)
-                    assert np.allclose(fg[fin], fr[fin], rtol=1e-6, atol=0)
+                    assert np.array_equal(fg, fr.astype(np.float32)), f"step {t} bg {bg} fractions"
                     want = O.topk_select(fr[None], n_ev)[0]
                     assert np.array_equal(idx.cpu().numpy()[b, g], want), f"step {t} evictions"
                     v_exp = v_before[b, g].copy()
@@ -412,26 +396,18 @@ def test_scissorhands_sampled_lockstep_small():
                 bg = b * Hkv + g
                 planes_now = unpack_planes(hist_now, bg, C)
                 assert np.array_equal(cnt[b, g], planes_now.sum(axis=1))
-                cache = O.ScissorhandsCache(1, 1, C, hist_len)
-                cache.valid[0, 0] = v_before[b, g].astype(bool)
                 if record:
-                    cache.attn_history[0, 0] = unpack_planes(hist_before, bg, C)
-                    cache.attn_counter = n_rec - 1
-                    low = cache.update_attn_history(ref_p[b, g][None, None])[0, 0]
-                    got = planes_now[:, (n_rec - 1) % hist_len].astype(bool)
-                    near = np.abs(ref_p[b, g] * v_before[b, g].sum() - 1.0) <= 1e-5
-                    assert np.array_equal(got[~near], low[~near]), f"step {t} bg {bg} low bits"
+                    st = oracle_state(v_before[b, g], unpack_planes(hist_before, bg, C), n_rec - 1, hist_len)
+                    low = st.record(ref_p[b, g][None, None])[0, 0]
+                    got = planes_now[:, (n_rec - 1) % hist_len]
+                    assert low_bits_agree(got, low, ref_p[b, g], v_before[b, g]), f"step {t} bg {bg} low bits"
                 else:
                     # nothing recorded: the history is unchanged
                     assert np.array_equal(hist_now[:, bg], hist_before[:, bg])
                 if evict:
-                    cache.attn_history[0, 0] = planes_now
-                    cache.attn_counter = n_rec
-                    fr = cache.low_fraction()[0, 0]
+                    fr = oracle_state(v_before[b, g], planes_now, n_rec, hist_len).fraction()[0, 0]
                     fg = frac.cpu().numpy()[b, g]
-                    assert np.array_equal(np.isinf(fg), np.isinf(fr))
-                    fin = np.isfinite(fr)
-                    assert np.allclose(fg[fin], fr[fin], rtol=1e-6, atol=0)
+                    assert np.array_equal(fg, fr.astype(np.float32)), f"step {t} bg {bg} fractions"
                     want = O.topk_select(fr[None], n_ev)[0]
                     assert np.array_equal(idx.cpu().numpy()[b, g], want), f"step {t} evictions"
                     v_exp = v_before[b, g].copy()
@@ -443,12 +419,12 @@ def test_scissorhands_queue_lockstep_small():
     """R28-R30 on the GPU: the prompt fills the first P slots, the next C - P
     steps fill the rest, then every step takes its slot from the eviction queue,
     refilled every m steps.  Teacher-forced: every refill's queue equals the
-    oracle's top-k on the GPU's counts, every insertion leaves the slot with the
-    new K/V rows, valid, a zero count and no history bit, and every step's low
-    bits match the oracle's on the GPU's state."""
+    oracle's top-k of the fractions of the GPU's state, each slot over its own
+    observations (R14); every insertion leaves the slot with the new K/V rows,
+    valid, a zero count, no history bit and its observation start; every step's
+    low bits match the oracle's on the GPU's state."""
     say("scissorhands queue lockstep small")
     B, H, Hkv, C, D, P, hist_len, m, steps = 2, 8, 2, 256, 128, 160, 6, 8, 140
-    G = H // Hkv
     L = lib()
     prob = synth.random_problem(5, B, Hkv, Hkv, C, D, 1, dtype="bf16", heavy_frac=0.05)
     k_cache, v_cache = dev(prob.k, "bf16").clone(), dev(prob.v, "bf16").clone()
@@ -457,28 +433,38 @@ def test_scissorhands_queue_lockstep_small():
     W = (C + 31) // 32
     hist = torch.zeros((hist_len, B * Hkv, W), dtype=torch.int32, device="cuda")
     counts = torch.zeros((B, Hkv, C), dtype=torch.int16, device="cuda")
+    since = torch.zeros((B, Hkv, C), dtype=torch.int64, device="cuda")
     queue = torch.zeros((B, Hkv, m), dtype=torch.int32, device="cuda")
-    insertions, qpos = P, m
+    insertions, qpos, n_differ = P, m, 0
     for t in range(steps):
         new = synth.random_problem(3000 + t, B, Hkv, Hkv, 1, D, 1, dtype="bf16")
         q = synth.random_problem(4000 + t, B, H, Hkv, 1, D, 1, dtype="bf16", with_v=False).q
         k_new, v_new = dev(new.k[:, :, 0], "bf16"), dev(new.v[:, :, 0], "bf16")
         if insertions < C:
-            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, fill_pos=insertions)
+            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, since, t, fill_pos=insertions)
             slots = np.full((B, Hkv), insertions)
         else:
             if qpos == m:
-                v_st = valid.cpu().numpy()
+                v_st, since_st, hist_st = valid.cpu().numpy(), since.cpu().numpy(), hist.cpu().numpy()
                 cnt_st = counts.cpu().numpy().view(np.uint16).astype(np.int64)
-                L.kvc_scissor_refill(t - 1, valid, counts, hist_len, P, m, queue=queue)
+                L.kvc_scissor_refill(t - 1, valid, counts, hist_len, P, m, queue=queue, since=since)
                 torch.cuda.synchronize()
-                frac = np.where(v_st.astype(bool), cnt_st / min(t, hist_len), -np.inf)
-                frac[..., :P] = -np.inf
-                want = O.topk_select(frac.reshape(B * Hkv, C), m).reshape(B, Hkv, m)
-                assert np.array_equal(queue.cpu().numpy(), want), f"step {t} queue"
+                qg = queue.cpu().numpy()
+                for b in range(B):
+                    for g in range(Hkv):
+                        bg = b * Hkv + g
+                        st = oracle_state(v_st[b, g], unpack_planes(hist_st, bg, C), t, hist_len, since_st[b, g])
+                        fr = st.fraction()[0, 0]
+                        fr[:P] = -np.inf
+                        want = O.topk_select(fr[None], m)[0]
+                        assert np.array_equal(qg[b, g], want), f"step {t} queue ({b},{g})"
+                        # the per-slot denominator changes the choice somewhere in this run
+                        glob = np.where(v_st[b, g].astype(bool), cnt_st[b, g] / min(t, hist_len), -np.inf)
+                        glob[:P] = -np.inf
+                        n_differ += int(not np.array_equal(O.topk_select(glob[None], m)[0], want))
                 qpos = 0
             slots = queue.cpu().numpy()[:, :, qpos]
-            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, queue=queue, j=qpos)
+            L.kvc_scissor_insert(k_new, v_new, k_cache, v_cache, valid, hist, counts, since, t, queue=queue, j=qpos)
             qpos += 1
         insertions += 1
         torch.cuda.synchronize()
@@ -486,6 +472,7 @@ def test_scissorhands_queue_lockstep_small():
         hist_ins = hist.cpu().numpy()
         cnt_ins = counts.cpu().numpy().view(np.uint16)
         v_ins = valid.cpu().numpy()
+        since_ins = since.cpu().numpy()
         kc_bits = host_bits(k_cache)
         vc_bits = host_bits(v_cache)
         for b in range(B):
@@ -493,7 +480,7 @@ def test_scissorhands_queue_lockstep_small():
                 e = int(slots[b, g])
                 assert e >= P
                 assert np.array_equal(kc_bits[b, g, e], new.k[b, g, 0]) and np.array_equal(vc_bits[b, g, e], new.v[b, g, 0])
-                assert v_ins[b, g, e] == 1 and cnt_ins[b, g, e] == 0
+                assert v_ins[b, g, e] == 1 and cnt_ins[b, g, e] == 0 and since_ins[b, g, e] == t
                 assert not unpack_planes(hist_ins, b * Hkv + g, C)[e].any()
         assert np.array_equal(kc_bits[:, :, :P], prob.k[:, :, :P])  # the prompt is never replaced
         # the step's attention with the new token in the cache, and its record
@@ -507,15 +494,12 @@ def test_scissorhands_queue_lockstep_small():
         for b in range(B):
             for g in range(Hkv):
                 bg = b * Hkv + g
-                cache = O.ScissorhandsCache(1, 1, C, hist_len)
-                cache.valid[0, 0] = v_ins[b, g].astype(bool)
-                cache.attn_history[0, 0] = unpack_planes(hist_ins, bg, C)
-                cache.attn_counter = t
-                low = cache.update_attn_history(ref_p[b, g][None, None])[0, 0]
-                got = unpack_planes(hist_now, bg, C)[:, t % hist_len].astype(bool)
-                near = np.abs(ref_p[b, g] * v_ins[b, g].sum() - 1.0) <= 1e-5
-                assert np.array_equal(got[~near], low[~near]), f"step {t} bg {bg} low bits"
+                st = oracle_state(v_ins[b, g], unpack_planes(hist_ins, bg, C), t, hist_len, since_ins[b, g])
+                low = st.record(ref_p[b, g][None, None])[0, 0]
+                got = unpack_planes(hist_now, bg, C)[:, t % hist_len]
+                assert low_bits_agree(got, low, ref_p[b, g], v_ins[b, g]), f"step {t} bg {bg} low bits"
     assert insertions - P == steps and qpos > 0
+    assert n_differ > 0, "no refill where the per-slot and the global denominators disagree"
 
 
 def O_bf16(bits):

@@ -364,42 +364,73 @@ def test_snapkv_then_think_channel_scores_over_kept_keys():
 
 def test_golden_scissorhands_steps():
     c = _golden("scissorhands_steps.json")
-    cache = O.ScissorhandsCache(1, 1, 4, c["history"])
+    st = O.LowAttentionState(1, 1, 4, c["history"])
     for t, attn in enumerate(c["attn"]):
-        low = cache.update_attn_history(np.array(attn, dtype=np.float64)[None, None, :])
+        low = st.record(np.array(attn, dtype=np.float64)[None, None, :])
         assert low[0, 0].astype(int).tolist() == c["low"][t]
-        assert cache.low_counts()[0, 0].tolist() == c["counts"][t]
-        ev = cache.evict(c["n_evict"]) if (t + 1) % c["evict_every"] == 0 else None
+        assert st.counts()[0, 0].tolist() == c["counts"][t]
+        ev = st.evict(c["n_evict"]) if (t + 1) % c["evict_every"] == 0 else None
         assert (None if ev is None else ev[0, 0].tolist()) == c["evicted"][t]
-        assert cache.valid[0, 0].astype(int).tolist() == c["valid_after"][t]
+        assert st.valid[0, 0].astype(int).tolist() == c["valid_after"][t]
+
+
+def test_golden_scissorhands_insertion():
+    """R14 with insertion, hand-worked: a slot's fraction divides its low count
+    by its own observations (the recordings since its token arrived, capped by
+    the window), not by the number of recordings of the layer."""
+    c = _golden("scissorhands_insertion.json")
+    st = O.LowAttentionState(1, 1, c["C"], c["history"])
+    for i, ev in enumerate(c["events"]):
+        if "record" in ev:
+            low = st.record(np.array(ev["record"], dtype=np.float64)[None, None, :])
+            assert low[0, 0].astype(int).tolist() == ev["low"], i
+        else:
+            st.occupy(np.array([[ev["insert"]]]))
+        cnt, obs = st.counts()[0, 0], st.observations()[0, 0]
+        assert cnt.tolist() == ev["counts"], i
+        assert obs.tolist() == ev["observations"], i
+        want = [a / b if b else 0.0 for a, b in zip(ev["counts"], ev["observations"])]
+        assert st.fraction()[0, 0].tolist() == want, i
+        assert O.topk_select(st.fraction()[0], 1)[0, 0] == ev["evict_one"], i
+    # the same recordings divided by min(n, history) for every slot would pick another slot
+    st2 = O.LowAttentionState(1, 1, c["C"], c["history"])
+    for ev in c["events"][:5]:
+        if "record" in ev:
+            st2.record(np.array(ev["record"], dtype=np.float64)[None, None, :])
+        else:
+            st2.occupy(np.array([[ev["insert"]]]))
+    glob = st2.counts()[0] / min(st2.n, c["history"])
+    assert O.topk_select(glob, 1)[0, 0] == c["global_denominator_would_evict_after_event_4"]
+    assert O.topk_select(st2.fraction()[0], 1)[0, 0] != c["global_denominator_would_evict_after_event_4"]
 
 
 @pytest.mark.parametrize("hist", [1, 3, 7])
-def test_scissorhands_ring_equals_windowed_sum(hist):
-    """P6/P7: the circular history count equals the sum of the full
-    [steps x slots] low matrix over the last min(t+1, hist) steps, and stays
-    within [0, min(t+1, hist)]."""
+def test_scissorhands_counts_equal_windowed_sum(hist):
+    """P6/P7: the count equals the sum of the full [steps x slots] low matrix
+    over the last min(t+1, hist) steps, within [0, min(t+1, hist)], and every
+    valid slot has min(t+1, hist) observations (no insertion)."""
     B, Hkv, C, steps = 2, 2, 11, 25
     rs = np.random.default_rng(hist)
-    cache = O.ScissorhandsCache(B, Hkv, C, hist)
+    st = O.LowAttentionState(B, Hkv, C, hist)
     lows = []
     for t in range(steps):
         attn = rs.dirichlet(np.ones(C) * 0.7, size=(B, Hkv))
-        attn = np.where(cache.valid, attn, 0.0)
-        lows.append(cache.update_attn_history(attn).astype(np.int64))
+        attn = np.where(st.valid, attn, 0.0)
+        lows.append(st.record(attn).astype(np.int64))
         # brute force: recompute the low test from its definition
         for b in range(B):
             for g in range(Hkv):
-                n = int(cache.valid[b, g].sum())
+                n = int(st.valid[b, g].sum())
                 for c in range(C):
-                    want = bool(cache.valid[b, g, c]) and attn[b, g, c] < 1.0 / n
+                    want = bool(st.valid[b, g, c]) and attn[b, g, c] < 1.0 / n
                     assert bool(lows[-1][b, g, c]) == want
         window = np.stack(lows[max(0, t + 1 - hist):t + 1]).sum(axis=0)
-        counts = cache.low_counts()
+        counts = st.counts()
         assert np.array_equal(counts, window)
         assert counts.min() >= 0 and counts.max() <= min(t + 1, hist)
+        assert (st.observations() == min(t + 1, hist)).all()
         if t % 6 == 5:
-            cache.evict(1)
+            st.evict(1)
 
 
 @pytest.mark.parametrize("M", [1, 3])
@@ -411,12 +442,12 @@ def test_scissorhands_sampled_recording(M):
     B, H, Hkv, C, D, hist, steps, every, n_ev = 1, 4, 2, 40, 8, 4, 20, 6, 2
     rs = np.random.default_rng(11 + M)
     k = rs.standard_normal((B, Hkv, C, D))
-    cache = O.ScissorhandsCache(B, Hkv, C, hist)
+    st = O.LowAttentionState(B, Hkv, C, hist)
     recorded = []
     for t in range(steps):
         q = rs.standard_normal((B, H, 1, D))
-        valid_before = cache.valid.copy()
-        probs, low, _ = O.scissorhands_step(cache, q, k, t, evict_every=every, n_evict=n_ev, record_every=M)
+        valid_before = st.valid.copy()
+        probs, low, _ = O.scissorhands_step(st, q, k, t, evict_every=every, n_evict=n_ev, record_every=M)
         if t % M == 0:
             ref = O.window_scores(q, k, valid=valid_before, reduce=O.REDUCE_GROUP, causal=False)
             assert np.array_equal(probs, ref)
@@ -424,59 +455,62 @@ def test_scissorhands_sampled_recording(M):
         else:
             assert probs is None and low is None
         n_rec = len(recorded)
-        assert cache.attn_counter == n_rec
+        assert st.n == n_rec
         window = np.stack(recorded[max(0, n_rec - hist):]).sum(axis=0)
-        assert np.array_equal(cache.low_counts(), window)
-        want_fr = np.where(cache.valid, window / min(n_rec, hist), -np.inf)
-        assert np.array_equal(cache.low_fraction(), want_fr)
+        assert np.array_equal(st.counts(), window)
+        want_fr = np.where(st.valid, window / min(n_rec, hist), -np.inf)
+        assert np.array_equal(st.fraction(), want_fr)
 
 
-@pytest.mark.parametrize("global_tokens", [-1, 3])
-def test_scissorhands_queue_cache(global_tokens):
+@pytest.mark.parametrize("protect", [-1, 3])
+def test_scissorhands_queue_cache(protect):
     """R28-R30: the prompt fills the first P slots and the next C - P steps fill
     the rest in order; after that every step replaces exactly one slot; the
-    drop_amount slots replaced after a refill are the bulk eviction set of O5
-    on the state at the refill (the pinned top-k rule); protected slots keep
-    their prompt keys; a replaced slot's history holds only the bits recorded
-    since its insertion."""
+    drop_amount slots replaced after a refill are the largest fractions of the
+    state at the refill, each slot's count and observations taken by brute
+    force from the full low matrix over the recordings since its token arrived
+    (at most the last `hist`); protected slots keep their prompt keys."""
     B, H, Hkv, C, D, P, hist, m, steps = 1, 4, 2, 24, 8, 10, 5, 4, 60
     rs = np.random.default_rng(21)
-    cache = O.ScissorhandsQueueCache(B, Hkv, C, D, hist, m, global_tokens)
+    cache = O.ScissorhandsQueue(B, Hkv, C, D, hist, m, protect)
     kp, vp = rs.standard_normal((B, Hkv, P, D)), rs.standard_normal((B, Hkv, P, D))
     cache.prefill(kp, vp)
-    protect = P if global_tokens == -1 else global_tokens
-    assert cache.global_tokens == protect
-    since = {}  # (b, g, slot) -> step of its last insertion
+    n_prot = P if protect < 0 else protect
+    assert cache.n_protect == n_prot
+    arrived = np.zeros((B, Hkv, C), dtype=np.int64)  # recordings made before each slot's token arrived
+    lows = []  # every step's low bits, in order
     pending = None
     for t in range(steps):
-        if cache.insertions >= C and cache.queue_pos >= cache.queue.shape[2]:
-            # the refill about to happen takes O5's bulk eviction set of this state
-            ref = O.ScissorhandsCache(B, Hkv, C, hist)
-            ref.valid = cache.valid.copy()
-            ref.attn_history = cache.attn_history.copy()
-            ref.attn_counter = cache.attn_counter
-            frac = ref.low_fraction()
-            frac[..., :protect] = -np.inf
+        if cache.filled >= C and cache.queue_pos >= cache.queue.shape[2]:
+            # brute force of the refill about to happen
+            L = np.stack(lows)  # [n, B, Hkv, C]
+            n = L.shape[0]
+            frac = np.full((B, Hkv, C), -np.inf)
+            for b in range(B):
+                for g in range(Hkv):
+                    for e in range(n_prot, C):
+                        first = max(int(arrived[b, g, e]), n - hist)
+                        obs = n - first
+                        frac[b, g, e] = L[first:, b, g, e].sum() / obs if obs > 0 else 0.0
             pending = O.topk_select(frac.reshape(B * Hkv, C), m).reshape(B, Hkv, m)
         kn, vn = rs.standard_normal((B, Hkv, D)), rs.standard_normal((B, Hkv, D))
         q = rs.standard_normal((B, H, 1, D))
         slots, probs, low = O.scissorhands_queue_step(cache, q, kn, vn)
+        lows.append(low.astype(np.int64))
         if t < C - P:
             assert (slots == P + t).all()
         else:
             j = (t - (C - P)) % m
             assert np.array_equal(slots, pending[:, :, j])
-            assert (slots >= protect).all()
+            assert (slots >= n_prot).all()
         for b in range(B):
             for g in range(Hkv):
                 e = int(slots[b, g])
                 assert np.array_equal(cache.k[b, g, e], kn[b, g])
-                since[(b, g, e)] = t
-        assert np.array_equal(cache.k[:, :, :protect], kp[:, :, :protect])
+                arrived[b, g, e] = t
+        assert np.array_equal(cache.k[:, :, :n_prot], kp[:, :, :n_prot])
         assert cache.valid.all() == (t >= C - P - 1)
-        # a slot's count covers only the steps since its insertion
-        for (b, g, e), t0 in since.items():
-            assert cache.low_counts()[b, g, e] <= min(t - t0 + 1, hist)
+        assert np.array_equal(cache.since, arrived)
 
 
 def test_scissorhands_equal_keys_never_low_and_dominant_key():
@@ -485,7 +519,7 @@ def test_scissorhands_equal_keys_never_low_and_dominant_key():
     count is min(t+1, history), and eviction takes the lowest indices."""
     B, H, Hkv, C, D, hist = 1, 2, 1, 70, 4, 5
     k_eq = np.ones((B, Hkv, C, D))
-    cache = O.ScissorhandsCache(B, Hkv, C, hist)
+    cache = O.LowAttentionState(B, Hkv, C, hist)
     rs = np.random.default_rng(5)
     for t in range(8):
         q = rs.standard_normal((B, H, 1, D))
@@ -495,11 +529,11 @@ def test_scissorhands_equal_keys_never_low_and_dominant_key():
     k_dom[0, 0, 65] = [40.0, 0, 0, 0]
     q = np.zeros((B, H, 1, D))
     q[..., 0] = 1.0
-    cache = O.ScissorhandsCache(B, Hkv, C, hist)
+    cache = O.LowAttentionState(B, Hkv, C, hist)
     for t in range(8):
         _, low, ev = O.scissorhands_step(cache, q, k_dom, t, evict_every=4, n_evict=3)
         assert not low[0, 0, 65]
-        counts = cache.low_counts()[0, 0]
+        counts = cache.counts()[0, 0]
         v = cache.valid[0, 0]
         if ev is not None:
             assert ev[0, 0].tolist() == [3 * (t // 4), 3 * (t // 4) + 1, 3 * (t // 4) + 2]
