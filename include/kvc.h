@@ -118,6 +118,28 @@ kvc_status kvc_window_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_wi
                              size_t* ws_bytes, hipStream_t stream);
 
 /*
+ * kvc_window_scores_noalloc — kvc_window_scores without a workspace argument
+ * and without any device allocation.
+ *
+ * For callers that cannot allocate device memory: code under HIP stream
+ * capture, serving loops that forbid allocation, harnesses that disallow it.
+ * Same arguments, definition, results and errors as kvc_window_scores, minus
+ * ws/ws_bytes.  Its scratch (the per-chunk row statistics, the log-normalisers
+ * and, for G*w <= 16, the stored logits) lives in one fixed device array of
+ * KVC_NOALLOC_SCRATCH_BYTES per GPU, which the library holds from the first
+ * call on that GPU until the process ends.  A shape whose kvc_window_scores
+ * workspace exceeds that size returns KVC_ERR_WORKSPACE and enqueues nothing.
+ * The scratch needs no initialisation.  Every call on one GPU shares that GPU's
+ * array: two calls that may overlap on the same GPU (different streams without
+ * ordering between them, or different host threads) race and give undefined
+ * scores.  Calls on one stream are ordered and safe.
+ */
+#define KVC_NOALLOC_SCRATCH_BYTES (32u << 20)
+kvc_status kvc_window_scores_noalloc(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
+                                     const uint8_t* valid, const int32_t* chan_idx, int32_t d_keep,
+                                     kvc_reduce reduce, int32_t causal, float* scores, hipStream_t stream);
+
+/*
  * kvc_scissor_update — Scissorhands low-attention history (record and evict).
  *
  * [COLD] cache.py hunks: a slot counts as unimportant at a step when its

@@ -18,6 +18,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvc.so"
 
 KVC_F32, KVC_BF16 = 0, 1
 KVC_REDUCE_GROUP, KVC_REDUCE_ALL_HEADS = 0, 1
+KVC_ERR_WORKSPACE = 5
+KVC_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/kvc.h
 
 STATUS_NAMES = {0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_ALIGN",
                 5: "KVC_ERR_WORKSPACE", 6: "KVC_ERR_UNSUPPORTED", 7: "KVC_ERR_HIP"}
@@ -25,7 +27,8 @@ STATUS_NAMES = {0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_
 # every symbol include/kvc.h declares
 EXPORTS = ["kvc_window_scores", "kvc_scissor_update", "kvc_channel_scores", "kvc_topk_select",
            "kvc_gather_compact", "kvc_gather_compress", "kvc_channel_expand", "kvc_query_channels",
-           "kvc_scissor_refill", "kvc_scissor_insert", "kvc_status_string", "kvc_abi_version"]
+           "kvc_scissor_refill", "kvc_scissor_insert", "kvc_window_scores_noalloc", "kvc_status_string",
+           "kvc_abi_version"]
 
 
 class KvcShape(ctypes.Structure):
@@ -47,6 +50,7 @@ def _load():
     SH = ctypes.POINTER(KvcShape)
     sig = {
         "kvc_window_scores": [SH, I32, P, P, P, P, I32, I32, I32, P, P, SZP, P],
+        "kvc_window_scores_noalloc": [SH, I32, P, P, P, P, I32, I32, I32, P, P],
         "kvc_scissor_update": [I32, I32, I32, I32, I64, P, P, P, P, P, P, P, I32, P],
         "kvc_channel_scores": [SH, I32, P, P, P, P, SZP, P],
         "kvc_topk_select": [P, I32, I32, I32, I32, P, P, SZP, P],
@@ -146,6 +150,24 @@ def kvc_window_scores(q, k, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, 
     _check("kvc_window_scores", LIB.kvc_window_scores(ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid),
                                                       _ptr(chan_idx), d_keep, reduce, int(causal), _ptr(scores),
                                                       _ptr(ws), ctypes.byref(n), _stream(stream)))
+    return scores
+
+
+def kvc_window_scores_noalloc(q, k, scores, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, causal=True,
+                              stream=None):
+    """kvc_window_scores into the caller's scores [B,Hkv,S] float32, with the
+    library's fixed per-GPU scratch instead of a workspace (nothing allocated)."""
+    _need(q, "q_win", 4)
+    _need(k, "k", 4)
+    _need(scores, "scores", 3)
+    sh = _shape(q, k)
+    d_keep = 0
+    if chan_idx is not None:
+        _need(chan_idx, "chan_idx", 3)
+        d_keep = chan_idx.shape[2]
+    _check("kvc_window_scores_noalloc",
+           LIB.kvc_window_scores_noalloc(ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid),
+                                         _ptr(chan_idx), d_keep, reduce, int(causal), _ptr(scores), _stream(stream)))
     return scores
 
 

@@ -43,24 +43,27 @@ const char* kvc_status_string(kvc_status s) {
 
 int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
 
-kvc_status kvc_window_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
-                             const uint8_t* valid, const int32_t* chan_idx, int32_t d_keep, kvc_reduce reduce,
-                             int32_t causal, float* scores, void* ws, size_t* ws_bytes, hipStream_t stream) {
-  if (!sh || !ws_bytes) return KVC_ERR_NULL;
+}  // extern "C"
+
+static_assert(kvc::kNoAllocScratchBytes == (size_t)KVC_NOALLOC_SCRATCH_BYTES, "scratch size of the header");
+
+namespace {
+
+// Validation and plan of kvc_window_scores (everything but the workspace).
+kvc_status window_scores_check(const kvc_shape* sh, kvc_dtype dt, kvc_reduce reduce, const int32_t* chan_idx,
+                               int32_t d_keep, kvc::WsPlan* plan) {
   if (dt != KVC_F32 && dt != KVC_BF16) return KVC_ERR_DTYPE;
   if (reduce != KVC_REDUCE_GROUP && reduce != KVC_REDUCE_ALL_HEADS) return KVC_ERR_DTYPE;
   kvc_status st = check_shape(sh, true);
   if (st != KVC_OK) return st;
   if (chan_idx && (d_keep < 1 || d_keep > sh->D)) return KVC_ERR_SHAPE;
-  kvc::WsPlan plan;
-  if (!kvc::ws_make_plan(sh->B, sh->H, sh->Hkv, sh->S, sh->w, &plan)) return KVC_ERR_UNSUPPORTED;
-  if (!ws) {
-    *ws_bytes = plan.bytes;
-    return KVC_OK;
-  }
-  if (*ws_bytes < plan.bytes) return KVC_ERR_WORKSPACE;
-  if (!q_win || !k || !scores) return KVC_ERR_NULL;
-  if (misaligned16(q_win) || misaligned16(k) || misaligned4(scores) || misaligned16(ws)) return KVC_ERR_ALIGN;
+  if (!kvc::ws_make_plan(sh->B, sh->H, sh->Hkv, sh->S, sh->w, plan)) return KVC_ERR_UNSUPPORTED;
+  return KVC_OK;
+}
+
+kvc_status window_scores_run(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
+                             const uint8_t* valid, const int32_t* chan_idx, int32_t d_keep, kvc_reduce reduce,
+                             int32_t causal, float* scores, void* ws, const kvc::WsPlan& plan, hipStream_t stream) {
   kvc::WsArgs a;
   a.bf16 = dt == KVC_BF16;
   a.B = sh->B;
@@ -79,6 +82,42 @@ kvc_status kvc_window_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_wi
   a.scores = scores;
   a.ws = ws;
   return hip_status(kvc::launch_window_scores(a, plan, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_window_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
+                             const uint8_t* valid, const int32_t* chan_idx, int32_t d_keep, kvc_reduce reduce,
+                             int32_t causal, float* scores, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  if (!sh || !ws_bytes) return KVC_ERR_NULL;
+  kvc::WsPlan plan;
+  const kvc_status st = window_scores_check(sh, dt, reduce, chan_idx, d_keep, &plan);
+  if (st != KVC_OK) return st;
+  if (!ws) {
+    *ws_bytes = plan.bytes;
+    return KVC_OK;
+  }
+  if (*ws_bytes < plan.bytes) return KVC_ERR_WORKSPACE;
+  if (!q_win || !k || !scores) return KVC_ERR_NULL;
+  if (misaligned16(q_win) || misaligned16(k) || misaligned4(scores) || misaligned16(ws)) return KVC_ERR_ALIGN;
+  return window_scores_run(sh, dt, q_win, k, valid, chan_idx, d_keep, reduce, causal, scores, ws, plan, stream);
+}
+
+kvc_status kvc_window_scores_noalloc(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
+                                     const uint8_t* valid, const int32_t* chan_idx, int32_t d_keep,
+                                     kvc_reduce reduce, int32_t causal, float* scores, hipStream_t stream) {
+  if (!sh) return KVC_ERR_NULL;
+  kvc::WsPlan plan;
+  const kvc_status st = window_scores_check(sh, dt, reduce, chan_idx, d_keep, &plan);
+  if (st != KVC_OK) return st;
+  if (plan.bytes > kvc::kNoAllocScratchBytes) return KVC_ERR_WORKSPACE;
+  if (!q_win || !k || !scores) return KVC_ERR_NULL;
+  if (misaligned16(q_win) || misaligned16(k) || misaligned4(scores)) return KVC_ERR_ALIGN;
+  void* ws = nullptr;
+  if (kvc::noalloc_scratch(&ws) != hipSuccess) return KVC_ERR_HIP;
+  return window_scores_run(sh, dt, q_win, k, valid, chan_idx, d_keep, reduce, causal, scores, ws, plan, stream);
 }
 
 kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_len, int64_t step,

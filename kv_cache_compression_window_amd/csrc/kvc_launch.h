@@ -23,6 +23,10 @@ struct WsArgs {
 };
 hipError_t launch_window_scores(const WsArgs& a, const WsPlan& plan, hipStream_t st);
 
+// Device address of the current device's fixed scratch (kNoAllocScratchBytes),
+// looked up once per device (noalloc.hip).
+hipError_t noalloc_scratch(void** ptr);
+
 struct CsArgs {
   int bf16;
   int B, H, Hkv, S, D, w;

@@ -32,6 +32,8 @@ struct WsPlan {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kMaxRows = 1024;  // G*w limit per KV head
+// Size of the fixed device scratch of kvc_window_scores_noalloc (one copy per GPU).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
 constexpr int kMergeLanes = 8;  // lanes of the merge kernel per (b, g, row)
 
 inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, WsPlan* p) {

@@ -86,6 +86,31 @@ def test_window_scores_validation(lib):
     assert lib.window_scores_ws_bytes(1, 32, 8, 32768, 128, 64) > 0
 
 
+def test_window_scores_noalloc_validation(lib):
+    """The allocation-free variant validates like kvc_window_scores and rejects a
+    shape whose workspace exceeds the fixed scratch, before any launch."""
+    f = lib.LIB.kvc_window_scores_noalloc
+    S = lib.KvcShape
+
+    def call(sh, dt=1, q=FAKE, k=FAKE, reduce=0, scores=FAKE):
+        return f(ctypes.byref(sh) if sh is not None else None, dt, q, k, None, None, 0, reduce, 1, scores, None)
+    ok = S(1, 32, 8, 4096, 128, 64)
+    assert call(None) == 1
+    assert call(ok, dt=5) == 3
+    assert call(ok, reduce=2) == 3
+    assert call(S(1, 30, 8, 4096, 128, 64)) == 2
+    assert call(S(1, 32, 8, 4096, 96, 64)) == 6
+    assert call(ok, q=None) == 1
+    assert call(ok, scores=None) == 1
+    assert call(ok, k=ODD) == 4
+    big = S(64, 32, 8, 8192, 128, 1)  # stored logits of 64 MiB
+    assert lib.window_scores_ws_bytes(64, 32, 8, 8192, 128, 1) > lib.KVC_NOALLOC_SCRATCH_BYTES
+    assert call(big) == 5
+    # the header's size and the binding's agree
+    assert f"#define KVC_NOALLOC_SCRATCH_BYTES (32u << 20)" in open(HEADER).read()
+    assert lib.KVC_NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
 def test_window_scores_workspace_grows_with_rows(lib):
     small = lib.window_scores_ws_bytes(1, 4, 2, 512, 64, 1)     # stored-logits path
     big = lib.window_scores_ws_bytes(1, 32, 8, 32768, 128, 64)  # two-pass path
