@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV tokens scored+pruned/s per layer (32k ctx, GQA 32/8) + % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK = 2.5e15  # dense bf16 MFMA, FLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_window_scores_snapkv_32k.json")
 SCORE_SOURCES = ["window_scores.hip", "kvc_device.h", "kvc_plan.h"]
 WORKLOADS = ["snapkv_32k", "tova_tiny", "tova_batched", "scissor_decode", "think_128k", "think_128k_kc",
@@ -62,6 +63,8 @@ def parse():
                     help="passes over the layers, each timed as one run of back-to-back calls of the dominant kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work budget of the oracle baseline")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the read-ceiling and exp-rate measurements")
+    ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph-captured variant")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
     a = ap.parse_args()
@@ -89,6 +92,48 @@ def timed_oracle(fn, budget_s):
         el = time.perf_counter() - t0
         if el >= budget_s:
             return n, el
+
+
+def measure_ceilings(c, reps: int = 5) -> dict:
+    """The box's own ceilings, measured in this run with libkvc_bench.so: a plain
+    streaming read of 2 GiB from HBM (the best of `reps` runs) and the v_exp_f32
+    rate (256 x 512 threads, eight independent exp2 chains each)."""
+    import ctypes
+    torch = c.torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "kv_cache_compression_window_amd", "libkvc_bench.so"))
+    lib.kvc_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.kvc_bench_exp_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    st = torch.cuda.current_stream(c.dev)
+    sh = ctypes.c_void_p(st.cuda_stream)
+    nbytes, blocks = 2 << 30, 4096
+    buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=c.dev)
+    out = torch.empty(blocks * 512, dtype=torch.int32, device=c.dev)
+    best = float("inf")
+    for r in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        assert lib.kvc_bench_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                                         blocks, sh) == 0
+        b.record(st)
+        torch.cuda.synchronize()
+        if r:  # the first run warms up
+            best = min(best, a.elapsed_time(b))
+    del buf
+    iters, eblocks = 20000, 256
+    fout = torch.empty(eblocks * 512, dtype=torch.float32, device=c.dev)
+    times = []
+    for r in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        assert lib.kvc_bench_exp_rate(ctypes.c_void_p(fout.data_ptr()), eblocks, iters, sh) == 0
+        b.record(st)
+        torch.cuda.synchronize()
+        if r:
+            times.append(a.elapsed_time(b))
+    exps = eblocks * 512 * 8 * iters
+    return {"stream_read_gbs": round(nbytes / (best * 1e-3) / 1e9, 1),
+            "exp_per_s": float(f"{exps / (min(times) * 1e-3):.4g}")}
 
 
 class Ctx:
@@ -202,7 +247,17 @@ def wl_snapkv_32k(c: Ctx, then_think: bool = False) -> dict:
             tr = json.load(f)
         if tr.get("kernel_hash") == score_kernel_hash():
             traffic = tr.get("bytes_per_launch")
-    return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes,
+    # the score call's contraction and exps: one contraction is 2*R*S*D flops per
+    # (b, g), R = G*w rows; the two passes compute it twice, with one exp2 per
+    # logit in each
+    one_contraction = 2.0 * B * H * w * S * D
+    compute = {"mfma_flops": 2 * one_contraction, "one_contraction_flops": one_contraction,
+               "exps": 2 * B * H * w * S}
+
+    def check_outputs():
+        return [t.clone() for t in (layers[0]["scores"], layers[0]["idx"], layers[0]["k_out"], layers[-1]["idx"])]
+    return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes, compute=compute,
+                check_outputs=check_outputs,
                 kernel=("kvc_window_scores (pass 1 + merge + pass 2)", [ly["kcall"] for ly in layers],
                         k_bytes + q_bytes + s_bytes, traffic),
                 cpu=cpu, metric=(f"KV tokens scored+pruned/s per layer ({cfg.name}, then ThinK on the kept keys)"
@@ -588,6 +643,46 @@ def build_workload(c: Ctx) -> dict:
     return wl_scissor_decode(c)
 
 
+def time_graph(c, wl, args) -> dict:
+    """The same step captured once into a HIP graph (the streams forked from and
+    joined to the capture stream) and replayed.  Two checked replays first, each
+    after eager work and a synchronisation, must reproduce the eager outputs bit
+    for bit; then `steps` replays are timed between two events."""
+    torch = c.torch
+    cur = torch.cuda.current_stream(c.dev)
+    eager = wl["check_outputs"]()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream(device=c.dev)
+    cs.wait_stream(cur)
+    with torch.cuda.graph(g, stream=cs):
+        for st in c.streams:
+            st.wait_stream(cs)
+        wl["step"]()
+        for st in c.streams:
+            cs.wait_stream(st)
+    torch.cuda.synchronize()
+    match = True
+    for _ in range(2):
+        scratch = torch.randn(1 << 20, device=c.dev)  # eager work between the replays
+        scratch.mul_(2.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = wl["check_outputs"]()
+        match = match and all(torch.equal(a, b) for a, b in zip(eager, got))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(cur)
+    for _ in range(args.steps):
+        g.replay()
+    b.record(cur)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    del g
+    us_layer = ms * 1e3 / (wl["layers"] * args.steps)
+    return {"us_per_layer": round(us_layer, 3), "value": round(wl["units_per_step"] * args.steps / (ms * 1e-3), 1),
+            "replays_match_eager": bool(match)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -637,6 +732,7 @@ def main():
     # pass one run of back-to-back calls on one stream between two HIP events
     # recorded on it, so that the average is the calls' own duration and not the
     # latency of an event and a dispatch per call
+    config = {"workload": wl["workload"], **wl["config"], "layers_per_step": wl["layers"], "streams": args.streams}
     label, kcalls, kbytes, traffic = wl["kernel"]
     st0 = c.streams[0]
     st0.wait_stream(cur)
@@ -659,6 +755,25 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": label,
                 "avg_us": round(k_us, 2), "algorithmic_bytes": kbytes}
 
+    graph = None
+    if not args.no_graph and wl.get("check_outputs") is not None:
+        graph = time_graph(c, wl, args)
+
+    ceilings = None if args.no_ceilings else measure_ceilings(c)
+    if ceilings:
+        roofline["frac_of_read_ceiling"] = round(achieved / ceilings["stream_read_gbs"], 4)
+    comp = wl.get("compute")
+    if comp:
+        k_s = k_us * 1e-6
+        roofline["compute"] = {
+            "mfma_tflops": round(comp["mfma_flops"] / k_s / 1e12, 1),
+            "mfma_frac": round(comp["mfma_flops"] / k_s / MFMA_BF16_PEAK, 4),
+            "one_contraction_frac": round(comp["one_contraction_flops"] / k_s / MFMA_BF16_PEAK, 4),
+            "mfma_peak_tflops": MFMA_BF16_PEAK / 1e12,
+            "exps": comp["exps"],
+            "exp_frac": round(comp["exps"] / k_s / ceilings["exp_per_s"], 4) if ceilings else None,
+        }
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=c.dev)
         dst = torch.empty_like(src)
@@ -666,9 +781,14 @@ def main():
         torch.cuda.synchronize()
 
     cpu = None if args.no_cpu_baseline else wl["cpu"](args.cpu_seconds)
-    config = {"workload": wl["workload"], **wl["config"], "layers_per_step": wl["layers"], "streams": args.streams,
-              "us_per_layer": round(t_layer_us, 3), "algorithmic_bytes_per_layer": wl["layer_bytes"],
-              "hbm_roofline_frac": round(hbm_frac, 4), "wall_s": round(wall, 4)}
+    config.update({"us_per_layer": round(t_layer_us, 3), "algorithmic_bytes_per_layer": wl["layer_bytes"],
+                   "hbm_roofline_frac": round(hbm_frac, 4), "wall_s": round(wall, 4)})
+    if ceilings:
+        config["ceilings"] = ceilings
+        config["read_ceiling_frac_per_layer"] = round(
+            wl["layer_bytes"] / (ceilings["stream_read_gbs"] * 1e9) / (t_layer_us * 1e-6), 4)
+    if graph:
+        config["graph"] = graph
     out = {
         "metric": wl["metric"],
         "value": round(value, 1),

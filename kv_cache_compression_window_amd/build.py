@@ -18,6 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libkvc.so")
+BENCH_DIR = os.path.join(CSRC, "bench")
+BENCH_LIB_PATH = os.path.join(HERE, "libkvc_bench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
@@ -28,9 +30,9 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD_DIR, src + ".o")
+def _compile(src: str, folder: str = CSRC) -> str:
+    path = os.path.join(folder, src)
+    obj = os.path.join(BUILD_DIR, os.path.basename(folder) + "_" + src + ".o")
     if src.endswith(".hip"):
         cmd = [HIPCC, *COMMON, *DEVICE, "-x", "hip", "-c", path, "-o", obj]
     else:
@@ -46,21 +48,29 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link libkvc.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16))
-    with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path):
+    tmp = path + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", *DEVICE, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    shutil.move(tmp, LIB_PATH)
+    shutil.move(tmp, path)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link libkvc.so (and bench.py's libkvc_bench.so,
+    the hardware-ceiling kernels); returns the library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    bench_srcs = sorted(f for f in os.listdir(BENCH_DIR) if f.endswith(".hip"))
+    jobs = max(1, min(len(srcs) + len(bench_srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+        bench_objs = list(ex.map(lambda f: _compile(f, BENCH_DIR), bench_srcs))
+    _link(objs, LIB_PATH)
+    _link(bench_objs, BENCH_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH} from {len(srcs)} sources")
+        print(f"built {LIB_PATH} from {len(srcs)} sources, {BENCH_LIB_PATH} from {len(bench_srcs)}")
     return LIB_PATH
 
 
