@@ -496,9 +496,13 @@ def wl_scissor_decode(c: Ctx) -> dict:
         return {"value": round(done["units"] / Hkv / el, 1), "unit": "token-steps/s", "cores": blas_threads(),
                 "kind": "oracle", "sample": f"{n} decode steps of one (batch, KV head) row of layer 0, C={C}, fp64 "
                                             f"numpy oracle (probabilities, record, eviction), {el:.1f} s"}
+    def final_state():
+        return [x for ly in layers for x in (ly["valid"], ly["hist"], ly["counts"], ly["frac"], ly["ev"])]
+
     return dict(step=step, reset=reset, units_per_step=units * nl / nsteps, layers=nl, layer_bytes=step_bytes,
                 kernel=("kvc_window_scores (w=1, stored logits)", [ly["kcall"] for ly in layers],
                         k_bytes + B * H * D * 2 + B * Hkv * C * 4, None),
+                final_state=final_state, graph_block=cfg.evict_every,
                 cpu=cpu, metric=f"KV token-steps scored+recorded/s per layer ({cfg.name})", unit="token-steps/s",
                 dtype="bf16", workload=cfg.name,
                 config={"B": B, "H": H, "Hkv": Hkv, "C": C, "D": D, "decode_steps": nsteps,
@@ -615,9 +619,14 @@ def wl_scissor_queue_decode(c: Ctx) -> dict:
         return {"value": round(done["units"] / Hkv / el, 1), "unit": "token-steps/s", "cores": blas_threads(),
                 "kind": "oracle", "sample": f"{n} decode steps of one (batch, KV head) row of layer 0, C={C}, fp64 "
                                             f"numpy oracle (insertion, probabilities, record, queue), {el:.1f} s"}
+    def final_state():
+        return [x for ly in layers for x in (ly["k"], ly["v"], ly["valid"], ly["hist"], ly["counts"], ly["since"],
+                                              ly["queue"])]
+
     return dict(step=step, reset=reset, units_per_step=units * nl / nsteps, layers=nl, layer_bytes=step_bytes,
                 kernel=("kvc_window_scores (w=1, stored logits)", [ly["kcall"] for ly in layers],
                         k_bytes + B * H * D * 2 + B * Hkv * C * 4, None),
+                final_state=final_state, graph_block=m,
                 cpu=cpu, metric=f"KV token-steps scored+recorded/s per layer ({cfg.name})", unit="token-steps/s",
                 dtype="bf16", workload=cfg.name,
                 config={"B": B, "H": H, "Hkv": Hkv, "C": C, "D": D, "decode_steps": nsteps, "prompt": P,
@@ -681,6 +690,60 @@ def time_graph(c, wl, args) -> dict:
     us_layer = ms * 1e3 / (wl["layers"] * args.steps)
     return {"us_per_layer": round(us_layer, 3), "value": round(wl["units_per_step"] * args.steps / (ms * 1e-3), 1),
             "replays_match_eager": bool(match)}
+
+
+def time_graph_blocks(c, wl, args) -> dict:
+    """A decode run captured as one HIP graph per block of `graph_block` steps
+    (one eviction or refill period; each block's step numbers, queries and
+    insert positions are its own) and replayed block after block from a fresh
+    state.  Two checked runs of replays first, each after eager work and a
+    synchronisation, must end in the eager run's final state bit for bit; then
+    one whole run of replays is timed between two events."""
+    torch = c.torch
+    cur = torch.cuda.current_stream(c.dev)
+    eager = [x.clone() for x in wl["final_state"]()]
+    blk = wl["graph_block"]
+    wl["reset"]()
+    graphs = []
+    cs = torch.cuda.Stream(device=c.dev)
+    t = 0
+    while t < args.steps:
+        n = min(blk, args.steps - t)
+        g = torch.cuda.CUDAGraph()
+        cs.wait_stream(cur)
+        with torch.cuda.graph(g, stream=cs):
+            for st in c.streams:
+                st.wait_stream(cs)
+            for _ in range(n):
+                wl["step"]()
+            for st in c.streams:
+                cs.wait_stream(st)
+        graphs.append(g)
+        t += n
+    torch.cuda.synchronize()
+    match = True
+    for _ in range(2):
+        wl["reset"]()
+        scratch = torch.randn(1 << 20, device=c.dev)  # eager work between the runs
+        scratch.mul_(2.0)
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        got = wl["final_state"]()
+        match = match and all(torch.equal(a, b) for a, b in zip(eager, got))
+    wl["reset"]()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(cur)
+    for g in graphs:
+        g.replay()
+    b.record(cur)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    del graphs
+    return {"us_per_layer": round(ms * 1e3 / (wl["layers"] * args.steps), 3),
+            "value": round(wl["units_per_step"] * args.steps / (ms * 1e-3), 1),
+            "steps_per_graph": blk, "graphs": (args.steps + blk - 1) // blk, "replays_match_eager": bool(match)}
 
 
 def main():
@@ -758,6 +821,8 @@ def main():
     graph = None
     if not args.no_graph and wl.get("check_outputs") is not None:
         graph = time_graph(c, wl, args)
+    elif not args.no_graph and wl.get("final_state") is not None:
+        graph = time_graph_blocks(c, wl, args)
 
     ceilings = None if args.no_ceilings else measure_ceilings(c)
     if ceilings:

@@ -105,6 +105,27 @@ def test_window_scores(case):
     assert torch.equal(s, s2)
 
 
+# The same (b, g) rows under two grid splits: batch 0 alone, and batch 0 next to
+# other sequences, which gives each KV head fewer, longer key chunks (the plan
+# aims at a fixed number of workgroups per call).  Two-pass: 8 KV heads take 32
+# chunks of 256 keys, 32 take 8 chunks of 1024.  Stored logits: 8 KV heads take
+# 16 chunks of 1024 keys, 64 take 8 of 2048.  Each split is bit-reproducible and
+# within the score tolerance of the oracle.
+@pytest.mark.parametrize("B2,S,w", [(4, 8192, 64), (8, 16384, 1)], ids=["two_pass", "stored_logits"])
+def test_window_scores_two_grid_splits(B2, S, w):
+    say(f"window_scores grid splits B=1 vs B={B2}, S={S}, w={w}")
+    p = synth.random_problem(77, B2, 32, 8, S, 128, w, dtype="bf16", heavy_frac=0.02)
+    ref = O.window_scores(p.q64()[:1], p.k64()[:1], causal=w > 1)
+    L = lib()
+    q, k = dev(p.q, "bf16"), dev(p.k, "bf16")
+    one = [L.kvc_window_scores(q[:1].contiguous(), k[:1].contiguous(), causal=w > 1) for _ in range(2)]
+    many = [L.kvc_window_scores(q, k, causal=w > 1) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(one[0], one[1]) and torch.equal(many[0], many[1])
+    check_scores(one[0].cpu().numpy(), ref, "batch alone")
+    check_scores(many[0][:1].cpu().numpy(), ref, f"batch 0 of {B2}")
+
+
 @pytest.mark.parametrize("rows,n,k,n_tail,levels", [
     (8, 32768, 4096, 64, 0), (3, 1000, 10, 0, 0), (5, 777, 300, 20, 4), (2, 200000, 5000, 64, 0),
     (64, 4096, 64, 0, 401), (7, 129, 64, 0, 3), (1, 50, 50, 5, 0), (4, 60, 5, 5, 0), (3, 64, 1, 0, 2),
