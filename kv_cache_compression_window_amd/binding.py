@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_
                 5: "KVC_ERR_WORKSPACE", 6: "KVC_ERR_UNSUPPORTED", 7: "KVC_ERR_HIP"}
 
 # every symbol include/kvc.h declares
-EXPORTS = ["kvc_window_scores", "kvc_scissor_update", "kvc_channel_scores", "kvc_topk_select",
+EXPORTS = ["kvc_window_scores", "kvc_window_scores_ex", "kvc_scissor_update", "kvc_channel_scores", "kvc_topk_select",
            "kvc_gather_compact", "kvc_gather_compress", "kvc_channel_expand", "kvc_query_channels",
            "kvc_scissor_refill", "kvc_scissor_insert", "kvc_window_scores_noalloc", "kvc_status_string",
            "kvc_abi_version"]
@@ -50,6 +50,7 @@ def _load():
     SH = ctypes.POINTER(KvcShape)
     sig = {
         "kvc_window_scores": [SH, I32, P, P, P, P, I32, I32, I32, P, P, SZP, P],
+        "kvc_window_scores_ex": [SH, I32, P, P, P, P, I32, I32, I32, I32, P, P, SZP, P],
         "kvc_window_scores_noalloc": [SH, I32, P, P, P, P, I32, I32, I32, P, P],
         "kvc_scissor_update": [I32, I32, I32, I32, I64, P, P, P, P, P, P, P, I32, P],
         "kvc_channel_scores": [SH, I32, P, P, P, P, SZP, P],
@@ -116,18 +117,28 @@ def _workspace(nbytes: int, device, ws):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def window_scores_ws_bytes(B, H, Hkv, S, D, w, dtype=None) -> int:
+def _ws_call(concurrent_calls, sh, dt, q, k, valid, chan, d_keep, reduce, causal, scores, ws, n, stream):
+    """kvc_window_scores, or kvc_window_scores_ex when a concurrency hint is given."""
+    if concurrent_calls in (None, 1):
+        return "kvc_window_scores", (sh, dt, q, k, valid, chan, d_keep, reduce, causal, scores, ws, n, stream)
+    return "kvc_window_scores_ex", (sh, dt, q, k, valid, chan, d_keep, reduce, causal, int(concurrent_calls),
+                                    scores, ws, n, stream)
+
+
+def window_scores_ws_bytes(B, H, Hkv, S, D, w, dtype=None, concurrent_calls=None) -> int:
     sh = KvcShape(B, H, Hkv, S, D, w)
     n = ctypes.c_size_t(0)
     dt = KVC_BF16 if dtype is None else dtype
-    _check("kvc_window_scores", LIB.kvc_window_scores(ctypes.byref(sh), dt, None, None, None, None, 0, 0, 0,
-                                                      None, None, ctypes.byref(n), None))
+    name, args = _ws_call(concurrent_calls, ctypes.byref(sh), dt, None, None, None, None, 0, 0, 0, None, None,
+                          ctypes.byref(n), None)
+    _check(name, getattr(LIB, name)(*args))
     return n.value
 
 
 def kvc_window_scores(q, k, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, causal=True, scores=None, ws=None,
-                      stream=None):
-    """scores [B,Hkv,S] float32 of the window rows q [B,H,w,D] against k [B,Hkv,S,D]."""
+                      stream=None, concurrent_calls=None):
+    """scores [B,Hkv,S] float32 of the window rows q [B,H,w,D] against k [B,Hkv,S,D]
+    (kvc_window_scores_ex when concurrent_calls is given and not 1)."""
     _need(q, "q_win", 4)
     _need(k, "k", 4)
     sh = _shape(q, k)
@@ -142,14 +153,15 @@ def kvc_window_scores(q, k, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, 
     if scores is None:
         scores = torch.empty((sh.B, sh.Hkv, sh.S), dtype=torch.float32, device=k.device)
     n = ctypes.c_size_t(0)
-    _check("kvc_window_scores", LIB.kvc_window_scores(ctypes.byref(sh), _dtype_code(k), None, None, None, None,
-                                                      d_keep, reduce, int(causal), None, None, ctypes.byref(n),
-                                                      None))
+    name, args = _ws_call(concurrent_calls, ctypes.byref(sh), _dtype_code(k), None, None, None, None, d_keep, reduce,
+                          int(causal), None, None, ctypes.byref(n), None)
+    _check(name, getattr(LIB, name)(*args))
     ws = _workspace(n.value, k.device, ws)
     n = ctypes.c_size_t(ws.numel() * ws.element_size())
-    _check("kvc_window_scores", LIB.kvc_window_scores(ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid),
-                                                      _ptr(chan_idx), d_keep, reduce, int(causal), _ptr(scores),
-                                                      _ptr(ws), ctypes.byref(n), _stream(stream)))
+    name, args = _ws_call(concurrent_calls, ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid),
+                          _ptr(chan_idx), d_keep, reduce, int(causal), _ptr(scores), _ptr(ws), ctypes.byref(n),
+                          _stream(stream))
+    _check(name, getattr(LIB, name)(*args))
     return scores
 
 
@@ -349,15 +361,17 @@ def _bound(fn_name, args):
     return call
 
 
-def bind_window_scores(q, k, scores, ws, stream, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, causal=True):
+def bind_window_scores(q, k, scores, ws, stream, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, causal=True,
+                       concurrent_calls=None):
     _need(q, "q_win", 4)
     _need(k, "k", 4)
     sh = _shape(q, k)
     d_keep = 0 if chan_idx is None else chan_idx.shape[2]
     n = ctypes.c_size_t(ws.numel() * ws.element_size())
-    args = (ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid), _ptr(chan_idx), d_keep, reduce,
-            int(causal), _ptr(scores), _ptr(ws), ctypes.byref(n), ctypes.c_void_p(stream.cuda_stream))
-    call = _bound("kvc_window_scores", args)
+    name, args = _ws_call(concurrent_calls, ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid),
+                          _ptr(chan_idx), d_keep, reduce, int(causal), _ptr(scores), _ptr(ws), ctypes.byref(n),
+                          ctypes.c_void_p(stream.cuda_stream))
+    call = _bound(name, args)
     call.keep_alive = (sh, n, q, k, valid, chan_idx, scores, ws)
     return call
 

@@ -36,7 +36,13 @@ constexpr int kMaxRows = 1024;  // G*w limit per KV head
 constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
 constexpr int kMergeLanes = 8;  // lanes of the merge kernel per (b, g, row)
 
-inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, WsPlan* p) {
+// `share` (>= 1): the number of score calls the caller runs at the same time;
+// each call then aims at 1/share of the workgroups that fill the GPU, so that the
+// calls run side by side with longer key chunks instead of queueing for the
+// whole chip.
+constexpr int kMaxShare = 64;
+
+inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, int share, WsPlan* p) {
   const int G = H / Hkv;
   const long long R = (long long)G * w;
   if (R > kMaxRows) return false;
@@ -53,7 +59,9 @@ inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, WsPlan* p) {
   if (bg * p->Rpad * kMergeLanes > 0x7fffffffLL) return false;
   // workgroups to aim for: about eight waves per CU on the two-pass path, two
   // four-wave streaming workgroups per CU on the (HBM-bound) stored-logits path
-  const long long target = p->store ? 512 : 256LL * 8 / p->NW;
+  long long target = p->store ? 512 : 256LL * 8 / p->NW;
+  target = target / (share < 1 ? 1 : share);
+  if (target < 1) target = 1;
   long long nch = (target + bg - 1) / bg;
   if (p->store) {
     // stored-logits chunks of at least 1024 keys (a quarter of the row when that

@@ -862,13 +862,54 @@ __global__ __launch_bounds__(kLogNW * 64) void ws_logits_kernel(WsParams p) {
 // rows of one KV head, or of every KV head of the sequence for ALL_HEADS) into
 // LDS, in chunk order, then s[b,g,j] = scale * sum over the rows of
 // exp2(logit - lse2).  Rows with no allowed key contribute 0.
-__global__ __launch_bounds__(256) void ws_finish_logits_kernel(WsParams p, int all_heads, float scale) {
+// Each thread owns KPT consecutive keys (one load per row: 16 bytes for GROUP,
+// whose workgroups cover 1024 keys of one KV head; 4 bytes for ALL_HEADS, whose
+// workgroups cover 256 keys and loop over the KV heads).  The logits of the
+// first KV head are requested before the statistics are merged, and those of
+// KV head g+1 while head g is summed, so a workgroup waits on memory about once
+// per KV head instead of once per row.  RM: the rows per KV head rounded up to
+// 4, 8 or 16 (R <= 16 on this path).
+constexpr int kFinThreads = 256;
+
+template <int KPT>
+struct FinVec {
+  float v[KPT];
+};
+
+template <int RM, int KPT>
+__global__ __launch_bounds__(kFinThreads) void ws_finish_logits_kernel(WsParams p, int all_heads, float scale) {
+  static_assert(KPT == 1 || KPT == 4, "one or four keys per thread");
   __shared__ float lds_lse[kFinishRows];
   const int b = blockIdx.z;
   const int g0 = all_heads ? 0 : blockIdx.y;
   const int ng = all_heads ? p.Hkv : 1;
   const int nrows = ng * p.R;
-  for (int t = threadIdx.x; t < nrows; t += blockDim.x) {
+  const int j0 = (blockIdx.x * kFinThreads + threadIdx.x) * KPT;
+  // j0 < S <= Spad and both are multiples of KPT, so the row's load stays inside
+  // the padded logits row (values past S are never stored)
+  const bool live = j0 < p.S;
+
+  auto load_head = [&](FinVec<KPT> (&lg)[RM], int gi) {
+    const float* src = p.logits + (((size_t)b * p.Hkv + g0 + gi) * p.R) * (size_t)p.Spad + j0;
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      if (live && r < p.R) {
+        if constexpr (KPT == 4) {
+          const float4 x = *reinterpret_cast<const float4*>(src + (size_t)r * p.Spad);
+          lg[r].v[0] = x.x;
+          lg[r].v[1] = x.y;
+          lg[r].v[2] = x.z;
+          lg[r].v[3] = x.w;
+        } else {
+          lg[r].v[0] = src[(size_t)r * p.Spad];
+        }
+      }
+    }
+  };
+  FinVec<KPT> lg[RM];
+  load_head(lg, 0);
+
+  for (int t = threadIdx.x; t < nrows; t += kFinThreads) {
     const int g = g0 + t / p.R, r = t % p.R;
     const size_t row = ((size_t)b * p.Hkv + g) * p.Rpad + r;
     float m = kNegInf, z = 0.0f;
@@ -880,20 +921,42 @@ __global__ __launch_bounds__(256) void ws_finish_logits_kernel(WsParams p, int a
     lds_lse[t] = (m == kNegInf || !(z > 0.0f)) ? kPosInf : m + log2f(z);
   }
   __syncthreads();
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= p.S) return;
-  float s = 0.0f;
+  if (!live) return;
+
+  float s[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) s[e] = 0.0f;
   for (int gi = 0; gi < ng; ++gi) {
-    const size_t bg = (size_t)b * p.Hkv + g0 + gi;
-    float sg = 0.0f;
-    for (int r = 0; r < p.R; ++r) sg += fast_exp2(p.logits[(bg * p.R + r) * (size_t)p.Spad + j] - lds_lse[gi * p.R + r]);
-    s += sg;
+    FinVec<KPT> nx[RM];
+    if (gi + 1 < ng) load_head(nx, gi + 1);
+    float sg[KPT];
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) sg[e] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      if (r < p.R) {
+        const float l = lds_lse[gi * p.R + r];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) sg[e] += fast_exp2(lg[r].v[e] - l);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) s[e] += sg[e];
+    if (gi + 1 < ng) {
+#pragma unroll
+      for (int r = 0; r < RM; ++r) lg[r] = nx[r];
+    }
   }
-  s *= scale;
-  if (all_heads) {
-    for (int g = 0; g < p.Hkv; ++g) p.scores[((size_t)b * p.Hkv + g) * p.S + j] = s;
-  } else {
-    p.scores[((size_t)b * p.Hkv + g0) * p.S + j] = s;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const int j = j0 + e;
+    if (j >= p.S) break;
+    const float v = s[e] * scale;
+    if (all_heads) {
+      for (int g = 0; g < p.Hkv; ++g) p.scores[((size_t)b * p.Hkv + g) * p.S + j] = v;
+    } else {
+      p.scores[((size_t)b * p.Hkv + g0) * p.S + j] = v;
+    }
   }
 }
 
@@ -1044,8 +1107,18 @@ hipError_t launch_window_scores(const WsArgs& a, const WsPlan& plan, hipStream_t
     else if (a.D == 128) ws_logits_kernel<float, 128><<<grid, kLogNW * 64, 0, st>>>(p);
     else ws_logits_kernel<float, 64><<<grid, kLogNW * 64, 0, st>>>(p);
     const int all = a.reduce ? 1 : 0;
-    const dim3 g2((a.S + 255) / 256, all ? 1 : a.Hkv, a.B);
-    ws_finish_logits_kernel<<<g2, 256, 0, st>>>(p, all, all ? 1.0f / (float)(a.H * a.w) : p.out_scale);
+    const float fscale = all ? 1.0f / (float)(a.H * a.w) : p.out_scale;
+    if (all) {
+      const dim3 g2((a.S + kFinThreads - 1) / kFinThreads, 1, a.B);
+      if (plan.R <= 4) ws_finish_logits_kernel<4, 1><<<g2, kFinThreads, 0, st>>>(p, all, fscale);
+      else if (plan.R <= 8) ws_finish_logits_kernel<8, 1><<<g2, kFinThreads, 0, st>>>(p, all, fscale);
+      else ws_finish_logits_kernel<16, 1><<<g2, kFinThreads, 0, st>>>(p, all, fscale);
+    } else {
+      const dim3 g2((a.S + 4 * kFinThreads - 1) / (4 * kFinThreads), a.Hkv, a.B);
+      if (plan.R <= 4) ws_finish_logits_kernel<4, 4><<<g2, kFinThreads, 0, st>>>(p, all, fscale);
+      else if (plan.R <= 8) ws_finish_logits_kernel<8, 4><<<g2, kFinThreads, 0, st>>>(p, all, fscale);
+      else ws_finish_logits_kernel<16, 4><<<g2, kFinThreads, 0, st>>>(p, all, fscale);
+    }
     return hipGetLastError();
   }
   for (int c = 0; c < plan.nrch; ++c) {  // row statistics

@@ -48,6 +48,14 @@ int main() {
   expect("ws small workspace", ws(&ok, 1, fake, fake, 0, fake, &small), KVC_ERR_WORKSPACE);
   expect("ws null q", ws(&ok, 1, nullptr, fake, 0, fake, &big), KVC_ERR_NULL);
   expect("ws misaligned k", ws(&ok, 1, fake, odd, 0, fake, &big), KVC_ERR_ALIGN);
+  auto wsx = [&](int conc, void* w, size_t* n) {
+    return kvc_window_scores_ex(&ok, KVC_BF16, fake, fake, nullptr, nullptr, 0, KVC_REDUCE_GROUP, 1, conc,
+                                static_cast<float*>(fake), w, n, nullptr);
+  };
+  expect("ws_ex hint < 0", wsx(-1, fake, &big), KVC_ERR_SHAPE);
+  expect("ws_ex hint > 64", wsx(65, fake, &big), KVC_ERR_SHAPE);
+  expect("ws_ex size query", wsx(2, nullptr, &q), KVC_OK);
+  expect("ws_ex small workspace", wsx(64, fake, &small), KVC_ERR_WORKSPACE);
   expect("ws noalloc overflow",
          kvc_window_scores_noalloc(&(const kvc_shape&)kvc_shape{64, 32, 8, 8192, 128, 1}, KVC_BF16, fake, fake,
                                    nullptr, nullptr, 0, KVC_REDUCE_GROUP, 0, static_cast<float*>(fake), nullptr),

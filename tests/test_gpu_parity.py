@@ -105,6 +105,27 @@ def test_window_scores(case):
     assert torch.equal(s, s2)
 
 
+# The concurrency hint of kvc_window_scores_ex: fewer, longer key chunks per
+# call; each hint's scores are within the tolerance of the oracle and
+# bit-reproducible.
+@pytest.mark.parametrize("conc", [2, 3, 7, 64])
+@pytest.mark.parametrize("case", [CASES[9], CASES[12], CASES[1], CASES[21], CASES[31]],
+                         ids=[CASES[i][0] for i in (9, 12, 1, 21, 31)])
+def test_window_scores_concurrency_hint(case, conc):
+    name, B, H, Hkv, S, D, w, dt, reduce, causal, holes, d_keep, qs = case
+    say(f"window_scores_ex {name} concurrent_calls={conc}")
+    p, valid, chan = _make(case, 100 + CASES.index(case))
+    ref = O.window_scores(p.q64(), p.k64(), valid=valid, chan_keep=chan, reduce=reduce, causal=causal)
+    L = lib()
+    args = dict(valid=None if valid is None else dev(valid), chan_idx=None if chan is None else dev(chan),
+                reduce=reduce, causal=bool(causal), concurrent_calls=conc)
+    s1 = L.kvc_window_scores(dev(p.q, dt), dev(p.k, dt), **args)
+    s2 = L.kvc_window_scores(dev(p.q, dt), dev(p.k, dt), **args)
+    torch.cuda.synchronize()
+    check_scores(s1.cpu().numpy(), ref, f"{name} hint {conc}")
+    assert torch.equal(s1, s2)
+
+
 # The same (b, g) rows under two grid splits: batch 0 alone, and batch 0 next to
 # other sequences, which gives each KV head fewer, longer key chunks (the plan
 # aims at a fixed number of workgroups per call).  Two-pass: 8 KV heads take 32
