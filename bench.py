@@ -70,6 +70,8 @@ def parse():
                     help="passes over the layers, each timed as one run of back-to-back calls of the dominant kernel")
     ap.add_argument("--concurrent-calls", type=int, default=None,
                     help="kvc_window_scores_ex's hint: score calls planned to run side by side (default per workload)")
+    ap.add_argument("--no-alone", action="store_true",
+                    help="with a concurrency hint, skip timing the calls planned to fill the GPU alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the read-ceiling and exp-rate measurements")
@@ -217,9 +219,10 @@ def wl_snapkv_32k(c: Ctx, then_think: bool = False) -> dict:
                             L.bind_gather_compress(ly["k_out"], None, ly["rows"], ly["ch"], ly["kc"], None, st)]
         ly["kcall"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], s0, reduce=L.KVC_REDUCE_GROUP,
                                            causal=True, concurrent_calls=conc)
-        if conc != 1:
+        if conc != 1:  # own workspace and scores: the step's outputs stay those of the hinted calls
             ly["ws1"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, S, D, w), torch.uint8)
-            ly["kcall1"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws1"], s0,
+            ly["scores1"] = c.empty((B, Hkv, S), torch.float32)
+            ly["kcall1"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores1"], ly["ws1"], s0,
                                                 reduce=L.KVC_REDUCE_GROUP, causal=True)
 
     def step():
@@ -386,9 +389,10 @@ def wl_think_128k(c: Ctx, compress: bool = False) -> dict:
                                                      chan_idx=ly["ch"]))
         ly["kcall"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], s0, chan_idx=ly["ch"],
                                            reduce=L.KVC_REDUCE_GROUP, causal=True, concurrent_calls=conc)
-        if conc != 1:
+        if conc != 1:  # own workspace and scores: the step's outputs stay those of the hinted calls
             ly["ws1"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, S, D, w), torch.uint8)
-            ly["kcall1"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws1"], s0, chan_idx=ly["ch"],
+            ly["scores1"] = c.empty((B, Hkv, S), torch.float32)
+            ly["kcall1"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores1"], ly["ws1"], s0, chan_idx=ly["ch"],
                                                 reduce=L.KVC_REDUCE_GROUP, causal=True)
 
     def step():
@@ -844,7 +848,7 @@ def main():
         return float(np.mean([a.elapsed_time(b) for (a, b) in kev])) / len(calls) * 1e3
     k_us = time_calls(kcalls)
     # the same calls planned to fill the GPU alone (kvc_window_scores without a hint)
-    k1_us = time_calls(wl["kernel_alone"]) if wl.get("kernel_alone") else None
+    k1_us = time_calls(wl["kernel_alone"]) if wl.get("kernel_alone") and not args.no_alone else None
 
     units = wl["units_per_step"] * args.steps
     value = units / (elapsed_ms * 1e-3)
