@@ -60,7 +60,13 @@ struct TopkShared {
   alignas(16) uint32_t wave_tot[NWAVE];
   uint32_t red_min[NWAVE], red_max[NWAVE];
   uint32_t bucket, krem, bcount;
+  uint32_t nlist;  // candidates collected by the second pass
 };
+
+// The second pass also collects the keys it counts (those in the first pass's
+// threshold bin) into a list in the words past the histogram; later passes read
+// that list instead of every key of the row.
+constexpr int kListCap = kXposeWords - NBIN * NCOPY;
 
 // Inclusive prefix sum over the 64 lanes of a wave: DPP shifts within rows of
 // 16 lanes, then the broadcasts of lane 15 and lane 31 into the later rows.
@@ -116,12 +122,22 @@ __device__ inline uint32_t block_exclusive_scan(TopkShared& sh, uint32_t x, int 
 // thread order is a suffix sum over the bins and exactly one thread sees it
 // cross krem.  Leaves the bin, the rank still to take inside it and the bin's
 // count in sh.bucket, sh.krem and sh.bcount.
-__device__ inline void find_bin(TopkShared& sh, uint32_t krem, int tid, int lane, int wave) {
+// `wide`: the histogram has NCOPY interleaved copies per bin (the first pass);
+// otherwise one counter per bin in the first NBIN words (the later passes, which
+// count few keys).
+__device__ inline void find_bin(TopkShared& sh, uint32_t krem, int tid, int lane, int wave, bool wide) {
   const int b_hi = NBIN - 1 - 2 * tid, b_lo = b_hi - 1;
-  const uint4* h = reinterpret_cast<const uint4*>(sh.hist);
-  const uint4 h0 = h[b_hi * 2], h1 = h[b_hi * 2 + 1], h2 = h[b_lo * 2], h3 = h[b_lo * 2 + 1];
-  const uint32_t c_hi = h0.x + h0.y + h0.z + h0.w + h1.x + h1.y + h1.z + h1.w;
-  const uint32_t c_lo = h2.x + h2.y + h2.z + h2.w + h3.x + h3.y + h3.z + h3.w;
+  uint32_t c_hi, c_lo;
+  if (wide) {
+    const uint4* h = reinterpret_cast<const uint4*>(sh.hist);
+    const uint4 h0 = h[b_hi * 2], h1 = h[b_hi * 2 + 1], h2 = h[b_lo * 2], h3 = h[b_lo * 2 + 1];
+    c_hi = h0.x + h0.y + h0.z + h0.w + h1.x + h1.y + h1.z + h1.w;
+    c_lo = h2.x + h2.y + h2.z + h2.w + h3.x + h3.y + h3.z + h3.w;
+  } else {
+    const uint2 h = reinterpret_cast<const uint2*>(sh.hist)[b_lo >> 1];  // bins b_lo (even) and b_hi
+    c_lo = h.x;
+    c_hi = h.y;
+  }
   const uint32_t local = c_hi + c_lo;
   const uint32_t winc = wave_inclusive_scan(local);
   if (lane == 63) sh.wave_tot[wave] = winc;
@@ -260,30 +276,55 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
   uint32_t prefix = 0u;                            // fixed high bits of rel(T)
   uint32_t krem = (uint32_t)kp;                    // still to take among the keys matching the prefix
   uint32_t last_count = (uint32_t)(ntiles * TILE);  // keys equal to T (all of them when npass == 0)
+  uint32_t* list = sh.xpose + NBIN * NCOPY;        // free during the passes
+  bool from_list = false;
   for (int pass = 0; pass < npass; ++pass) {
     const int hi = L - DBITS * pass;       // bits [hi, 32) of rel are fixed
     const int shift = max(0, hi - DBITS);  // this digit is bits [shift, hi)
     const uint32_t fixed = hi >= 32 ? 0u : ~0u << hi;
+    const bool wide = pass == 0;
+    if (wide) {
 #pragma unroll
-    for (int j = 0; j < NBIN * NCOPY / 4 / NTH; ++j)
-      reinterpret_cast<uint4*>(sh.hist)[j * NTH + tid] = make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < NBIN * NCOPY / 4 / NTH; ++j)
+        reinterpret_cast<uint4*>(sh.hist)[j * NTH + tid] = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+      if (tid < NBIN / 4) reinterpret_cast<uint4*>(sh.hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
+      if (pass == 1 && tid == 0) sh.nlist = 0u;
+    }
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      if constexpr (!RESIDENT) load_rel_coalesced(t);
-      if (pass == 0) {
+    if (from_list) {
+      const int nl = (int)sh.nlist;
+      for (int j = tid; j < nl; j += NTH) {
+        const uint32_t x = list[j];
+        if ((x & fixed) == prefix) atomicAdd(&sh.hist[(x >> shift) & (NBIN - 1)], 1u);
+      }
+    } else {
+      for (int t = 0; t < ntiles; ++t) {
+        if constexpr (!RESIDENT) load_rel_coalesced(t);
+        if (wide) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) atomicAdd(&sh.hist[((u[i] >> shift) & (NBIN - 1)) * NCOPY + cp], 1u);
-      } else {
+          for (int i = 0; i < KPT; ++i) atomicAdd(&sh.hist[((u[i] >> shift) & (NBIN - 1)) * NCOPY + cp], 1u);
+        } else {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i)
-          if ((u[i] & fixed) == prefix) atomicAdd(&sh.hist[((u[i] >> shift) & (NBIN - 1)) * NCOPY + cp], 1u);
+          for (int i = 0; i < KPT; ++i) {
+            if ((u[i] & fixed) == prefix) {
+              atomicAdd(&sh.hist[(u[i] >> shift) & (NBIN - 1)], 1u);
+              if (pass == 1) {
+                const uint32_t pos = atomicAdd(&sh.nlist, 1u);
+                if (pos < (uint32_t)kListCap) list[pos] = u[i];
+              }
+            }
+          }
+        }
       }
     }
     __syncthreads();
-    find_bin(sh, krem, tid, lane, wave);
+    find_bin(sh, krem, tid, lane, wave, wide);
     prefix |= sh.bucket << shift;
     krem = sh.krem;
     last_count = sh.bcount;
+    // the list holds every key of the second pass's prefix unless it overflowed
+    if (pass == 1) from_list = sh.nlist <= (uint32_t)kListCap;
   }
   const uint32_t T = prefix;      // rel of the kp-th largest eligible score
   const uint32_t take_eq = krem;  // keys equal to T to take, lowest positions first
