@@ -63,10 +63,15 @@ struct TopkShared {
   uint32_t nlist;  // candidates collected by the second pass
 };
 
-// The second pass also collects the keys it counts (those in the first pass's
-// threshold bin) into a list in the words past the histogram; later passes read
-// that list instead of every key of the row.
-constexpr int kListCap = kXposeWords - NBIN * NCOPY;
+// The passes after the first count few keys: each has its own one-copy
+// histogram at the end of the hand-over area, cleared with the first pass's, so
+// they start without a clear and a barrier.  The second pass also collects the
+// keys it counts (those in the first pass's threshold bin) into a list between
+// the first histogram and those; later passes read that list instead of every
+// key of the row.
+constexpr int kNarrowHist0 = kXposeWords - 2 * NBIN;  // second pass; the third at + NBIN
+constexpr int kListCap = kNarrowHist0 - NBIN * NCOPY;
+static_assert(kListCap > 4 * NTH, "room for the candidate list");
 
 // Inclusive prefix sum over the 64 lanes of a wave: DPP shifts within rows of
 // 16 lanes, then the broadcasts of lane 15 and lane 31 into the later rows.
@@ -125,16 +130,17 @@ __device__ inline uint32_t block_exclusive_scan(TopkShared& sh, uint32_t x, int 
 // `wide`: the histogram has NCOPY interleaved copies per bin (the first pass);
 // otherwise one counter per bin in the first NBIN words (the later passes, which
 // count few keys).
-__device__ inline void find_bin(TopkShared& sh, uint32_t krem, int tid, int lane, int wave, bool wide) {
+__device__ inline void find_bin(TopkShared& sh, const uint32_t* hist, uint32_t krem, int tid, int lane, int wave,
+                                bool wide) {
   const int b_hi = NBIN - 1 - 2 * tid, b_lo = b_hi - 1;
   uint32_t c_hi, c_lo;
   if (wide) {
-    const uint4* h = reinterpret_cast<const uint4*>(sh.hist);
+    const uint4* h = reinterpret_cast<const uint4*>(hist);
     const uint4 h0 = h[b_hi * 2], h1 = h[b_hi * 2 + 1], h2 = h[b_lo * 2], h3 = h[b_lo * 2 + 1];
     c_hi = h0.x + h0.y + h0.z + h0.w + h1.x + h1.y + h1.z + h1.w;
     c_lo = h2.x + h2.y + h2.z + h2.w + h3.x + h3.y + h3.z + h3.w;
   } else {
-    const uint2 h = reinterpret_cast<const uint2*>(sh.hist)[b_lo >> 1];  // bins b_lo (even) and b_hi
+    const uint2 h = reinterpret_cast<const uint2*>(hist)[b_lo >> 1];  // bins b_lo (even) and b_hi
     c_lo = h.x;
     c_hi = h.y;
   }
@@ -283,20 +289,21 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
     const int shift = max(0, hi - DBITS);  // this digit is bits [shift, hi)
     const uint32_t fixed = hi >= 32 ? 0u : ~0u << hi;
     const bool wide = pass == 0;
+    uint32_t* hist = wide ? sh.hist : sh.xpose + kNarrowHist0 + (pass - 1) * NBIN;
     if (wide) {
 #pragma unroll
       for (int j = 0; j < NBIN * NCOPY / 4 / NTH; ++j)
         reinterpret_cast<uint4*>(sh.hist)[j * NTH + tid] = make_uint4(0u, 0u, 0u, 0u);
-    } else {
-      if (tid < NBIN / 4) reinterpret_cast<uint4*>(sh.hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
-      if (pass == 1 && tid == 0) sh.nlist = 0u;
+      static_assert(2 * NBIN / 4 == NTH, "one 16-byte clear per thread for the later histograms");
+      reinterpret_cast<uint4*>(sh.xpose + kNarrowHist0)[tid] = make_uint4(0u, 0u, 0u, 0u);
+      if (tid == 0) sh.nlist = 0u;
+      __syncthreads();
     }
-    __syncthreads();
     if (from_list) {
       const int nl = (int)sh.nlist;
       for (int j = tid; j < nl; j += NTH) {
         const uint32_t x = list[j];
-        if ((x & fixed) == prefix) atomicAdd(&sh.hist[(x >> shift) & (NBIN - 1)], 1u);
+        if ((x & fixed) == prefix) atomicAdd(&hist[(x >> shift) & (NBIN - 1)], 1u);
       }
     } else {
       for (int t = 0; t < ntiles; ++t) {
@@ -308,7 +315,7 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
 #pragma unroll
           for (int i = 0; i < KPT; ++i) {
             if ((u[i] & fixed) == prefix) {
-              atomicAdd(&sh.hist[(u[i] >> shift) & (NBIN - 1)], 1u);
+              atomicAdd(&hist[(u[i] >> shift) & (NBIN - 1)], 1u);
               if (pass == 1) {
                 const uint32_t pos = atomicAdd(&sh.nlist, 1u);
                 if (pos < (uint32_t)kListCap) list[pos] = u[i];
@@ -319,7 +326,7 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
       }
     }
     __syncthreads();
-    find_bin(sh, krem, tid, lane, wave, wide);
+    find_bin(sh, hist, krem, tid, lane, wave, wide);
     prefix |= sh.bucket << shift;
     krem = sh.krem;
     last_count = sh.bcount;
