@@ -56,6 +56,7 @@ struct WsParams {
   int Hkv, S, w, R, Rpad, d_keep, causal, CH, nchunks, Spad, rows_total;
   int row0;        // first row of the current row chunk
   int accumulate;  // scores pass: add to the scores already written
+  int lse_from_part;  // scores pass: merge the chunk partials itself (no merge launch)
   float c;         // log2(e) / sqrt(D)
   float out_scale; // scores: 1/(G*w) for GROUP, 1 for ALL_HEADS (normalised later)
   float2* part;    // [nchunks][B*Hkv*Rpad] (max, sum of exp2) in base-2 units
@@ -264,6 +265,34 @@ __device__ inline void load_neg_lse(float (&nb)[16], const WsParams& p, size_t b
     nb[4 * v4 + 2] = -l4.z;
     nb[4 * v4 + 3] = -l4.w;
   }
+}
+
+// The same values merged here from the chunk partials of the statistics pass
+// (the scores pass then needs no merge launch before it): lane (col, half) folds
+// chunks half, half+2, ... of row rowblk+col, the two lane halves are merged,
+// and every lane fetches its 16 accumulator rows from the lanes that hold them.
+// Rows past R, and rows with no allowed key, get +inf.
+__device__ inline void neg_lse_from_part(float (&nb)[16], const WsParams& p, size_t bg, int rowblk, int lane,
+                                         int half) {
+  const int r = rowblk + (lane & 31);
+  const float2* part = p.part + bg * p.Rpad + r;
+  float m = kNegInf, z = 0.0f;
+  int c = half;
+  for (; c + 6 < p.nchunks; c += 8) {  // four partials requested together
+    float2 pc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pc[i] = part[(size_t)(c + 2 * i) * p.rows_total];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lse2_merge(m, z, pc[i].x, pc[i].y);
+  }
+  for (; c < p.nchunks; c += 2) {
+    const float2 pc = part[(size_t)c * p.rows_total];
+    lse2_merge(m, z, pc.x, pc.y);
+  }
+  lse2_merge(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));
+  const float l = (r >= p.R || m == kNegInf || !(z > 0.0f)) ? kPosInf : m + log2f(z);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) nb[v] = -__shfl(l, acc_row(v, lane));
 }
 
 // Fold the 16 logits of one (query row, 16 keys) lane slice into the lane's
@@ -537,7 +566,8 @@ __global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
   if constexpr (QLDS) load_query_rows<T, D>(qf, p, bg, rowblk, lane, half, keep, lds_q[wave]);
   else load_query<T, D>(qf, p, bg, rowblk + col, half, keep);
   float nb[16];
-  load_neg_lse(nb, p, bg, rowblk, half);
+  if (p.lse_from_part) neg_lse_from_part(nb, p, bg, rowblk, lane, half);
+  else load_neg_lse(nb, p, bg, rowblk, half);
 
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
   auto mfma = [&](const Frag<T, D>& kf) { return mma_block<T, D>(qf, kf); };
@@ -677,7 +707,8 @@ __global__ __launch_bounds__(64) void ws_scores_wave_kernel(WsParams p) {
   Frag<T, D> qf;
   load_query<T, D>(qf, p, bg, col, half, keep);
   float nb[16];
-  load_neg_lse(nb, p, bg, 0, half);
+  if (p.lse_from_part) neg_lse_from_part(nb, p, bg, p.row0, lane, half);
+  else load_neg_lse(nb, p, bg, 0, half);
 
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
   Stager<T, D, 64, TK> stg;
@@ -1080,6 +1111,7 @@ hipError_t launch_window_scores(const WsArgs& a, const WsPlan& plan, hipStream_t
   p.rows_total = a.B * a.Hkv * plan.Rpad;
   p.row0 = 0;
   p.accumulate = 0;
+  p.lse_from_part = 0;
   p.c = kLog2e / sqrtf((float)a.D);
   const int G = a.H / a.Hkv;
   p.out_scale = a.reduce ? 1.0f : 1.0f / (float)(G * a.w);
@@ -1125,8 +1157,12 @@ hipError_t launch_window_scores(const WsArgs& a, const WsPlan& plan, hipStream_t
     p.row0 = c * rows_per_launch;
     run(false);
   }
-  ws_merge_kernel<<<(p.rows_total * kMergeLanes + 255) / 256, 256, 0, st>>>(p.part, p.lse, p.rows_total, plan.Rpad,
-                                                                            plan.R, plan.nchunks);
+  // the scores passes merge the row statistics themselves; the stored-logits
+  // path's reduction kernel reads the merged normalisers
+  p.lse_from_part = plan.store ? 0 : 1;
+  if (plan.store)
+    ws_merge_kernel<<<(p.rows_total * kMergeLanes + 255) / 256, 256, 0, st>>>(p.part, p.lse, p.rows_total,
+                                                                              plan.Rpad, plan.R, plan.nchunks);
   const float scale_all = 1.0f / (float)(a.H * a.w);
   if (plan.store) {
     const dim3 g2((a.S + 255) / 256, a.reduce ? 1 : a.Hkv, a.B);
