@@ -491,18 +491,224 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
   }
 }
 
-template <typename T, int D, int NW, bool SHORT>
-__global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
-  using G_ = TileGeom<T, D>;
+// ---------------------------------------------------------------------------
+// ThinK with at most 64 of 128 bf16 key channels kept: the passes contract on
+// the kept channels only.  K tiles are staged as usual (coalesced 16-byte
+// loads) into a two-tile ring of full rows; one tile later every thread builds
+// a 16-byte unit of a compacted row (8 kept channels, 2-byte LDS reads) into the
+// three-tile ring the MFMAs read, 64 channels per key.  The query rows are
+// compacted in the same channel order.
+// ---------------------------------------------------------------------------
+
+// Byte offsets, within a 128-channel bf16 row, of the 8 kept channels that make
+// up this thread's 16-byte unit of a compacted row (unit tid % 8).
+struct ChOff {
+  int off[8];
+};
+
+// The kept channels in ascending order (from the keep mask, so a repeated entry
+// counts once), padded with channel 0 up to 64; returns how many are kept.  The
+// list must have been zeroed before build_keep's first barrier.
+__device__ inline int kept_channel_list(uint16_t* lds_ch, const uint32_t* keep, int tid) {
+  if (tid < 128) {
+    const int wd = tid >> 5, b = tid & 31;
+    if ((keep[wd] >> b) & 1u) {
+      int rank = __popc(keep[wd] & ((1u << b) - 1u));
+      for (int i = 0; i < wd; ++i) rank += __popc(keep[i]);
+      if (rank < 64) lds_ch[rank] = (uint16_t)tid;
+    }
+  }
+  __syncthreads();
+  return __popc(keep[0]) + __popc(keep[1]) + __popc(keep[2]) + __popc(keep[3]);
+}
+
+// Query fragments of the 32 rows rowblk .. rowblk+31 of (b, g) on the kept
+// channels: the rows go through the wave's LDS slot as in load_query_rows, and
+// compacted channel i of a row is its channel lds_ch[i] (zero past n_kept).
+__device__ inline void load_query_rows_kept(Frag<__bf16, 64>& qf, const WsParams& p, size_t bg, int rowblk, int lane,
+                                            int half, const uint16_t* lds_ch, int n_kept, unsigned char* slot) {
+  using GL = TileGeom<__bf16, 128>;
+  constexpr int UPL = 32 * GL::ROWB / 16 / 64;
+  const unsigned char* src =
+      reinterpret_cast<const unsigned char*>(p.q) + (bg * p.R + (size_t)rowblk) * (size_t)GL::ROWB;
+  u32x4_t d[UPL];
+#pragma unroll
+  for (int u = 0; u < UPL; ++u) {
+    const int off = u * 1024 + lane * 16;
+    d[u] = (rowblk + off / GL::ROWB < p.R) ? *reinterpret_cast<const u32x4_t*>(src + off) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int u = 0; u < UPL; ++u) {
+    const int off = u * 1024 + lane * 16;
+    *reinterpret_cast<u32x4_t*>(slot + (off / GL::ROWB) * GL::LSTRIDE + off % GL::ROWB) = d[u];
+  }
+  __builtin_amdgcn_wave_barrier();
+  const unsigned char* row = slot + (lane & 31) * GL::LSTRIDE;
+  uint32_t w[16];  // this lane's compacted channels half*32 .. half*32+31, two per word
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int i0 = half * 32 + 2 * j, i1 = i0 + 1;
+    const uint32_t lo = i0 < n_kept ? *reinterpret_cast<const uint16_t*>(row + 2 * lds_ch[i0]) : 0u;
+    const uint32_t hi = i1 < n_kept ? *reinterpret_cast<const uint16_t*>(row + 2 * lds_ch[i1]) : 0u;
+    w[j] = lo | (hi << 16);
+  }
+  __builtin_amdgcn_wave_barrier();
+  static_assert(sizeof(qf.u) == sizeof(w), "32 bf16 per lane");
+  __builtin_memcpy(&qf.u[0], w, sizeof(w));
+}
+
+constexpr int kRawStride = TileGeom<__bf16, 128>::LSTRIDE;  // full 128-channel rows
+constexpr int kKeptStride = TileGeom<__bf16, 64>::LSTRIDE;  // compacted 64-channel rows
+
+// Compact one staged tile: this thread's units (key u/8, unit u%8) of the
+// 64-key tile, and the tile's validity bytes.
+template <int NT>
+__device__ inline void gather_kept_tile(const unsigned char* raw, const uint8_t* raw_v, unsigned char* kept,
+                                        uint8_t* kept_v, int tid, const ChOff& ch, bool has_valid) {
+  constexpr int UPT = 64 * 8 / NT;
+  static_assert(UPT * NT == 64 * 8 && NT % 8 == 0, "units split evenly; a thread keeps its unit column");
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT;
+    const unsigned char* r = raw + (u >> 3) * kRawStride;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = *reinterpret_cast<const uint16_t*>(r + ch.off[2 * q]);
+      const uint32_t hi = *reinterpret_cast<const uint16_t*>(r + ch.off[2 * q + 1]);
+      w[q] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(kept + (u >> 3) * kKeptStride + (u & 7) * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+  if (has_valid && tid < 64) kept_v[tid] = raw_v[tid];
+}
+
+// The stream skeleton of stream_blocks on compacted keys: staged tiles go to
+// the two-slot ring of full rows one tile earlier, and at the end of tile t
+// the staged tile t+2 is compacted into the ring slot the MFMAs read, behind
+// the same barrier (so the pipeline takes one more tile of staging ahead).
+template <int NW, bool SHORT, typename Mma, typename Epi, typename Post>
+__device__ inline void stream_blocks_kept(const unsigned char* kbase, const uint8_t* vrow, int key0, int key1,
+                                          int ntiles, bool has_valid, int tid, int col, int half, int S, int w,
+                                          int causal, unsigned char (*lds_raw)[64 * kRawStride],
+                                          uint8_t (*lds_rv)[64], unsigned char (*lds_k)[64 * kKeptStride],
+                                          uint8_t (*lds_v)[64], const ChOff& ch, Mma mfma, Epi epi, Post post) {
+  using T = __bf16;
+  constexpr int D = 64;
   constexpr int NT = NW * 64;
-  constexpr int TK = StreamTK<T, D, NW>::value;
+  constexpr int TK = 64;
+  static_assert(StreamTK<T, 128, NW>::value == TK && StreamTK<T, D, NW>::value == TK, "64-key tiles");
+  constexpr int NSTG = StreamNSTG<T, 128, NW, SHORT>::value;
+  constexpr int KB = TK / 32;
+  using G_ = TileGeom<T, D>;
+  using Stg = Stager<T, 128, NT, TK>;
+  static_assert(NSTG >= 1 && NSTG <= 3, "one to three staging sets");
+
+  Stg s0, s1, s2;
+  {
+    // staged tiles 0 and 1 compacted behind the first barrier; staged tile 2
+    // stored behind the second (the gather of tile 0 is still reading its slot)
+    Stg p0, p1, p2;
+    p0.load(kbase, vrow, key0, key1, tid);
+    p1.load(kbase, vrow, key0 + TK, key1, tid);
+    __builtin_amdgcn_sched_barrier(0);
+    p2.load(kbase, vrow, key0 + 2 * TK, key1, tid);
+    s0.load(kbase, vrow, key0 + 3 * TK, key1, tid);
+    if (ntiles > 0) p0.store(lds_raw[0], lds_rv[0], tid, has_valid);
+    if (ntiles > 1) p1.store(lds_raw[1], lds_rv[1], tid, has_valid);
+    __syncthreads();
+    if (ntiles > 0) gather_kept_tile<NT>(lds_raw[0], lds_rv[0], lds_k[0], lds_v[0], tid, ch, has_valid);
+    if (ntiles > 1) gather_kept_tile<NT>(lds_raw[1], lds_rv[1], lds_k[1], lds_v[1], tid, ch, has_valid);
+    __syncthreads();
+    if (ntiles > 2) p2.store(lds_raw[0], lds_rv[0], tid, has_valid);
+  }
+  __syncthreads();
+  if (ntiles <= 0) return;
+  if constexpr (NSTG > 1) s1.load(kbase, vrow, key0 + 4 * TK, key1, tid);
+  if constexpr (NSTG > 2) s2.load(kbase, vrow, key0 + 5 * TK, key1, tid);
+
+  Frag<T, D> kf[2];
+  read_frag<T, D>(kf[0], lds_k[0], col, half);
+  read_frag<T, D>(kf[1], lds_k[0], 32 + col, half);
+  f32x16_t acc = mfma(kf[0]);
+
+  // tile t; `st` holds staged tile t+3 and is refilled with tile t+3+NSTG
+  auto tile = [&](int t, Stg& st, auto full_tag) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int base = key0 + t * TK;
+    const bool masked = has_valid || (base + TK > S) || (causal && base + TK - 1 > S - w);
+    const unsigned char* next_tile = lds_k[(t + 1) % 3];
+    const unsigned char* this_tile = lds_k[t % 3];
+
+    auto run = [&](auto masked_tag, auto last_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      constexpr bool LAST = decltype(last_tag)::value;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int cur = kb & 1;
+        if (!LAST || kb + 2 < KB) {
+          const unsigned char* src = (kb + 2 < KB) ? this_tile : next_tile;
+          read_frag<T, D>(kf[cur], src, ((kb + 2) % KB) * 32 + col, half);
+        }
+        f32x16_t nxt;
+        if (!LAST || kb + 1 < KB) nxt = mfma(kf[cur ^ 1]);
+        epi(acc, t, kb, MASKED);
+        if constexpr (!MASKED) interleave_hint<G_::NSTEP, 6>();
+        __builtin_amdgcn_sched_barrier(0);
+        if (!LAST || kb + 1 < KB) acc = nxt;
+      }
+    };
+    if (t + 1 < ntiles) {
+      if (masked) run(bool_t<true>(), bool_t<false>());
+      else run(bool_t<false>(), bool_t<false>());
+    } else {
+      if (masked) run(bool_t<true>(), bool_t<true>());
+      else run(bool_t<false>(), bool_t<true>());
+    }
+
+    if (FULL || t + 3 < ntiles) st.store(lds_raw[(t + 1) & 1], lds_rv[(t + 1) & 1], tid, has_valid);
+    if (FULL || t + 2 < ntiles)
+      gather_kept_tile<NT>(lds_raw[t & 1], lds_rv[t & 1], lds_k[(t + 2) % 3], lds_v[(t + 2) % 3], tid, ch,
+                           has_valid);
+    __syncthreads();
+    post(t);
+    st.load(kbase, vrow, base + (3 + NSTG) * TK, key1, tid);  // past the chunk: an empty descriptor, nothing read
+  };
+  int t = 0;
+  for (; t + 2 * NSTG + 2 < ntiles; t += NSTG) {  // steady state
+    tile(t, s0, bool_t<true>());
+    if constexpr (NSTG > 1) tile(t + 1, s1, bool_t<true>());
+    if constexpr (NSTG > 2) tile(t + 2, s2, bool_t<true>());
+  }
+  for (; t < ntiles; t += NSTG) {
+    tile(t, s0, bool_t<false>());
+    if constexpr (NSTG > 1)
+      if (t + 1 < ntiles) tile(t + 1, s1, bool_t<false>());
+    if constexpr (NSTG > 2)
+      if (t + 2 < ntiles) tile(t + 2, s2, bool_t<false>());
+  }
+}
+
+// GATHER (bf16, D = 128, at most 64 kept channels): the contraction runs on the
+// kept channels only (DC = 64) through stream_blocks_kept.
+template <typename T, int D, int NW, bool SHORT, bool GATHER>
+__global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
+  static_assert(!GATHER || (sizeof(T) == 2 && D == 128), "compaction of 128 bf16 channels to 64");
+  constexpr int DC = GATHER ? 64 : D;
+  using GL = TileGeom<T, D>;   // stored rows
+  using G_ = TileGeom<T, DC>;  // the ring the MFMAs read
+  constexpr int NT = NW * 64;
+  constexpr int TK = StreamTK<T, DC, NW>::value;
 
   __shared__ __attribute__((aligned(16))) unsigned char lds_k[3][TK * G_::LSTRIDE];
   __shared__ __attribute__((aligned(16))) uint8_t lds_valid[3][TK];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[GATHER ? 2 : 1][GATHER ? 64 * kRawStride : 16];
+  __shared__ uint8_t lds_rv[GATHER ? 2 : 1][64];
   // query staging slots (bf16 only: fp32 rows would not fit next to the ring)
   constexpr bool QLDS = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_q[QLDS ? NW : 1][QLDS ? 32 * G_::LSTRIDE : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_q[QLDS ? NW : 1][QLDS ? 32 * GL::LSTRIDE : 16];
   __shared__ uint32_t lds_keep[D / 32];
+  __shared__ uint16_t lds_ch[GATHER ? 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
   const int chunk = blockIdx.x;
@@ -513,23 +719,38 @@ __global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
   const bool has_valid = p.valid != nullptr;
   const uint8_t* vrow = has_valid ? p.valid + bg * p.S : nullptr;
 
+  if constexpr (GATHER)
+    if (tid < 64) lds_ch[tid] = 0;
   const uint32_t* keep = build_keep<D, NT>(lds_keep, p, bg, tid);
   const int r = p.row0 + wave * 32 + col;  // this lane's query row
-  Frag<T, D> qf;
-  if constexpr (QLDS) load_query_rows<T, D>(qf, p, bg, p.row0 + wave * 32, lane, half, keep, lds_q[wave]);
-  else load_query<T, D>(qf, p, bg, r, half, keep);
+  Frag<T, DC> qf;
+  ChOff choff;
+  if constexpr (GATHER) {
+    const int n_kept = kept_channel_list(lds_ch, keep, tid);
+    load_query_rows_kept(qf, p, bg, p.row0 + wave * 32, lane, half, lds_ch, n_kept, lds_q[wave]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) choff.off[e] = 2 * lds_ch[(tid & 7) * 8 + e];
+  } else if constexpr (QLDS) {
+    load_query_rows<T, D>(qf, p, bg, p.row0 + wave * 32, lane, half, keep, lds_q[wave]);
+  } else {
+    load_query<T, D>(qf, p, bg, r, half, keep);
+  }
   int lim = p.S - 1;
   if (p.causal && r < p.R) lim = min(p.S - 1, p.S - p.w + r % p.w);
   float m_run = kNegInf, z_run = 0.0f;
 
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
-  auto mfma = [&](const Frag<T, D>& kf) { return mma_block<T, D>(kf, qf); };
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * GL::ROWB;
+  auto mfma = [&](const Frag<T, DC>& kf) { return mma_block<T, DC>(kf, qf); };
   auto epi = [&](f32x16_t& a, int t, int kb, bool masked) {
     if (masked) mask_stats(a, key0 + t * TK + kb * 32, lim, &lds_valid[t % 3][kb * 32], has_valid, half);
     fold_stats_ref(a, p.c, m_run, z_run);
   };
-  stream_blocks<T, D, NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal, lds_k,
-                          lds_valid, mfma, epi, [](int) {});
+  if constexpr (GATHER)
+    stream_blocks_kept<NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal,
+                                  lds_raw, lds_rv, lds_k, lds_valid, choff, mfma, epi, [](int) {});
+  else
+    stream_blocks<T, D, NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal,
+                                   lds_k, lds_valid, mfma, epi, [](int) {});
 
   const float m2 = __shfl_xor(m_run, 32);
   const float z2 = __shfl_xor(z_run, 32);
@@ -537,19 +758,25 @@ __global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
   if (half == 0) p.part[(size_t)chunk * p.rows_total + bg * p.Rpad + r] = make_float2(m_run, z_run);
 }
 
-template <typename T, int D, int NW, bool SHORT>
+template <typename T, int D, int NW, bool SHORT, bool GATHER>
 __global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
-  using G_ = TileGeom<T, D>;
+  static_assert(!GATHER || (sizeof(T) == 2 && D == 128), "compaction of 128 bf16 channels to 64");
+  constexpr int DC = GATHER ? 64 : D;
+  using GL = TileGeom<T, D>;   // stored rows
+  using G_ = TileGeom<T, DC>;  // the ring the MFMAs read
   constexpr int NT = NW * 64;
-  constexpr int TK = StreamTK<T, D, NW>::value;
+  constexpr int TK = StreamTK<T, DC, NW>::value;
 
   __shared__ __attribute__((aligned(16))) unsigned char lds_k[3][TK * G_::LSTRIDE];
   __shared__ __attribute__((aligned(16))) uint8_t lds_valid[3][TK];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[GATHER ? 2 : 1][GATHER ? 64 * kRawStride : 16];
+  __shared__ uint8_t lds_rv[GATHER ? 2 : 1][64];
   __shared__ float lds_red[3][2 * NW][TK];
   // query staging slots (bf16 only: fp32 rows would not fit next to the ring)
   constexpr bool QLDS = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_q[QLDS ? NW : 1][QLDS ? 32 * G_::LSTRIDE : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_q[QLDS ? NW : 1][QLDS ? 32 * GL::LSTRIDE : 16];
   __shared__ uint32_t lds_keep[D / 32];
+  __shared__ uint16_t lds_ch[GATHER ? 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
   const int chunk = blockIdx.x;
@@ -560,17 +787,28 @@ __global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
   const bool has_valid = p.valid != nullptr;
   const uint8_t* vrow = has_valid ? p.valid + bg * p.S : nullptr;
 
+  if constexpr (GATHER)
+    if (tid < 64) lds_ch[tid] = 0;
   const uint32_t* keep = build_keep<D, NT>(lds_keep, p, bg, tid);
   const int rowblk = p.row0 + wave * 32;
-  Frag<T, D> qf;
-  if constexpr (QLDS) load_query_rows<T, D>(qf, p, bg, rowblk, lane, half, keep, lds_q[wave]);
-  else load_query<T, D>(qf, p, bg, rowblk + col, half, keep);
+  Frag<T, DC> qf;
+  ChOff choff;
+  if constexpr (GATHER) {
+    const int n_kept = kept_channel_list(lds_ch, keep, tid);
+    load_query_rows_kept(qf, p, bg, rowblk, lane, half, lds_ch, n_kept, lds_q[wave]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) choff.off[e] = 2 * lds_ch[(tid & 7) * 8 + e];
+  } else if constexpr (QLDS) {
+    load_query_rows<T, D>(qf, p, bg, rowblk, lane, half, keep, lds_q[wave]);
+  } else {
+    load_query<T, D>(qf, p, bg, rowblk + col, half, keep);
+  }
   float nb[16];
   if (p.lse_from_part) neg_lse_from_part(nb, p, bg, rowblk, lane, half);
   else load_neg_lse(nb, p, bg, rowblk, half);
 
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * G_::ROWB;
-  auto mfma = [&](const Frag<T, D>& kf) { return mma_block<T, D>(qf, kf); };
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + bg * (size_t)p.S * GL::ROWB;
+  auto mfma = [&](const Frag<T, DC>& kf) { return mma_block<T, DC>(qf, kf); };
   auto epi = [&](f32x16_t& a, int t, int kb, bool masked) {
     float cs[4];
     if (masked) {
@@ -608,8 +846,12 @@ __global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
       }
     }
   };
-  stream_blocks<T, D, NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal, lds_k,
-                          lds_valid, mfma, epi, post);
+  if constexpr (GATHER)
+    stream_blocks_kept<NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal,
+                                  lds_raw, lds_rv, lds_k, lds_valid, choff, mfma, epi, post);
+  else
+    stream_blocks<T, D, NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal,
+                                   lds_k, lds_valid, mfma, epi, post);
 }
 
 // ---------------------------------------------------------------------------
@@ -1061,7 +1303,9 @@ __global__ void ws_all_heads_kernel(float* __restrict__ scores, int Hkv, int S, 
   for (int g = 0; g < Hkv; ++g) scores[(b * Hkv + g) * S + j] = s;
 }
 
-template <typename T, int D>
+// GATHER: the stream kernels on ThinK's kept channels (bf16, D = 128, at most 64
+// kept); the one-wave kernels keep the masked 128-channel contraction.
+template <typename T, int D, bool GATHER = false>
 void launch_pass(const WsParams& p, const WsPlan& plan, dim3 grid, hipStream_t st, bool scores_pass) {
   switch (plan.NW) {
     case 1:
@@ -1070,21 +1314,21 @@ void launch_pass(const WsParams& p, const WsPlan& plan, dim3 grid, hipStream_t s
       else ws_stats_wave_kernel<T, D, false><<<grid, 64, 0, st>>>(p);
       break;
     case 2:
-      if (scores_pass) ws_scores_stream_kernel<T, D, 2, false><<<grid, 128, 0, st>>>(p);
-      else ws_stats_stream_kernel<T, D, 2, false><<<grid, 128, 0, st>>>(p);
+      if (scores_pass) ws_scores_stream_kernel<T, D, 2, false, GATHER><<<grid, 128, 0, st>>>(p);
+      else ws_stats_stream_kernel<T, D, 2, false, GATHER><<<grid, 128, 0, st>>>(p);
       break;
     case 4:
-      if (scores_pass) ws_scores_stream_kernel<T, D, 4, false><<<grid, 256, 0, st>>>(p);
-      else ws_stats_stream_kernel<T, D, 4, false><<<grid, 256, 0, st>>>(p);
+      if (scores_pass) ws_scores_stream_kernel<T, D, 4, false, GATHER><<<grid, 256, 0, st>>>(p);
+      else ws_stats_stream_kernel<T, D, 4, false, GATHER><<<grid, 256, 0, st>>>(p);
       break;
     default:
       // eight waves: the staging depth follows the number of tiles per workgroup
       if (plan.CH <= kShortChunkTiles * StreamTK<T, D, 8>::value) {
-        if (scores_pass) ws_scores_stream_kernel<T, D, 8, true><<<grid, 512, 0, st>>>(p);
-        else ws_stats_stream_kernel<T, D, 8, true><<<grid, 512, 0, st>>>(p);
+        if (scores_pass) ws_scores_stream_kernel<T, D, 8, true, GATHER><<<grid, 512, 0, st>>>(p);
+        else ws_stats_stream_kernel<T, D, 8, true, GATHER><<<grid, 512, 0, st>>>(p);
       } else {
-        if (scores_pass) ws_scores_stream_kernel<T, D, 8, false><<<grid, 512, 0, st>>>(p);
-        else ws_stats_stream_kernel<T, D, 8, false><<<grid, 512, 0, st>>>(p);
+        if (scores_pass) ws_scores_stream_kernel<T, D, 8, false, GATHER><<<grid, 512, 0, st>>>(p);
+        else ws_stats_stream_kernel<T, D, 8, false, GATHER><<<grid, 512, 0, st>>>(p);
       }
       break;
   }
@@ -1123,8 +1367,11 @@ hipError_t launch_window_scores(const WsArgs& a, const WsPlan& plan, hipStream_t
 
   const dim3 grid(plan.nchunks, a.Hkv, a.B);
   const bool bf = a.bf16 != 0;
+  // ThinK with at most 64 kept channels: contract on the kept channels only
+  const bool gather = bf && a.D == 128 && a.chan_idx != nullptr && a.d_keep <= 64;
   auto run = [&](bool scores_pass) {
-    if (bf && a.D == 128) launch_pass<__bf16, 128>(p, plan, grid, st, scores_pass);
+    if (gather) launch_pass<__bf16, 128, true>(p, plan, grid, st, scores_pass);
+    else if (bf && a.D == 128) launch_pass<__bf16, 128>(p, plan, grid, st, scores_pass);
     else if (bf && a.D == 64) launch_pass<__bf16, 64>(p, plan, grid, st, scores_pass);
     else if (!bf && a.D == 128) launch_pass<float, 128>(p, plan, grid, st, scores_pass);
     else launch_pass<float, 64>(p, plan, grid, st, scores_pass);
