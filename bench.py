@@ -277,7 +277,7 @@ def wl_snapkv_32k(c: Ctx, then_think: bool = False) -> dict:
         return [t.clone() for t in (layers[0]["scores"], layers[0]["idx"], layers[0]["k_out"], layers[-1]["idx"])]
     return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes, compute=compute,
                 check_outputs=check_outputs,
-                kernel=("kvc_window_scores (pass 1 + merge + pass 2)", [ly["kcall"] for ly in layers],
+                kernel=("kvc_window_scores (pass 1 + pass 2)", [ly["kcall"] for ly in layers],
                         k_bytes + q_bytes + s_bytes, traffic),
                 kernel_alone=[ly["kcall1"] for ly in layers] if conc != 1 else None,
                 cpu=cpu, metric=(f"KV tokens scored+pruned/s per layer ({cfg.name}, then ThinK on the kept keys)"
@@ -428,7 +428,7 @@ def wl_think_128k(c: Ctx, compress: bool = False) -> dict:
                 "kind": "oracle", "sample": f"{n} KV heads (of {Hkv} per layer) of layer 0, S={S}, fp64 numpy "
                                             f"oracle (channels, scores, top-k, gather), {el:.1f} s"}
     return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes,
-                kernel=("kvc_window_scores with 64 of 128 key channels (pass 1 + merge + pass 2)",
+                kernel=("kvc_window_scores with 64 of 128 key channels (pass 1 + pass 2)",
                         [ly["kcall"] for ly in layers], k_bytes + q_bytes + s_bytes, None),
                 kernel_alone=[ly["kcall1"] for ly in layers] if conc != 1 else None,
                 cpu=cpu, metric=f"KV tokens scored+pruned/s per layer ({cfg.name}{'_kc' if compress else ''})",
