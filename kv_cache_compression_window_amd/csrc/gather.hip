@@ -4,9 +4,9 @@
 // +0.0, and v_out likewise without channel pruning.  Source: "Add ThinK_Press"
 // (kvpress PR 18), option 3a: put zeros in the key cache.
 //
-// One thread moves one 16-byte unit of one row of K and the same unit of V
-// (V only when k is NULL: the kept-channel key cache is then written by the
-// channel gathers).
+// A thread moves one 16-byte unit (four in small gathers) of the kept rows of K
+// and the same units of V (V only when k is NULL: the kept-channel key cache is
+// then written by the channel gathers).
 // Consecutive threads cover consecutive units of a row, so every kept row is
 // read as whole 128-byte lines and the output is written densely.  Output
 // stores are non-temporal: the compacted cache is not read again by this layer.
@@ -19,7 +19,12 @@ namespace {
 
 constexpr int NTH = 256;
 
-template <int ESZ, int D>
+// UT 16-byte units per thread (UT rows' worth of the thread's unit column):
+// every index is requested first, then every K and V load, then the stores, so a
+// thread has 2*UT loads in flight.  Small gathers take UT = 4 (a quarter of the
+// workgroups, which then share the GPU better with other streams' kernels);
+// large ones UT = 1.
+template <int ESZ, int D, int UT>
 __global__ __launch_bounds__(NTH) void gather_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                      const int32_t* __restrict__ idx, int S, int n_keep,
                                                      const int32_t* __restrict__ chan_idx, int d_keep,
@@ -27,6 +32,7 @@ __global__ __launch_bounds__(NTH) void gather_kernel(const uint4* __restrict__ k
                                                      int Hkv) {
   constexpr int UPR = D * ESZ / 16;  // 16-byte units per row
   constexpr int EPU = 16 / ESZ;      // elements per unit
+  static_assert(NTH % UPR == 0, "a thread keeps its unit column");
   __shared__ uint32_t keep[D / 32];
   const size_t bg = (size_t)blockIdx.z * Hkv + blockIdx.y;
   const int tid = threadIdx.x;
@@ -39,52 +45,76 @@ __global__ __launch_bounds__(NTH) void gather_kernel(const uint4* __restrict__ k
     }
     __syncthreads();
   }
-  const long long u = (long long)blockIdx.x * NTH + tid;
-  const int r = (int)(u / UPR);
-  const int cu = (int)(u % UPR);
-  if (r >= n_keep) return;
-  // indices are caller data: clamp so that a bad index cannot read out of bounds
-  const int src = min(max(idx[bg * n_keep + r], 0), S - 1);
-  const size_t in_off = (bg * S + src) * UPR + cu;
-  const size_t out_off = (bg * n_keep + r) * UPR + cu;
-  if (v) {
-    const uint4 vv = v[in_off];
-    __builtin_nontemporal_store(vv.x, &v_out[out_off].x);
-    __builtin_nontemporal_store(vv.y, &v_out[out_off].y);
-    __builtin_nontemporal_store(vv.z, &v_out[out_off].z);
-    __builtin_nontemporal_store(vv.w, &v_out[out_off].w);
-  }
-  if (!k) return;  // V only
-  uint4 kv = k[in_off];
-  if (chan_idx) {
-    uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
+  const int cu = tid % UPR;
+  size_t in_off[UT], out_off[UT];
+  bool ok[UT];
 #pragma unroll
-    for (int e = 0; e < EPU; ++e) {
-      const int d = cu * EPU + e;
-      if (!((keep[d >> 5] >> (d & 31)) & 1u)) {
-        if constexpr (ESZ == 4) {
-          w[e] = 0u;
-        } else {
-          w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+  for (int j = 0; j < UT; ++j) {
+    const long long u = ((long long)blockIdx.x * UT + j) * NTH + tid;
+    const int r = (int)(u / UPR);
+    ok[j] = r < n_keep;
+    // indices are caller data: clamp so that a bad index cannot read out of bounds
+    const int src = ok[j] ? min(max(idx[bg * n_keep + r], 0), S - 1) : 0;
+    in_off[j] = (bg * S + src) * UPR + cu;
+    out_off[j] = (bg * n_keep + (ok[j] ? r : 0)) * UPR + cu;
+  }
+  uint4 vv[UT], kk[UT];
+#pragma unroll
+  for (int j = 0; j < UT; ++j) {
+    if (v && ok[j]) vv[j] = v[in_off[j]];
+    if (k && ok[j]) kk[j] = k[in_off[j]];
+  }
+#pragma unroll
+  for (int j = 0; j < UT; ++j) {
+    if (!ok[j]) continue;
+    if (v) {
+      __builtin_nontemporal_store(vv[j].x, &v_out[out_off[j]].x);
+      __builtin_nontemporal_store(vv[j].y, &v_out[out_off[j]].y);
+      __builtin_nontemporal_store(vv[j].z, &v_out[out_off[j]].z);
+      __builtin_nontemporal_store(vv[j].w, &v_out[out_off[j]].w);
+    }
+    if (!k) continue;  // V only
+    uint4 kv = kk[j];
+    if (chan_idx) {
+      uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        const int d = cu * EPU + e;
+        if (!((keep[d >> 5] >> (d & 31)) & 1u)) {
+          if constexpr (ESZ == 4) {
+            w[e] = 0u;
+          } else {
+            w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+          }
         }
       }
+      kv = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    kv = make_uint4(w[0], w[1], w[2], w[3]);
+    __builtin_nontemporal_store(kv.x, &k_out[out_off[j]].x);
+    __builtin_nontemporal_store(kv.y, &k_out[out_off[j]].y);
+    __builtin_nontemporal_store(kv.z, &k_out[out_off[j]].z);
+    __builtin_nontemporal_store(kv.w, &k_out[out_off[j]].w);
   }
-  __builtin_nontemporal_store(kv.x, &k_out[out_off].x);
-  __builtin_nontemporal_store(kv.y, &k_out[out_off].y);
-  __builtin_nontemporal_store(kv.z, &k_out[out_off].z);
-  __builtin_nontemporal_store(kv.w, &k_out[out_off].w);
 }
+
+// Gathers of at most this many 16-byte units per call take four units per thread.
+constexpr long long kSmallGatherUnits = 1LL << 20;
 
 template <int ESZ, int D>
 void run(const GatherArgs& a, hipStream_t st) {
   constexpr int UPR = D * ESZ / 16;
   const long long units = (long long)a.n_keep * UPR;
-  const dim3 grid((unsigned)((units + NTH - 1) / NTH), a.Hkv, a.B);
-  gather_kernel<ESZ, D><<<grid, NTH, 0, st>>>(
-      static_cast<const uint4*>(a.k), static_cast<const uint4*>(a.v), a.idx, a.S, a.n_keep, a.chan_idx, a.d_keep,
-      static_cast<uint4*>(a.k_out), static_cast<uint4*>(a.v_out), a.Hkv);
+  const auto* k = static_cast<const uint4*>(a.k);
+  const auto* v = static_cast<const uint4*>(a.v);
+  auto* ko = static_cast<uint4*>(a.k_out);
+  auto* vo = static_cast<uint4*>(a.v_out);
+  if (units * a.Hkv * a.B <= kSmallGatherUnits) {
+    const dim3 grid((unsigned)((units + 4 * NTH - 1) / (4 * NTH)), a.Hkv, a.B);
+    gather_kernel<ESZ, D, 4><<<grid, NTH, 0, st>>>(k, v, a.idx, a.S, a.n_keep, a.chan_idx, a.d_keep, ko, vo, a.Hkv);
+  } else {
+    const dim3 grid((unsigned)((units + NTH - 1) / NTH), a.Hkv, a.B);
+    gather_kernel<ESZ, D, 1><<<grid, NTH, 0, st>>>(k, v, a.idx, a.S, a.n_keep, a.chan_idx, a.d_keep, ko, vo, a.Hkv);
+  }
 }
 
 }  // namespace
