@@ -4,7 +4,7 @@
 // +0.0, and v_out likewise without channel pruning.  Source: "Add ThinK_Press"
 // (kvpress PR 18), option 3a: put zeros in the key cache.
 //
-// A thread moves one 16-byte unit (four in small gathers) of the kept rows of K
+// A thread moves one 16-byte unit (four in mid-sized gathers) of the kept rows of K
 // and the same units of V (V only when k is NULL: the kept-channel key cache is
 // then written by the channel gathers).
 // Consecutive threads cover consecutive units of a row, so every kept row is
@@ -21,9 +21,9 @@ constexpr int NTH = 256;
 
 // UT 16-byte units per thread (UT rows' worth of the thread's unit column):
 // every index is requested first, then every K and V load, then the stores, so a
-// thread has 2*UT loads in flight.  Small gathers take UT = 4 (a quarter of the
-// workgroups, which then share the GPU better with other streams' kernels);
-// large ones UT = 1.
+// thread has 2*UT loads in flight.  Mid-sized gathers take UT = 4 (a quarter of
+// the workgroups, which then share the GPU better with other streams' kernels);
+// large and tiny ones UT = 1.
 template <int ESZ, int D, int UT>
 __global__ __launch_bounds__(NTH) void gather_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                      const int32_t* __restrict__ idx, int S, int n_keep,
@@ -97,8 +97,10 @@ __global__ __launch_bounds__(NTH) void gather_kernel(const uint4* __restrict__ k
   }
 }
 
-// Gathers of at most this many 16-byte units per call take four units per thread.
-constexpr long long kSmallGatherUnits = 1LL << 20;
+// Gathers of 2^18 to 2^20 16-byte units per call take four units per thread
+// (still 256 or more workgroups); smaller ones keep one, for parallelism.
+constexpr long long kFourUnitsMin = 1LL << 18;
+constexpr long long kFourUnitsMax = 1LL << 20;
 
 template <int ESZ, int D>
 void run(const GatherArgs& a, hipStream_t st) {
@@ -108,7 +110,8 @@ void run(const GatherArgs& a, hipStream_t st) {
   const auto* v = static_cast<const uint4*>(a.v);
   auto* ko = static_cast<uint4*>(a.k_out);
   auto* vo = static_cast<uint4*>(a.v_out);
-  if (units * a.Hkv * a.B <= kSmallGatherUnits) {
+  const long long total = units * a.Hkv * a.B;
+  if (total >= kFourUnitsMin && total <= kFourUnitsMax) {
     const dim3 grid((unsigned)((units + 4 * NTH - 1) / (4 * NTH)), a.Hkv, a.B);
     gather_kernel<ESZ, D, 4><<<grid, NTH, 0, st>>>(k, v, a.idx, a.S, a.n_keep, a.chan_idx, a.d_keep, ko, vo, a.Hkv);
   } else {
