@@ -41,7 +41,8 @@ constexpr int NTH = 1024;  // threads per row
 constexpr int NWAVE = NTH / 64;
 constexpr int DBITS = 11;  // digit width
 constexpr int NBIN = 1 << DBITS;
-constexpr int NCOPY = 8;   // interleaved histogram copies
+constexpr int NCOPY = 2;   // interleaved copies of the first pass's histogram
+constexpr int kSplitCopies = 8;  // interleaved copies of the sliced kernels' histograms
 
 static_assert(NBIN == 2 * NTH, "each thread owns two bins when the threshold bin is searched");
 
@@ -52,26 +53,25 @@ static_assert(NBIN == 2 * NTH, "each thread owns two bins when the threshold bin
 __device__ inline int xpose_idx(int p) { return p + (p >> 5); }
 constexpr int kXposeWords = 33 * NTH;  // padded size of a 32-key-per-thread tile
 
+// The first pass's histogram has LDS of its own, so it is cleared while the keys
+// are loaded.  The hand-over area is free once the keys are in registers: the
+// later passes, which count few keys, have one-copy histograms at its end
+// (cleared after the first pass's counting), and the second pass lists the keys
+// it counts (those in the first pass's threshold bin) at its start; the third
+// pass reads that list instead of every key of the row.
 struct TopkShared {
-  union {
-    uint32_t hist[NBIN * NCOPY];
-    uint32_t xpose[kXposeWords];
-  };
+  uint32_t xpose[kXposeWords];
+  alignas(16) uint32_t hist[NBIN * NCOPY];
   alignas(16) uint32_t wave_tot[NWAVE];
+  alignas(16) uint32_t list_tot[NWAVE];
   uint32_t red_min[NWAVE], red_max[NWAVE];
   uint32_t bucket, krem, bcount;
-  uint32_t nlist;  // candidates collected by the second pass
 };
 
-// The passes after the first count few keys: each has its own one-copy
-// histogram at the end of the hand-over area, cleared with the first pass's, so
-// they start without a clear and a barrier.  The second pass also collects the
-// keys it counts (those in the first pass's threshold bin) into a list between
-// the first histogram and those; later passes read that list instead of every
-// key of the row.
 constexpr int kNarrowHist0 = kXposeWords - 2 * NBIN;  // second pass; the third at + NBIN
-constexpr int kListCap = kNarrowHist0 - NBIN * NCOPY;
+constexpr int kListCap = kNarrowHist0;
 static_assert(kListCap > 4 * NTH, "room for the candidate list");
+static_assert(NBIN * NCOPY == 4 * NTH && 2 * NBIN == 4 * NTH, "one 16-byte clear per thread per histogram set");
 
 // Inclusive prefix sum over the 64 lanes of a wave: DPP shifts within rows of
 // 16 lanes, then the broadcasts of lane 15 and lane 31 into the later rows.
@@ -98,8 +98,8 @@ __device__ inline uint32_t wave_max(uint32_t x) {
 }
 
 // Sum of the per-wave totals (already in LDS) of the waves before `wave`.
-__device__ inline uint32_t waves_before(const TopkShared& sh, int wave) {
-  const uint4* wt = reinterpret_cast<const uint4*>(sh.wave_tot);
+__device__ inline uint32_t waves_before(const uint32_t* tot, int wave) {
+  const uint4* wt = reinterpret_cast<const uint4*>(tot);
   uint32_t before = 0u;
 #pragma unroll
   for (int q = 0; q < NWAVE / 4; ++q) {
@@ -116,8 +116,8 @@ __device__ inline uint32_t block_exclusive_scan(TopkShared& sh, uint32_t x, int 
   const uint32_t winc = wave_inclusive_scan(x);
   if (lane == 63) sh.wave_tot[wave] = winc;
   __syncthreads();
-  const uint32_t r = waves_before(sh, wave) + winc - x;
-  *total = waves_before(sh, NWAVE);
+  const uint32_t r = waves_before(sh.wave_tot, wave) + winc - x;
+  *total = waves_before(sh.wave_tot, NWAVE);
   __syncthreads();
   return r;
 }
@@ -135,10 +135,10 @@ __device__ inline void find_bin(TopkShared& sh, const uint32_t* hist, uint32_t k
   const int b_hi = NBIN - 1 - 2 * tid, b_lo = b_hi - 1;
   uint32_t c_hi, c_lo;
   if (wide) {
-    const uint4* h = reinterpret_cast<const uint4*>(hist);
-    const uint4 h0 = h[b_hi * 2], h1 = h[b_hi * 2 + 1], h2 = h[b_lo * 2], h3 = h[b_lo * 2 + 1];
-    c_hi = h0.x + h0.y + h0.z + h0.w + h1.x + h1.y + h1.z + h1.w;
-    c_lo = h2.x + h2.y + h2.z + h2.w + h3.x + h3.y + h3.z + h3.w;
+    static_assert(NCOPY == 2, "two copies of bins b_lo (even) and b_hi in one 16-byte word");
+    const uint4 h = reinterpret_cast<const uint4*>(hist)[b_lo >> 1];
+    c_lo = h.x + h.y;
+    c_hi = h.z + h.w;
   } else {
     const uint2 h = reinterpret_cast<const uint2*>(hist)[b_lo >> 1];  // bins b_lo (even) and b_hi
     c_lo = h.x;
@@ -148,7 +148,7 @@ __device__ inline void find_bin(TopkShared& sh, const uint32_t* hist, uint32_t k
   const uint32_t winc = wave_inclusive_scan(local);
   if (lane == 63) sh.wave_tot[wave] = winc;
   __syncthreads();
-  const uint32_t incl = waves_before(sh, wave) + winc, excl = incl - local;
+  const uint32_t incl = waves_before(sh.wave_tot, wave) + winc, excl = incl - local;
   if (excl < krem && incl >= krem) {
     if (excl + c_hi >= krem) {
       sh.bucket = (uint32_t)b_hi;
@@ -217,9 +217,6 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
       kmax = max(kmax, key);
       sh.xpose[xpose_idx(p)] = key;
     }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) u[i] = sh.xpose[xpose_idx(tid * KPT + i)];
   } else {
     for (int t = 0; t < ntiles; ++t) {
       load_coalesced(t);
@@ -230,13 +227,19 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
       }
     }
   }
+  // one barrier for the hand-over, the key range and the first histogram's clear
   kmin = wave_min(kmin);
   kmax = wave_max(kmax);
   if (lane == 0) {
     sh.red_min[wave] = kmin;
     sh.red_max[wave] = kmax;
   }
+  reinterpret_cast<uint4*>(sh.hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
+  if constexpr (RESIDENT) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) u[i] = sh.xpose[xpose_idx(tid * KPT + i)];
+  }
   kmin = sh.red_min[0];
   kmax = sh.red_max[0];
 #pragma unroll
@@ -282,26 +285,19 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
   uint32_t prefix = 0u;                            // fixed high bits of rel(T)
   uint32_t krem = (uint32_t)kp;                    // still to take among the keys matching the prefix
   uint32_t last_count = (uint32_t)(ntiles * TILE);  // keys equal to T (all of them when npass == 0)
-  uint32_t* list = sh.xpose + NBIN * NCOPY;        // free during the passes
+  uint32_t* list = sh.xpose;  // free once the keys are in registers
   bool from_list = false;
+  int nlist = 0;
   for (int pass = 0; pass < npass; ++pass) {
     const int hi = L - DBITS * pass;       // bits [hi, 32) of rel are fixed
     const int shift = max(0, hi - DBITS);  // this digit is bits [shift, hi)
     const uint32_t fixed = hi >= 32 ? 0u : ~0u << hi;
     const bool wide = pass == 0;
+    const bool listing = RESIDENT && pass == 1;  // the second pass lists the keys it counts
     uint32_t* hist = wide ? sh.hist : sh.xpose + kNarrowHist0 + (pass - 1) * NBIN;
-    if (wide) {
-#pragma unroll
-      for (int j = 0; j < NBIN * NCOPY / 4 / NTH; ++j)
-        reinterpret_cast<uint4*>(sh.hist)[j * NTH + tid] = make_uint4(0u, 0u, 0u, 0u);
-      static_assert(2 * NBIN / 4 == NTH, "one 16-byte clear per thread for the later histograms");
-      reinterpret_cast<uint4*>(sh.xpose + kNarrowHist0)[tid] = make_uint4(0u, 0u, 0u, 0u);
-      if (tid == 0) sh.nlist = 0u;
-      __syncthreads();
-    }
+    uint32_t mask = 0u;  // listing: the slots counted
     if (from_list) {
-      const int nl = (int)sh.nlist;
-      for (int j = tid; j < nl; j += NTH) {
+      for (int j = tid; j < nlist; j += NTH) {
         const uint32_t x = list[j];
         if ((x & fixed) == prefix) atomicAdd(&hist[(x >> shift) & (NBIN - 1)], 1u);
       }
@@ -310,28 +306,45 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
         if constexpr (!RESIDENT) load_rel_coalesced(t);
         if (wide) {
 #pragma unroll
-          for (int i = 0; i < KPT; ++i) atomicAdd(&sh.hist[((u[i] >> shift) & (NBIN - 1)) * NCOPY + cp], 1u);
+          for (int i = 0; i < KPT; ++i) atomicAdd(&hist[((u[i] >> shift) & (NBIN - 1)) * NCOPY + cp], 1u);
         } else {
 #pragma unroll
           for (int i = 0; i < KPT; ++i) {
             if ((u[i] & fixed) == prefix) {
               atomicAdd(&hist[(u[i] >> shift) & (NBIN - 1)], 1u);
-              if (pass == 1) {
-                const uint32_t pos = atomicAdd(&sh.nlist, 1u);
-                if (pos < (uint32_t)kListCap) list[pos] = u[i];
-              }
+              mask |= 1u << i;
             }
           }
         }
       }
     }
+    uint32_t cnt = 0u, winc = 0u;
+    if (listing) {
+      cnt = (uint32_t)__popc(mask);
+      winc = wave_inclusive_scan(cnt);
+      if (lane == 63) sh.list_tot[wave] = winc;
+    }
     __syncthreads();
-    find_bin(sh, hist, krem, tid, lane, wave, wide);
+    if (wide) {
+      // every thread has its keys in registers: the later passes' histograms
+      // (in the hand-over area) are cleared here, visible after find_bin's barriers
+      reinterpret_cast<uint4*>(sh.xpose + kNarrowHist0)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (listing) {
+      const uint32_t total = waves_before(sh.list_tot, NWAVE);
+      nlist = (int)total;
+      from_list = total <= (uint32_t)kListCap;
+      if (from_list) {
+        uint32_t pos = waves_before(sh.list_tot, wave) + winc - cnt;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+          if ((mask >> i) & 1u) list[pos++] = u[i];
+      }
+    }
+    find_bin(sh, hist, krem, tid, lane, wave, wide);  // its barriers publish the clears and the list
     prefix |= sh.bucket << shift;
     krem = sh.krem;
     last_count = sh.bcount;
-    // the list holds every key of the second pass's prefix unless it overflowed
-    if (pass == 1) from_list = sh.nlist <= (uint32_t)kListCap;
   }
   const uint32_t T = prefix;      // rel of the kp-th largest eligible score
   const uint32_t take_eq = krem;  // keys equal to T to take, lowest positions first
@@ -472,7 +485,7 @@ __global__ __launch_bounds__(SNT) void topk_split_hist_kernel(const float* __res
                                                               uint32_t* __restrict__ hist,
                                                               uint32_t* __restrict__ state) {
   __shared__ SplitScan sh;
-  __shared__ __attribute__((aligned(16))) uint32_t lds_hist[NBIN * NCOPY];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_hist[NBIN * kSplitCopies];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t row = blockIdx.y;
   const int slice = blockIdx.x;
@@ -498,21 +511,21 @@ __global__ __launch_bounds__(SNT) void topk_split_hist_kernel(const float* __res
   constexpr int NB = 1 << split_bits(PASS), SHIFT = split_shift(PASS);
   constexpr uint32_t HI = PASS == 0 ? 0u : ~0u << (SHIFT + split_bits(PASS));  // bits fixed before this pass
 #pragma unroll
-  for (int j = 0; j < NB * NCOPY / 4 / SNT; ++j)
+  for (int j = 0; j < NB * kSplitCopies / 4 / SNT; ++j)
     reinterpret_cast<uint4*>(lds_hist)[j * SNT + tid] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   const int base = slice * kTopkSlice;
-  const int cp = lane & (NCOPY - 1);
+  const int cp = lane & (kSplitCopies - 1);
   uint32_t key[SKPT];
 #pragma unroll
   for (int j = 0; j < SKPT; ++j) key[j] = float_key(s[min(base + j * SNT + tid, E - 1)]);
 #pragma unroll
   for (int j = 0; j < SKPT; ++j)
     if (base + j * SNT + tid < E && (key[j] & HI) == prefix)
-      atomicAdd(&lds_hist[((key[j] >> SHIFT) & (NB - 1)) * NCOPY + cp], 1u);
+      atomicAdd(&lds_hist[((key[j] >> SHIFT) & (NB - 1)) * kSplitCopies + cp], 1u);
   __syncthreads();
   for (int b = tid; b < NB; b += SNT) {
-    const uint4* h = reinterpret_cast<const uint4*>(&lds_hist[b * NCOPY]);
+    const uint4* h = reinterpret_cast<const uint4*>(&lds_hist[b * kSplitCopies]);
     const uint4 h0 = h[0], h1 = h[1];
     const uint32_t c = h0.x + h0.y + h0.z + h0.w + h1.x + h1.y + h1.z + h1.w;
     if (c) atomicAdd(&gh[PASS * kTopkBins + b], c);
