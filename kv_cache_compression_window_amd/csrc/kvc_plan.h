@@ -13,9 +13,9 @@ constexpr int kTileKeys = 128;
 
 // How kvc_window_scores runs a given shape.
 //  * two-pass path (rows per KV head R > 16): pass 1 computes per-row (max, sum
-//    of exp2) over a chunk of keys, a merge kernel combines the chunks into a
-//    per-row log-normaliser, pass 2 recomputes the logits and sums the
-//    normalised probabilities over the group's rows;
+//    of exp2) over a chunk of keys; pass 2 combines the chunks' partials into
+//    each row's log-normaliser, recomputes the logits and sums the normalised
+//    probabilities over the group's rows;
 //  * stored-logits path (R <= 16): pass 1 also writes the scaled logits of the
 //    real rows, and a light kernel normalises and reduces them, so the keys are
 //    read from HBM once.

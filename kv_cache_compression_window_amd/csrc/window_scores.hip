@@ -18,10 +18,11 @@
 //   stats   MFMA A = key block, B = query block.  Each lane holds 16 keys of one
 //           query row, so the row's running max and sum of exp2 stay in the lane.
 //           Writes (max, sum) per row and key chunk.
-//   merge   combines the chunk partials into a base-2 log-normaliser per row.
-//   scores  MFMA A = query block, B = key block.  Each lane holds 16 rows of one
-//           key, so the column sums of exp2(l*c - lse2) stay in the lane; the
-//           partial sums of the waves are added in a fixed order in LDS.
+//   scores  first combines the chunk partials of its rows into a base-2
+//           log-normaliser per row.  MFMA A = query block, B = key block.  Each
+//           lane holds 16 rows of one key, so the column sums of
+//           exp2(l*c - lse2) stay in the lane; the partial sums of the waves are
+//           added in a fixed order in LDS.
 //   all_heads    (TOVA) sums the group sums over the KV heads and repeats them.
 // Multi-wave workgroups (one wave per 32 query rows, up to 256 rows per launch)
 // run a continuous stream of 32-key blocks: while the exp work of block b runs
