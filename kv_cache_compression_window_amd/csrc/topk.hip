@@ -14,9 +14,10 @@
 // Selection is an MSB-first radix select on  rel = key - min_key .  Digits of up
 // to 11 bits are taken from bit L-1 of the key range downwards, so the first
 // histogram already spreads the keys over the range they occupy (scores of one
-// row usually share their leading key bits).  Histograms live in LDS in eight
-// interleaved copies picked by lane, so lanes of one wave that fall into one bin
-// spread over eight counters.  The passes yield the exact rel T of the kp-th
+// row usually share their leading key bits).  The first pass's histogram lives
+// in LDS in two interleaved copies picked by lane, so lanes of one wave that fall
+// into one bin spread over two counters; the later passes count few keys into
+// one copy.  The passes yield the exact rel T of the kp-th
 // largest eligible score and the number of keys equal to T that must be taken.
 // The compaction then keeps every key above T and the lowest-indexed keys equal
 // to T: a thread's first output slot is the exclusive scan, over the threads,
