@@ -343,7 +343,10 @@ def wl_tova(c: Ctx, cfg, gen, dtype, tdtype) -> dict:
         return {"value": round(S * n / el, 1), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
                 "sample": f"{n} sequences (of {B} per layer) of layer 0, S={S}, fp64 numpy oracle (scores, top-k, "
                           f"gather), {el:.1f} s"}
+    def check_outputs():
+        return [t.clone() for t in (layers[0]["scores"], layers[0]["idx"], layers[0]["k_out"], layers[-1]["idx"])]
     return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes,
+                check_outputs=check_outputs,
                 kernel=kernel, cpu=cpu, metric=f"KV tokens scored+pruned/s per layer ({cfg.name})",
                 unit="tokens/s", dtype=dtype, workload=cfg.name,
                 config={"B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep})
@@ -427,7 +430,11 @@ def wl_think_128k(c: Ctx, compress: bool = False) -> dict:
         return {"value": round(B * S * n / Hkv / el, 1), "unit": "tokens/s", "cores": blas_threads(),
                 "kind": "oracle", "sample": f"{n} KV heads (of {Hkv} per layer) of layer 0, S={S}, fp64 numpy "
                                             f"oracle (channels, scores, top-k, gather), {el:.1f} s"}
+    def check_outputs():
+        return [t.clone() for t in (layers[0]["ch"], layers[0]["scores"], layers[0]["idx"], layers[0]["k_out"],
+                                    layers[-1]["idx"])]
     return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes,
+                check_outputs=check_outputs,
                 kernel=("kvc_window_scores with 64 of 128 key channels (pass 1 + pass 2)",
                         [ly["kcall"] for ly in layers], k_bytes + q_bytes + s_bytes, None),
                 kernel_alone=[ly["kcall1"] for ly in layers] if conc != 1 else None,
