@@ -58,7 +58,8 @@ kvc_status window_scores_check(const kvc_shape* sh, kvc_dtype dt, kvc_reduce red
   kvc_status st = check_shape(sh, true);
   if (st != KVC_OK) return st;
   if (chan_idx && (d_keep < 1 || d_keep > sh->D)) return KVC_ERR_SHAPE;
-  if (!kvc::ws_make_plan(sh->B, sh->H, sh->Hkv, sh->S, sh->w, concurrent_calls < 1 ? 1 : concurrent_calls, plan))
+  if (!kvc::ws_make_plan(sh->B, sh->H, sh->Hkv, sh->S, sh->w, concurrent_calls < 1 ? 1 : concurrent_calls,
+                         kvc::ws_max_waves(dt == KVC_F32, sh->D), plan))
     return KVC_ERR_UNSUPPORTED;
   return KVC_OK;
 }

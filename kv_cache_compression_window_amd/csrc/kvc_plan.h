@@ -42,17 +42,25 @@ constexpr int kMergeLanes = 8;  // lanes of the merge kernel per (b, g, row)
 // whole chip.
 constexpr int kMaxShare = 64;
 
-inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, int share, WsPlan* p) {
+// Most waves per workgroup for a storage type and head size: eight-wave
+// workgroups run two waves per SIMD, which leaves each wave 256 registers; fp32
+// rows of 128 channels need more than that (their query and key fragments are
+// twice the bf16 ones), so they run at most four waves (one per SIMD, up to 512
+// registers each).
+inline int ws_max_waves(bool fp32, int D) { return fp32 && D == 128 ? 4 : 8; }
+
+inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, int share, int max_nw, WsPlan* p) {
   const int G = H / Hkv;
   const long long R = (long long)G * w;
   if (R > kMaxRows) return false;
   p->R = (int)R;
   p->store = R <= 16;
   const long long bg = (long long)B * Hkv;
-  // one wave per 32 query rows, up to 8 waves; beyond 256 rows the rows are
-  // processed in chunks of 256 by successive launches
+  // one wave per 32 query rows, up to 8 waves (max_nw); beyond NW*32 rows the
+  // rows are processed in chunks of NW*32 by successive launches
   const int nrb = (int)((R + 31) / 32);
   p->NW = nrb <= 1 ? 1 : nrb == 2 ? 2 : nrb <= 4 ? 4 : 8;
+  if (p->NW > max_nw) p->NW = max_nw;
   p->nrch = (nrb + p->NW - 1) / p->NW;
   p->Rpad = p->nrch * p->NW * 32;
   // the merge kernel indexes rows and lanes in 32-bit integers

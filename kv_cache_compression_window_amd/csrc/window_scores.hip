@@ -1323,13 +1323,16 @@ void launch_pass(const WsParams& p, const WsPlan& plan, dim3 grid, hipStream_t s
       else ws_stats_stream_kernel<T, D, 4, false, GATHER><<<grid, 256, 0, st>>>(p);
       break;
     default:
-      // eight waves: the staging depth follows the number of tiles per workgroup
-      if (plan.CH <= kShortChunkTiles * StreamTK<T, D, 8>::value) {
-        if (scores_pass) ws_scores_stream_kernel<T, D, 8, true, GATHER><<<grid, 512, 0, st>>>(p);
-        else ws_stats_stream_kernel<T, D, 8, true, GATHER><<<grid, 512, 0, st>>>(p);
-      } else {
-        if (scores_pass) ws_scores_stream_kernel<T, D, 8, false, GATHER><<<grid, 512, 0, st>>>(p);
-        else ws_stats_stream_kernel<T, D, 8, false, GATHER><<<grid, 512, 0, st>>>(p);
+      // eight waves (never for fp32 rows of 128 channels: ws_max_waves): the
+      // staging depth follows the number of tiles per workgroup
+      if constexpr (!(sizeof(T) == 4 && D == 128)) {
+        if (plan.CH <= kShortChunkTiles * StreamTK<T, D, 8>::value) {
+          if (scores_pass) ws_scores_stream_kernel<T, D, 8, true, GATHER><<<grid, 512, 0, st>>>(p);
+          else ws_stats_stream_kernel<T, D, 8, true, GATHER><<<grid, 512, 0, st>>>(p);
+        } else {
+          if (scores_pass) ws_scores_stream_kernel<T, D, 8, false, GATHER><<<grid, 512, 0, st>>>(p);
+          else ws_stats_stream_kernel<T, D, 8, false, GATHER><<<grid, 512, 0, st>>>(p);
+        }
       }
       break;
   }

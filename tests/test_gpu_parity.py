@@ -39,6 +39,10 @@ CASES = [
     ("two_pass_r32_d64", 1, 4, 1, 300, 64, 8, "bf16", 0, 1, 0.0, 0, 1.0),
     ("two_pass_r64", 1, 8, 2, 777, 128, 16, "bf16", 0, 1, 0.0, 0, 1.0),
     ("two_pass_r96_f32", 1, 4, 2, 500, 128, 48, "f32", 0, 1, 0.0, 0, 1.0),
+    # fp32 rows of 128 channels: two waves (R 64), and four-wave row chunks where
+    # bf16 would take eight waves (R 256)
+    ("f32_d128_r64_nw2_holes", 1, 8, 2, 600, 128, 16, "f32", 0, 1, 0.1, 0, 1.0),
+    ("f32_d128_r256_row_chunks", 1, 16, 4, 700, 128, 64, "f32", 0, 1, 0.0, 0, 1.0),
     ("two_pass_r256_snapkv", 1, 32, 8, 1000, 128, 64, "bf16", 0, 1, 0.0, 0, 1.0),
     ("two_pass_r256_allheads", 2, 32, 8, 700, 128, 64, "bf16", 1, 1, 0.0, 0, 1.0),
     ("two_pass_r256_chan", 1, 32, 8, 700, 128, 64, "bf16", 0, 1, 0.0, 64, 1.0),
@@ -108,9 +112,13 @@ def test_window_scores(case):
 # The concurrency hint of kvc_window_scores_ex: fewer, longer key chunks per
 # call; each hint's scores are within the tolerance of the oracle and
 # bit-reproducible.
+HINT_CASES = [c for n in ("two_pass_r256_snapkv", "two_pass_r256_holes", "store_group_holes",
+                          "w8_long_s9000_allheads", "w8_long_chunks_s36000", "f32_d128_r256_row_chunks")
+              for c in CASES if c[0] == n]
+
+
 @pytest.mark.parametrize("conc", [2, 3, 7, 64])
-@pytest.mark.parametrize("case", [CASES[9], CASES[12], CASES[1], CASES[21], CASES[31]],
-                         ids=[CASES[i][0] for i in (9, 12, 1, 21, 31)])
+@pytest.mark.parametrize("case", HINT_CASES, ids=[c[0] for c in HINT_CASES])
 def test_window_scores_concurrency_hint(case, conc):
     name, B, H, Hkv, S, D, w, dt, reduce, causal, holes, d_keep, qs = case
     say(f"window_scores_ex {name} concurrent_calls={conc}")
