@@ -114,7 +114,15 @@ constexpr int kRawBufferFlags = 0x00020000;
 // chunk read nothing (zero: past S those keys are masked, and tiles never
 // straddle an inner chunk boundary), and a tile wholly past the chunk costs no
 // memory traffic.  The vector offsets are per-thread constants.
-template <typename T, int D, int NT, int TK>
+// Cache policy of the K staging loads (the buffer loads' cache-policy operand:
+// 0 default, 2 non-temporal).  The statistics pass reads K normally: the scores
+// pass reads the same keys right after it and finds part of them in the caches
+// (non-temporal there cost c2 2.5%).  The scores pass is K's last use, so its
+// loads are non-temporal and leave the caches to the other streams' data.
+constexpr int kStatsCpol = 0;
+constexpr int kScoresCpol = 2;
+
+template <typename T, int D, int NT, int TK, int CPOL = 0>
 struct Stager {
   using G_ = TileGeom<T, D>;
   static constexpr int UPT = TK * G_::UPR / NT;
@@ -133,11 +141,11 @@ struct Stager {
         const_cast<unsigned char*>(kbase) + (size_t)base * G_::ROWB, (short)0,
         (int)(unsigned)(kbytes < 0xFFFFFFFFull ? kbytes : 0xFFFFFFFFull), kRawBufferFlags);
 #pragma unroll
-    for (int i = 0; i < UPT; ++i) pre[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid + i * NT) * 16, 0, 0);
+    for (int i = 0; i < UPT; ++i) pre[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid + i * NT) * 16, 0, CPOL);
     const __amdgpu_buffer_rsrc_t rv =
         vrow ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vrow) + base, (short)0, left, kRawBufferFlags)
              : rk;
-    pre_valid = __builtin_amdgcn_raw_buffer_load_b8(rv, tid % TK, 0, 0);
+    pre_valid = __builtin_amdgcn_raw_buffer_load_b8(rv, tid % TK, 0, CPOL);
   }
   __device__ inline void store(unsigned char* lds_k, uint8_t* lds_v, int tid, bool has_valid) {
 #pragma unroll
@@ -392,10 +400,11 @@ using bool_t = std::integral_constant<bool, B>;
 // staging registers), tile loop with the three-tile LDS ring, and the block
 // stream.  `mfma(kf)` runs the contraction of one block, `epi(acc, t, kb,
 // masked)` its VALU work, `post(t)` runs after the barrier ending tile t.
-template <typename T, int D, int NW, bool SHORT, typename Mma, typename Epi, typename Post>
+template <typename T, int D, int NW, bool SHORT, int CPOL, typename Mma, typename Epi, typename Post>
 __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* vrow, int key0, int key1,
                                      int ntiles, bool has_valid, int tid, int col, int half, int S, int w,
-                                     int causal, unsigned char (*lds_k)[StreamTK<T, D, NW>::value * TileGeom<T, D>::LSTRIDE],
+                                     int causal,
+                                     unsigned char (*lds_k)[StreamTK<T, D, NW>::value * TileGeom<T, D>::LSTRIDE],
                                      uint8_t (*lds_v)[StreamTK<T, D, NW>::value], Mma mfma, Epi epi, Post post) {
   constexpr int NT = NW * 64;
   constexpr int TK = StreamTK<T, D, NW>::value;
@@ -403,7 +412,7 @@ __device__ inline void stream_blocks(const unsigned char* kbase, const uint8_t* 
   constexpr int KB = TK / 32;
   static_assert(KB % 2 == 0, "fragment double buffer alternates within a tile");
   using G_ = TileGeom<T, D>;
-  using Stg = Stager<T, D, NT, TK>;
+  using Stg = Stager<T, D, NT, TK, CPOL>;
 
   static_assert(NSTG >= 1 && NSTG <= 3, "one to three staging sets");
   Stg s0, s1, s2;  // the staging sets (s1, s2 unused with fewer)
@@ -588,7 +597,7 @@ __device__ inline void gather_kept_tile(const unsigned char* raw, const uint8_t*
 // the two-slot ring of full rows one tile earlier, and at the end of tile t
 // the staged tile t+2 is compacted into the ring slot the MFMAs read, behind
 // the same barrier (so the pipeline takes one more tile of staging ahead).
-template <int NW, bool SHORT, typename Mma, typename Epi, typename Post>
+template <int NW, bool SHORT, int CPOL, typename Mma, typename Epi, typename Post>
 __device__ inline void stream_blocks_kept(const unsigned char* kbase, const uint8_t* vrow, int key0, int key1,
                                           int ntiles, bool has_valid, int tid, int col, int half, int S, int w,
                                           int causal, unsigned char (*lds_raw)[64 * kRawStride],
@@ -602,7 +611,7 @@ __device__ inline void stream_blocks_kept(const unsigned char* kbase, const uint
   constexpr int NSTG = StreamNSTG<T, 128, NW, SHORT>::value;
   constexpr int KB = TK / 32;
   using G_ = TileGeom<T, D>;
-  using Stg = Stager<T, 128, NT, TK>;
+  using Stg = Stager<T, 128, NT, TK, CPOL>;
   static_assert(NSTG >= 1 && NSTG <= 3, "one to three staging sets");
 
   Stg s0, s1, s2;
@@ -747,11 +756,12 @@ __global__ __launch_bounds__(NW * 64) void ws_stats_stream_kernel(WsParams p) {
     fold_stats_ref(a, p.c, m_run, z_run);
   };
   if constexpr (GATHER)
-    stream_blocks_kept<NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal,
-                                  lds_raw, lds_rv, lds_k, lds_valid, choff, mfma, epi, [](int) {});
+    stream_blocks_kept<NW, SHORT, kStatsCpol>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w,
+                                              p.causal, lds_raw, lds_rv, lds_k, lds_valid, choff, mfma, epi,
+                                              [](int) {});
   else
-    stream_blocks<T, D, NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal,
-                                   lds_k, lds_valid, mfma, epi, [](int) {});
+    stream_blocks<T, D, NW, SHORT, kStatsCpol>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w,
+                                               p.causal, lds_k, lds_valid, mfma, epi, [](int) {});
 
   const float m2 = __shfl_xor(m_run, 32);
   const float z2 = __shfl_xor(z_run, 32);
@@ -848,11 +858,11 @@ __global__ __launch_bounds__(NW * 64) void ws_scores_stream_kernel(WsParams p) {
     }
   };
   if constexpr (GATHER)
-    stream_blocks_kept<NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal,
-                                  lds_raw, lds_rv, lds_k, lds_valid, choff, mfma, epi, post);
+    stream_blocks_kept<NW, SHORT, kScoresCpol>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w,
+                                               p.causal, lds_raw, lds_rv, lds_k, lds_valid, choff, mfma, epi, post);
   else
-    stream_blocks<T, D, NW, SHORT>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w, p.causal,
-                                   lds_k, lds_valid, mfma, epi, post);
+    stream_blocks<T, D, NW, SHORT, kScoresCpol>(kbase, vrow, key0, key1, ntiles, has_valid, tid, col, half, p.S, p.w,
+                                                p.causal, lds_k, lds_valid, mfma, epi, post);
 }
 
 // ---------------------------------------------------------------------------
@@ -1055,13 +1065,16 @@ __global__ __launch_bounds__(kLogNW * 64) void ws_logits_kernel(WsParams p) {
   auto blk_key = [&](int i) { return key0 + (wave + i * kLogNW) * 32; };
   // Unconditional loads: rows past S read row S-1 instead (never used), and
   // without a validity mask the byte comes from the key data and is ignored.
+  // The keys are read once, so the loads are non-temporal: the stream does not
+  // push the logits, statistics and other streams' data out of the caches.
   auto load_blk = [&](KB& b, int i) {
     const int kb0 = blk_key(i);
 #pragma unroll
     for (int u = 0; u < KB::UPL; ++u) {
       const int off = u * 1024 + lane * 16;
       const int key = min(kb0 + off / G_::ROWB, p.S - 1);
-      b.d[u] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * G_::ROWB + off % G_::ROWB);
+      b.d[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * G_::ROWB + off % G_::ROWB));
     }
     const uint8_t* vsrc = vrow ? vrow : kbase;
     b.v = vsrc[min(kb0 + col, p.S - 1)];
