@@ -115,11 +115,14 @@ constexpr int kRawBufferFlags = 0x00020000;
 // straddle an inner chunk boundary), and a tile wholly past the chunk costs no
 // memory traffic.  The vector offsets are per-thread constants.
 // Cache policy of the K staging loads (the buffer loads' cache-policy operand:
-// 0 default, 2 non-temporal).  The statistics pass reads K normally: the scores
-// pass reads the same keys right after it and finds part of them in the caches
-// (non-temporal there cost c2 2.5%).  The scores pass is K's last use, so its
-// loads are non-temporal and leave the caches to the other streams' data.
-constexpr int kStatsCpol = 0;
+// 1 sc0, 2 non-temporal).  A K tile is read once per workgroup, so neither pass
+// gains from the per-CU cache; the statistics pass reads K with sc0 (c2 +1.2%
+// over six interleaved pairs, c5 +1.2% over two) but not non-temporal: the
+// scores pass reads the same keys right after it and finds part of them in the
+// shared caches (non-temporal there cost c2 2.5%).  The scores pass is K's last
+// use, so its loads are non-temporal and leave the caches to the other streams'
+// data.
+constexpr int kStatsCpol = 1;
 constexpr int kScoresCpol = 2;
 
 template <typename T, int D, int NT, int TK, int CPOL = 0>
