@@ -1,4 +1,4 @@
-"""Helpers shared by the GPU tests: device upload and the parity verdicts.
+"""Helpers shared by the GPU tests: device upload and the parity checks.
 
 Parity rules (the pages state none; these readings are in force for every test):
   * scores: |gpu - oracle| <= 1e-3 * |oracle| + 1e-30 elementwise (bf16 inputs,
