@@ -24,8 +24,8 @@
 //           exp2(l*c - lse2) stay in the lane; the partial sums of the waves are
 //           added in a fixed order in LDS.
 //   all_heads    (TOVA) sums the group sums over the KV heads and repeats them.
-// Multi-wave workgroups (one wave per 32 query rows, up to 256 rows per launch)
-// run a continuous stream of 32-key blocks: while the exp work of block b runs
+// Multi-wave workgroups (one wave per 32 query rows, up to 256 rows per launch;
+// 128 for fp32 rows of 128 channels) run a continuous stream of 32-key blocks: while the exp work of block b runs
 // on the VALU, the MFMAs of block b+1 run on the matrix cores and the K
 // fragments of block b+2 are read from LDS.  64-key K tiles pass through a
 // three-tile LDS ring (the next tile is already resident when a tile ends), fed
