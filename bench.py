@@ -50,10 +50,13 @@ DEFAULT_CONCURRENT = {"snapkv_32k": 2, "snapkv_think_32k": 2, "think_128k": 2, "
 
 
 def score_kernel_hash() -> str:
+    """Hash of the score kernels' code: the sources without their // comments and
+    blank lines, so that a comment edit does not void the recorded counters."""
     h = hashlib.sha256()
     for f in SCORE_SOURCES:
-        with open(os.path.join(ROOT, "kv_cache_compression_window_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "kv_cache_compression_window_amd", "csrc", f), encoding="utf-8") as fh:
+            lines = (line.split("//", 1)[0].rstrip() for line in fh.read().splitlines())
+            h.update("\n".join(line for line in lines if line).encode())
     return h.hexdigest()[:16]
 
 
