@@ -42,8 +42,10 @@ class Workload:
 
 
 TOVA_TINY = Workload("tova_tiny_s512", "tova", 1, 4, 2, 512, 64, 1, 128, "f32", REDUCE_ALL_HEADS, 0, 0)
+# 32 distinct layers per timed step: the depth of the Llama-3-8B-shaped model the
+# layer shape comes from (a step compresses every layer of one prefill once)
 SNAPKV_32K = Workload("snapkv_32k_gqa32x8_w64", "snapkv", 1, 32, 8, 32768, 128, 64, 4096, "bf16",
-                      REDUCE_GROUP, 1, 64, layers=8)
+                      REDUCE_GROUP, 1, 64, layers=32)
 TOVA_BATCHED = Workload("tova_batched_b16_s8192", "tova", 16, 32, 8, 8192, 128, 1, 4096, "bf16",
                         REDUCE_ALL_HEADS, 0, 0, layers=2)
 SCISSOR_DECODE = Workload("scissorhands_decode_b8_c4096", "scissorhands", 8, 32, 8, 4096, 128, 1, 0,
