@@ -26,6 +26,9 @@
  *     Arithmetic is float32: bf16 x bf16 products are exact in fp32 and are
  *     accumulated in fp32.  Scores are float32; indices are int32.
  *   - head_dim D must be 64 or 128 (KVC_ERR_UNSUPPORTED otherwise).
+ *   - Positions along one row (the S keys of a KV head, the C cache slots, the n
+ *     entries of a top-k row, the n rows of the channel calls) number at most
+ *     2^30 (KVC_ERR_UNSUPPORTED otherwise).
  *   - Query head h reads KV head h / (H / Hkv) (the repeat_interleave order of
  *     [COLD]'s GQA hunk).  Window row i (0 <= i < w) is query position S-w+i.
  *   - Calls that take a workspace `ws` use it like this.  With ws == NULL,

@@ -8,6 +8,12 @@
 
 namespace {
 
+// Most positions per row (keys of a (b, g), cache slots, entries of a top-k row,
+// rows of the channel calls): the kernels keep key and slot indices, chunk ends
+// and strided loop counters in 32-bit integers, which stay below 2^31 with this
+// margin.
+constexpr int kMaxPositions = 1 << 30;
+
 inline bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 inline bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
 
@@ -20,6 +26,7 @@ kvc_status check_shape(const kvc_shape* sh, bool need_window) {
   if (sh->B > 65535 || sh->Hkv > 65535) return KVC_ERR_SHAPE;  // grid y/z limits
   if (need_window && (sh->w < 1 || sh->w > sh->S)) return KVC_ERR_SHAPE;
   if (sh->D != 64 && sh->D != 128) return KVC_ERR_UNSUPPORTED;
+  if (sh->S > kMaxPositions) return KVC_ERR_UNSUPPORTED;
   return KVC_OK;
 }
 
@@ -138,6 +145,7 @@ kvc_status kvc_scissor_update(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
   if (B < 1 || Hkv < 1 || C < 1 || hist_len < 1 || hist_len > 65535 || step < 0) return KVC_ERR_SHAPE;
   if ((int64_t)B * Hkv > 0x7fffffffLL) return KVC_ERR_SHAPE;
   if (n_evict < 0 || n_evict > C) return KVC_ERR_SHAPE;
+  if (C > kMaxPositions) return KVC_ERR_UNSUPPORTED;
   if (!valid) return KVC_ERR_NULL;
   if (probs && (!hist || !counts)) return KVC_ERR_NULL;
   if (frac_out && !counts) return KVC_ERR_NULL;
@@ -170,6 +178,7 @@ kvc_status kvc_scissor_refill(int32_t B, int32_t Hkv, int32_t C, int32_t hist_le
   if (B < 1 || Hkv < 1 || C < 1 || hist_len < 1 || hist_len > 65535 || step < 0) return KVC_ERR_SHAPE;
   if ((int64_t)B * Hkv > 65535) return KVC_ERR_SHAPE;
   if (n_protect < 0 || n_protect >= C || m < 1 || m > C - n_protect) return KVC_ERR_SHAPE;
+  if (C > kMaxPositions) return KVC_ERR_UNSUPPORTED;
   size_t off_topk = 0;
   const size_t need = kvc::scissor_refill_ws_bytes(B, Hkv, C, &off_topk);
   if (!ws) {
@@ -208,6 +217,7 @@ kvc_status kvc_scissor_insert(int32_t B, int32_t Hkv, int32_t C, int32_t D, int3
   if (D != 64 && D != 128) return KVC_ERR_UNSUPPORTED;
   if (queue ? (m < 1 || j < 0 || j >= m) : (fill_pos < 0 || fill_pos >= C)) return KVC_ERR_SHAPE;
   if (rec < 0) return KVC_ERR_SHAPE;
+  if (C > kMaxPositions) return KVC_ERR_UNSUPPORTED;
   if (!k_new || !k_cache || !valid || !hist || !counts || !since) return KVC_ERR_NULL;
   if (v_new && !v_cache) return KVC_ERR_NULL;
   if (misaligned16(k_new) || misaligned16(k_cache) || (v_new && (misaligned16(v_new) || misaligned16(v_cache))) ||
@@ -270,6 +280,7 @@ kvc_status kvc_topk_select(const float* scores, int32_t rows, int32_t n, int32_t
                            void* ws, size_t* ws_bytes, hipStream_t stream) {
   if (!ws_bytes) return KVC_ERR_NULL;
   if (rows < 0 || n < 1 || n_tail < 0 || n_tail > k || k > n) return KVC_ERR_SHAPE;
+  if (n > kMaxPositions) return KVC_ERR_UNSUPPORTED;
   if (!ws) {
     *ws_bytes = kvc::topk_ws_bytes(rows, n);
     return KVC_OK;
@@ -371,6 +382,7 @@ kvc_status kvc_channel_expand(int32_t B, int32_t Hkv, int32_t n, int32_t D, kvc_
   if (B < 1 || Hkv < 1 || n < 0) return KVC_ERR_SHAPE;
   if (D != 64 && D != 128) return KVC_ERR_UNSUPPORTED;
   if (d_keep < 1 || d_keep > D) return KVC_ERR_SHAPE;
+  if (n > kMaxPositions) return KVC_ERR_UNSUPPORTED;
   if (n == 0) return KVC_OK;
   if (!k_c || !chan_idx || !k_full) return KVC_ERR_NULL;
   const uintptr_t ea = dt == KVC_BF16 ? 1u : 3u;
@@ -401,6 +413,7 @@ kvc_status kvc_query_channels(int32_t B, int32_t H, int32_t Hkv, int32_t n, int3
   if (B < 1 || H < 1 || Hkv < 1 || n < 0 || H % Hkv != 0) return KVC_ERR_SHAPE;
   if (D != 64 && D != 128) return KVC_ERR_UNSUPPORTED;
   if (d_keep < 1 || d_keep > D) return KVC_ERR_SHAPE;
+  if (n > kMaxPositions) return KVC_ERR_UNSUPPORTED;
   if (n == 0) return KVC_OK;
   if (!q || !chan_idx || !q_c) return KVC_ERR_NULL;
   const uintptr_t ea = dt == KVC_BF16 ? 1u : 3u;

@@ -68,6 +68,8 @@ def test_window_scores_validation(lib):
     assert ws_call(lib, S(1, 32, 8, 63, 128, 64)) == 2         # w > S
     assert ws_call(lib, S(1, 32, 8, 4096, 96, 64)) == 6        # D
     assert ws_call(lib, S(1, 64, 8, 4096, 128, 256)) == 6      # G*w > 1024
+    assert ws_call(lib, S(1, 32, 8, (1 << 30) + 1, 128, 64)) == 6  # S > 2^30
+    assert ws_call(lib, S(1, 32, 8, 1 << 30, 128, 64), ws=None) == 0  # S = 2^30 (size query)
     # (b, g, padded row) x merge lanes past 2^31 - 1: 4096 x 1024 x 64 x 8 = 2^31
     assert ws_call(lib, S(4096, 1024, 1024, 4096, 128, 64)) == 6
     assert ws_call(lib, S(2048, 1024, 1024, 4096, 128, 64), ws=None) == 0  # 2^30 is still fine (size query)
@@ -171,6 +173,7 @@ def test_scissor_validation(lib):
     assert up(step=3, probs=None, hist_p=None, frac=FAKE, since=ctypes.c_void_p(0x100004)) == 4
     # nothing to do is not an error
     assert up(probs=None, hist_p=None, counts=None) == 0
+    assert up(B=1, Hkv=1, C=(1 << 30) + 1) == 6  # more than 2^30 slots per row
 
 
 def test_scissor_queue_validation(lib):
@@ -233,6 +236,8 @@ def test_topk_validation(lib):
     q = ctypes.c_size_t(0)
     assert f(None, 8, 100, 10, 0, None, None, ctypes.byref(q), None) == 0 and q.value > 0
     assert f(FAKE, 0, 100, 10, 0, FAKE, FAKE, ctypes.byref(n), None) == 0  # no rows: no-op
+    # rows longer than 2^30 positions are not supported (32-bit loop counters)
+    assert f(FAKE, 1, (1 << 30) + 1, 10, 0, FAKE, FAKE, ctypes.byref(n), None) == 6
 
 
 def test_compressed_key_cache_validation(lib):
