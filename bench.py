@@ -4,10 +4,10 @@ Default workload (the one the metric is quoted on): SnapKV prefill on a
 Llama-3-8B-shaped layer (batch 1, 32 query heads, 8 KV heads, head_dim 128,
 S = 32768 cached positions, a 64-query observation window that is always kept,
 4096 positions kept per KV head), bf16 N(0,1) Q/K/V with 1% of the prefix keys
-scaled by 4.  One step runs the whole path on each of 8 distinct layers: window
-scores -> top-k with the window forced -> gather of the kept K/V.  The layers
-together (1.07 GB of K/V) exceed the 256 MB Infinity Cache, so every layer's
-keys come from HBM.
+scaled by 4.  One step runs the whole path on each of 32 distinct layers (the
+model's depth): window scores -> top-k with the window forced -> gather of the
+kept K/V.  The layers together (4.3 GB of K/V) exceed the 256 MB Infinity Cache
+many times over, so every layer's keys come from HBM.
 
 --workload selects one of the other four workloads instead (TOVA tiny, TOVA
 batched, Scissorhands decode, ThinK + SnapKV at 128k); each prints the same kind
@@ -101,6 +101,18 @@ def blas_threads() -> int:
         return int(max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1]))
     except Exception:  # pragma: no cover
         return 1
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, as /proc/cpuinfo gives it."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def timed_oracle(fn, budget_s):
@@ -907,6 +919,8 @@ def main():
         torch.cuda.synchronize()
 
     cpu = None if args.no_cpu_baseline else wl["cpu"](args.cpu_seconds)
+    if cpu:
+        cpu["cpu_model"] = cpu_model()
     config.update({"us_per_layer": round(t_layer_us, 3), "algorithmic_bytes_per_layer": wl["layer_bytes"],
                    "hbm_roofline_frac": round(hbm_frac, 4), "wall_s": round(wall, 4)})
     if ceilings:
