@@ -47,11 +47,16 @@ DEFAULT_STEPS = {"snapkv_32k": (250, 50), "tova_tiny": (2000, 200), "tova_batche
                  "snapkv_think_32k": (250, 50), "scissor_queue_decode": (800, 0)}
 
 
-# kvc_window_scores_ex's concurrency hint for the workloads whose score calls
-# overlap on several streams (1: each call planned to fill the GPU).  Measured on
-# MI355X with 3 streams: 2 gives the two-pass workloads 5-10% more tokens/s than
-# 1, 3 and 4 give less; the stored-logits workloads gain nothing.
-DEFAULT_CONCURRENT = {"snapkv_32k": 2, "snapkv_think_32k": 2, "think_128k": 2, "think_128k_kc": 2}
+# kvc_window_scores_ex's compute-unit budget for the workloads whose score calls
+# overlap on several streams (0: each call planned to fill the GPU's 256 CUs).
+# Measured on MI355X with 3 streams, in interleaved runs: half the GPU per call
+# (128) gives the two-pass workloads 5-10% more tokens/s than the whole GPU;
+# below that, the budget that leaves the other streams' top-k, gathers and
+# channel kernels free CUs without idling the chip depends on how much of that
+# work a layer has: SnapKV 32k peaks at 96 (+2% over 128), SnapKV then ThinK at
+# 112 (+11%), ThinK 128k at 128 (96: -13%).  The stored-logits workloads gain
+# nothing.
+DEFAULT_CU_BUDGET = {"snapkv_32k": 96, "snapkv_think_32k": 112, "think_128k": 128, "think_128k_kc": 128}
 
 
 def score_kernel_hash() -> str:
@@ -76,10 +81,11 @@ def parse():
                     help="layers are spread round-robin over this many streams in the timed region")
     ap.add_argument("--kernel-reps", type=int, default=20,
                     help="passes over the layers, each timed as one run of back-to-back calls of the dominant kernel")
-    ap.add_argument("--concurrent-calls", type=int, default=None,
-                    help="kvc_window_scores_ex's hint: score calls planned to run side by side (default per workload)")
+    ap.add_argument("--cu-budget", type=int, default=None,
+                    help="kvc_window_scores_ex's compute-unit budget per score call (0: the whole GPU; "
+                         "default per workload)")
     ap.add_argument("--no-alone", action="store_true",
-                    help="with a concurrency hint, skip timing the calls planned to fill the GPU alone")
+                    help="with a compute-unit budget, skip timing the calls planned to fill the GPU alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the read-ceiling and exp-rate measurements")
@@ -90,8 +96,8 @@ def parse():
     st, wu = DEFAULT_STEPS[a.workload]
     a.steps = st if a.steps is None else a.steps
     a.warmup = wu if a.warmup is None else a.warmup
-    if a.concurrent_calls is None:
-        a.concurrent_calls = DEFAULT_CONCURRENT.get(a.workload, 1)
+    if a.cu_budget is None:
+        a.cu_budget = DEFAULT_CU_BUDGET.get(a.workload, 0)
     return a
 
 
@@ -213,8 +219,8 @@ def wl_snapkv_32k(c: Ctx, then_think: bool = False) -> dict:
         p = c.synth.snapkv(layer)
         layers.append(dict(q=c.up(p.q), k=c.up(p.k), v=c.up(p.v)))
         host0 = host0 or p
-    conc = c.args.concurrent_calls
-    ws_bytes = L.window_scores_ws_bytes(B, H, Hkv, S, D, w, concurrent_calls=conc)
+    cub = c.args.cu_budget
+    ws_bytes = L.window_scores_ws_bytes(B, H, Hkv, S, D, w, cu_budget=cub)
     s0 = c.streams[0]
     for i, ly in enumerate(layers):
         st = c.streams[i % len(c.streams)]
@@ -225,7 +231,7 @@ def wl_snapkv_32k(c: Ctx, then_think: bool = False) -> dict:
         ly["ws"] = c.empty(ws_bytes, torch.uint8)
         ly["tk_ws"] = c.empty(L.topk_ws_bytes(B * Hkv, S), torch.uint8)
         ly["calls"] = [L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st, reduce=L.KVC_REDUCE_GROUP,
-                                            causal=True, concurrent_calls=conc),
+                                            causal=True, cu_budget=cub),
                        L.bind_topk_select(ly["scores"], keep, w, ly["idx"], ly["tk_ws"], st),
                        L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st)]
         if then_think:
@@ -238,8 +244,8 @@ def wl_snapkv_32k(c: Ctx, then_think: bool = False) -> dict:
                             L.bind_topk_select(ly["cs"], dk, 0, ly["ch"], ly["tk_ws"], st),
                             L.bind_gather_compress(ly["k_out"], None, ly["rows"], ly["ch"], ly["kc"], None, st)]
         ly["kcall"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], s0, reduce=L.KVC_REDUCE_GROUP,
-                                           causal=True, concurrent_calls=conc)
-        if conc != 1:  # own workspace and scores: the step's outputs stay those of the hinted calls
+                                           causal=True, cu_budget=cub)
+        if cub != 0:  # own workspace and scores: the step's outputs stay those of the budgeted calls
             ly["ws1"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, S, D, w), torch.uint8)
             ly["scores1"] = c.empty((B, Hkv, S), torch.float32)
             ly["kcall1"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores1"], ly["ws1"], s0,
@@ -284,7 +290,7 @@ def wl_snapkv_32k(c: Ctx, then_think: bool = False) -> dict:
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("kernel_hash") == score_kernel_hash() and tr.get("concurrent_calls", 1) == conc:
+        if tr.get("kernel_hash") == score_kernel_hash() and tr.get("cu_budget", 0) == cub:
             traffic = tr.get("bytes_per_launch")
     # the score call's contraction and exps: one contraction is 2*R*S*D flops per
     # (b, g), R = G*w rows; the two passes compute it twice, with one exp2 per
@@ -299,7 +305,7 @@ def wl_snapkv_32k(c: Ctx, then_think: bool = False) -> dict:
                 check_outputs=check_outputs,
                 kernel=("kvc_window_scores (pass 1 + pass 2)", [ly["kcall"] for ly in layers],
                         k_bytes + q_bytes + s_bytes, traffic),
-                kernel_alone=[ly["kcall1"] for ly in layers] if conc != 1 else None,
+                kernel_alone=[ly["kcall1"] for ly in layers] if cub != 0 else None,
                 cpu=cpu, metric=(f"KV tokens scored+pruned/s per layer ({cfg.name}, then ThinK on the kept keys)"
                                  if then_think else METRIC), unit="tokens/s", dtype="bf16",
                 workload=cfg.name + ("_then_think" if then_think else ""),
@@ -317,9 +323,9 @@ def wl_tova(c: Ctx, cfg, gen, dtype, tdtype) -> dict:
         p = gen(layer)
         layers.append(dict(q=c.up(p.q, dtype), k=c.up(p.k, dtype), v=c.up(p.v, dtype)))
         host0 = host0 or p
-    conc = c.args.concurrent_calls
+    cub = c.args.cu_budget
     ws_bytes = L.window_scores_ws_bytes(B, H, Hkv, S, D, w, L.KVC_BF16 if dtype == "bf16" else L.KVC_F32,
-                                        concurrent_calls=conc)
+                                        cu_budget=cub)
     s0 = c.streams[0]
     for i, ly in enumerate(layers):
         st = c.streams[i % len(c.streams)]
@@ -330,11 +336,11 @@ def wl_tova(c: Ctx, cfg, gen, dtype, tdtype) -> dict:
         ly["ws"] = c.empty(ws_bytes, torch.uint8)
         ly["tk_ws"] = c.empty(L.topk_ws_bytes(B * Hkv, S), torch.uint8)
         ly["calls"] = [L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st,
-                                            reduce=L.KVC_REDUCE_ALL_HEADS, causal=False, concurrent_calls=conc),
+                                            reduce=L.KVC_REDUCE_ALL_HEADS, causal=False, cu_budget=cub),
                        L.bind_topk_select(ly["scores"], keep, 0, ly["idx"], ly["tk_ws"], st),
                        L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st)]
         ly["kscore"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], s0,
-                                            reduce=L.KVC_REDUCE_ALL_HEADS, causal=False, concurrent_calls=conc)
+                                            reduce=L.KVC_REDUCE_ALL_HEADS, causal=False, cu_budget=cub)
         ly["kgather"] = L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], s0)
 
     def step():
@@ -384,8 +390,8 @@ def wl_think_128k(c: Ctx, compress: bool = False) -> dict:
         p = c.synth.think_snapkv(layer)
         layers.append(dict(q=c.up(p.q), k=c.up(p.k), v=c.up(p.v)))
         host0 = host0 or p
-    conc = c.args.concurrent_calls
-    ws_bytes = L.window_scores_ws_bytes(B, H, Hkv, S, D, w, concurrent_calls=conc)
+    cub = c.args.cu_budget
+    ws_bytes = L.window_scores_ws_bytes(B, H, Hkv, S, D, w, cu_budget=cub)
     cs_bytes = L.channel_scores_ws_bytes(B, H, Hkv, S, D, w)
     s0 = c.streams[0]
     for i, ly in enumerate(layers):
@@ -401,7 +407,7 @@ def wl_think_128k(c: Ctx, compress: bool = False) -> dict:
         ly["calls"] = [L.bind_channel_scores(ly["q"], ly["k"], ly["cs"], ly["ws"], st),
                        L.bind_topk_select(ly["cs"], dk, 0, ly["ch"], ly["tk_ws"], st),
                        L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], st, chan_idx=ly["ch"],
-                                            reduce=L.KVC_REDUCE_GROUP, causal=True, concurrent_calls=conc),
+                                            reduce=L.KVC_REDUCE_GROUP, causal=True, cu_budget=cub),
                        L.bind_topk_select(ly["scores"], keep, w, ly["idx"], ly["tk_ws"], st)]
         if compress:
             ly["q_c"] = c.empty((B, H, w, dk), torch.bfloat16)
@@ -411,8 +417,8 @@ def wl_think_128k(c: Ctx, compress: bool = False) -> dict:
             ly["calls"].append(L.bind_gather_compact(ly["k"], ly["v"], ly["idx"], ly["k_out"], ly["v_out"], st,
                                                      chan_idx=ly["ch"]))
         ly["kcall"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores"], ly["ws"], s0, chan_idx=ly["ch"],
-                                           reduce=L.KVC_REDUCE_GROUP, causal=True, concurrent_calls=conc)
-        if conc != 1:  # own workspace and scores: the step's outputs stay those of the hinted calls
+                                           reduce=L.KVC_REDUCE_GROUP, causal=True, cu_budget=cub)
+        if cub != 0:  # own workspace and scores: the step's outputs stay those of the budgeted calls
             ly["ws1"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, S, D, w), torch.uint8)
             ly["scores1"] = c.empty((B, Hkv, S), torch.float32)
             ly["kcall1"] = L.bind_window_scores(ly["q"], ly["k"], ly["scores1"], ly["ws1"], s0, chan_idx=ly["ch"],
@@ -457,7 +463,7 @@ def wl_think_128k(c: Ctx, compress: bool = False) -> dict:
                 check_outputs=check_outputs,
                 kernel=("kvc_window_scores with 64 of 128 key channels (pass 1 + pass 2)",
                         [ly["kcall"] for ly in layers], k_bytes + q_bytes + s_bytes, None),
-                kernel_alone=[ly["kcall1"] for ly in layers] if conc != 1 else None,
+                kernel_alone=[ly["kcall1"] for ly in layers] if cub != 0 else None,
                 cpu=cpu, metric=f"KV tokens scored+pruned/s per layer ({cfg.name}{'_kc' if compress else ''})",
                 unit="tokens/s", dtype="bf16", workload=cfg.name + ("_kc" if compress else ""),
                 config={"B": B, "H": H, "Hkv": Hkv, "S": S, "D": D, "w": w, "keep": keep, "d_keep": dk,
@@ -469,7 +475,7 @@ def wl_scissor_decode(c: Ctx) -> dict:
     B, H, Hkv, C, D = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D
     nl = c.args.layers or cfg.layers
     nsteps = c.args.steps
-    conc = c.args.concurrent_calls
+    cub = c.args.cu_budget
     W = (C + 31) // 32
     layers = []
     for layer in range(nl):
@@ -481,7 +487,7 @@ def wl_scissor_decode(c: Ctx) -> dict:
         ly["probs"] = c.empty((B, Hkv, C), torch.float32)
         ly["frac"] = c.empty((B, Hkv, C), torch.float32)
         ly["ev"] = c.empty((B, Hkv, cfg.n_evict), torch.int32)
-        ly["ws"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, C, D, 1, concurrent_calls=conc),
+        ly["ws"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, C, D, 1, cu_budget=cub),
                            torch.uint8)
         ly["tk_ws"] = c.empty(L.topk_ws_bytes(B * Hkv, C), torch.uint8)
         layers.append(ly)
@@ -490,10 +496,10 @@ def wl_scissor_decode(c: Ctx) -> dict:
         st = c.streams[i % len(c.streams)]
         ly["st"] = st
         ly["score"] = [L.bind_window_scores(ly["q"][t], ly["k"], ly["probs"], ly["ws"], st, valid=ly["valid"],
-                                            reduce=L.KVC_REDUCE_GROUP, causal=False, concurrent_calls=conc)
+                                            reduce=L.KVC_REDUCE_GROUP, causal=False, cu_budget=cub)
                        for t in range(nsteps)]
         ly["kcall"] = L.bind_window_scores(ly["q"][0], ly["k"], ly["probs"], ly["ws"], s0, valid=ly["valid"],
-                                           reduce=L.KVC_REDUCE_GROUP, causal=False, concurrent_calls=conc)
+                                           reduce=L.KVC_REDUCE_GROUP, causal=False, cu_budget=cub)
         ly["topk"] = L.bind_topk_select(ly["frac"], cfg.n_evict, 0, ly["ev"], ly["tk_ws"], st)
         ly["record"], ly["record_step"] = L.bind_scissor_update(ly["valid"], ly["hist"], ly["counts"], st,
                                                                 probs=ly["probs"])
@@ -578,7 +584,7 @@ def wl_scissor_queue_decode(c: Ctx) -> dict:
     B, H, Hkv, C, D, P, m = cfg.B, cfg.H, cfg.Hkv, cfg.S, cfg.D, cfg.keep, cfg.n_evict
     nl = c.args.layers or cfg.layers
     nsteps = c.args.steps
-    conc = c.args.concurrent_calls
+    cub = c.args.cu_budget
     W = (C + 31) // 32
     layers = []
     for layer in range(nl):
@@ -593,7 +599,7 @@ def wl_scissor_queue_decode(c: Ctx) -> dict:
         ly["since"] = c.empty((B, Hkv, C), torch.int64)
         ly["probs"] = c.empty((B, Hkv, C), torch.float32)
         ly["queue"] = c.empty((B, Hkv, m), torch.int32)
-        ly["ws"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, C, D, 1, concurrent_calls=conc),
+        ly["ws"] = c.empty(L.window_scores_ws_bytes(B, H, Hkv, C, D, 1, cu_budget=cub),
                            torch.uint8)
         ly["rf_ws"] = c.empty(L.scissor_refill_ws_bytes(B, Hkv, C), torch.uint8)
         layers.append(ly)
@@ -601,10 +607,10 @@ def wl_scissor_queue_decode(c: Ctx) -> dict:
     for i, ly in enumerate(layers):
         st = c.streams[i % len(c.streams)]
         ly["score"] = [L.bind_window_scores(ly["q"][t], ly["k"], ly["probs"], ly["ws"], st, valid=ly["valid"],
-                                            reduce=L.KVC_REDUCE_GROUP, causal=False, concurrent_calls=conc)
+                                            reduce=L.KVC_REDUCE_GROUP, causal=False, cu_budget=cub)
                        for t in range(nsteps)]
         ly["kcall"] = L.bind_window_scores(ly["q"][0], ly["k"], ly["probs"], ly["ws"], s0, valid=ly["valid"],
-                                           reduce=L.KVC_REDUCE_GROUP, causal=False, concurrent_calls=conc)
+                                           reduce=L.KVC_REDUCE_GROUP, causal=False, cu_budget=cub)
         ly["record"], ly["record_step"] = L.bind_scissor_update(ly["valid"], ly["hist"], ly["counts"], st,
                                                                 probs=ly["probs"])
         ly["refill"], ly["refill_step"] = L.bind_scissor_refill(ly["valid"], ly["counts"], ly["since"], cfg.hist_len,
@@ -858,7 +864,7 @@ def main():
     # recorded on it, so that the average is the calls' own duration and not the
     # latency of an event and a dispatch per call
     config = {"workload": wl["workload"], **wl["config"], "layers_per_step": wl["layers"], "streams": args.streams,
-              "concurrent_calls": args.concurrent_calls}
+              "cu_budget": args.cu_budget}
     label, kcalls, kbytes, traffic = wl["kernel"]
     st0 = c.streams[0]
     st0.wait_stream(cur)
@@ -874,7 +880,7 @@ def main():
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for (a, b) in kev])) / len(calls) * 1e3
     k_us = time_calls(kcalls)
-    # the same calls planned to fill the GPU alone (kvc_window_scores without a hint)
+    # the same calls planned to fill the GPU alone (kvc_window_scores without a budget)
     k1_us = time_calls(wl["kernel_alone"]) if wl.get("kernel_alone") and not args.no_alone else None
 
     units = wl["units_per_step"] * args.steps
@@ -885,10 +891,10 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": label,
                 "avg_us": round(k_us, 2), "algorithmic_bytes": kbytes,
-                "concurrent_calls": args.concurrent_calls}
+                "cu_budget": args.cu_budget}
     if k1_us is not None:
         a1 = kbytes / (k1_us * 1e-6) / 1e9
-        roofline["planned_alone"] = {"concurrent_calls": 1, "avg_us": round(k1_us, 2), "achieved": round(a1, 1),
+        roofline["planned_alone"] = {"cu_budget": 256, "avg_us": round(k1_us, 2), "achieved": round(a1, 1),
                                      "frac": round(a1 / HBM_PEAK_GBS, 4)}
 
     graph = None

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 4
+#define KVC_ABI_VERSION 5
 
 typedef enum {
   KVC_OK = 0,
@@ -121,26 +121,27 @@ kvc_status kvc_window_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_wi
                              size_t* ws_bytes, hipStream_t stream);
 
 /*
- * kvc_window_scores_ex — kvc_window_scores with a launch hint for callers that
- * score several layers (or sequences) at the same time on different streams.
+ * kvc_window_scores_ex — kvc_window_scores planned for part of the GPU, for
+ * callers that score several layers (or sequences) at the same time on
+ * different streams.
  *
  * Same definition, arguments and errors as kvc_window_scores, plus:
- *   concurrent_calls  how many score calls the caller keeps running at once on
- *             this GPU.  0 or 1: one call is planned to fill the GPU (what
- *             kvc_window_scores does).  n > 1: each call is planned for about 1/n
- *             of the GPU's compute units, with n times longer key chunks per
- *             workgroup, so that n calls and the other streams' kernels run side
+ *   cu_budget  the number of the GPU's 256 compute units the call is planned
+ *             for.  0 or 256: one call fills the GPU (what kvc_window_scores
+ *             does).  Less: the call uses about that many compute units, with
+ *             correspondingly longer key chunks per workgroup, so that several
+ *             calls (128 each for two) and the other streams' kernels run side
  *             by side instead of each call waiting for the whole chip; a call
- *             running alone then takes longer.  0..64, else KVC_ERR_SHAPE.
- * The hint changes the key chunking and with it the order in which the float
- * sums are added: scores may differ from those of another hint by float
- * rounding (within the same tolerance of the definition); for a given hint they
- * are deterministic.  The workspace size depends on the hint: query it with the
- * same value.
+ *             running alone then takes longer.  0..256, else KVC_ERR_SHAPE.
+ * The budget changes the key chunking and with it the order in which the float
+ * sums are added: scores may differ from those of another budget by float
+ * rounding (within the same tolerance of the definition); for a given budget
+ * they are deterministic.  The workspace size depends on the budget: query it
+ * with the same value.
  */
 kvc_status kvc_window_scores_ex(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
                                 const uint8_t* valid, const int32_t* chan_idx, int32_t d_keep,
-                                kvc_reduce reduce, int32_t causal, int32_t concurrent_calls, float* scores,
+                                kvc_reduce reduce, int32_t causal, int32_t cu_budget, float* scores,
                                 void* ws, size_t* ws_bytes, hipStream_t stream);
 
 /*

@@ -117,28 +117,28 @@ def _workspace(nbytes: int, device, ws):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def _ws_call(concurrent_calls, sh, dt, q, k, valid, chan, d_keep, reduce, causal, scores, ws, n, stream):
-    """kvc_window_scores, or kvc_window_scores_ex when a concurrency hint is given."""
-    if concurrent_calls in (None, 1):
+def _ws_call(cu_budget, sh, dt, q, k, valid, chan, d_keep, reduce, causal, scores, ws, n, stream):
+    """kvc_window_scores, or kvc_window_scores_ex when a compute-unit budget is given."""
+    if cu_budget in (None, 0):
         return "kvc_window_scores", (sh, dt, q, k, valid, chan, d_keep, reduce, causal, scores, ws, n, stream)
-    return "kvc_window_scores_ex", (sh, dt, q, k, valid, chan, d_keep, reduce, causal, int(concurrent_calls),
+    return "kvc_window_scores_ex", (sh, dt, q, k, valid, chan, d_keep, reduce, causal, int(cu_budget),
                                     scores, ws, n, stream)
 
 
-def window_scores_ws_bytes(B, H, Hkv, S, D, w, dtype=None, concurrent_calls=None) -> int:
+def window_scores_ws_bytes(B, H, Hkv, S, D, w, dtype=None, cu_budget=None) -> int:
     sh = KvcShape(B, H, Hkv, S, D, w)
     n = ctypes.c_size_t(0)
     dt = KVC_BF16 if dtype is None else dtype
-    name, args = _ws_call(concurrent_calls, ctypes.byref(sh), dt, None, None, None, None, 0, 0, 0, None, None,
+    name, args = _ws_call(cu_budget, ctypes.byref(sh), dt, None, None, None, None, 0, 0, 0, None, None,
                           ctypes.byref(n), None)
     _check(name, getattr(LIB, name)(*args))
     return n.value
 
 
 def kvc_window_scores(q, k, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, causal=True, scores=None, ws=None,
-                      stream=None, concurrent_calls=None):
+                      stream=None, cu_budget=None):
     """scores [B,Hkv,S] float32 of the window rows q [B,H,w,D] against k [B,Hkv,S,D]
-    (kvc_window_scores_ex when concurrent_calls is given and not 1)."""
+    (kvc_window_scores_ex when cu_budget is given and not 0)."""
     _need(q, "q_win", 4)
     _need(k, "k", 4)
     sh = _shape(q, k)
@@ -153,12 +153,12 @@ def kvc_window_scores(q, k, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, 
     if scores is None:
         scores = torch.empty((sh.B, sh.Hkv, sh.S), dtype=torch.float32, device=k.device)
     n = ctypes.c_size_t(0)
-    name, args = _ws_call(concurrent_calls, ctypes.byref(sh), _dtype_code(k), None, None, None, None, d_keep, reduce,
+    name, args = _ws_call(cu_budget, ctypes.byref(sh), _dtype_code(k), None, None, None, None, d_keep, reduce,
                           int(causal), None, None, ctypes.byref(n), None)
     _check(name, getattr(LIB, name)(*args))
     ws = _workspace(n.value, k.device, ws)
     n = ctypes.c_size_t(ws.numel() * ws.element_size())
-    name, args = _ws_call(concurrent_calls, ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid),
+    name, args = _ws_call(cu_budget, ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid),
                           _ptr(chan_idx), d_keep, reduce, int(causal), _ptr(scores), _ptr(ws), ctypes.byref(n),
                           _stream(stream))
     _check(name, getattr(LIB, name)(*args))
@@ -362,13 +362,13 @@ def _bound(fn_name, args):
 
 
 def bind_window_scores(q, k, scores, ws, stream, valid=None, chan_idx=None, reduce=KVC_REDUCE_GROUP, causal=True,
-                       concurrent_calls=None):
+                       cu_budget=None):
     _need(q, "q_win", 4)
     _need(k, "k", 4)
     sh = _shape(q, k)
     d_keep = 0 if chan_idx is None else chan_idx.shape[2]
     n = ctypes.c_size_t(ws.numel() * ws.element_size())
-    name, args = _ws_call(concurrent_calls, ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid),
+    name, args = _ws_call(cu_budget, ctypes.byref(sh), _dtype_code(k), _ptr(q), _ptr(k), _ptr(valid),
                           _ptr(chan_idx), d_keep, reduce, int(causal), _ptr(scores), _ptr(ws), ctypes.byref(n),
                           ctypes.c_void_p(stream.cuda_stream))
     call = _bound(name, args)

@@ -58,14 +58,14 @@ namespace {
 
 // Validation and plan of kvc_window_scores (everything but the workspace).
 kvc_status window_scores_check(const kvc_shape* sh, kvc_dtype dt, kvc_reduce reduce, const int32_t* chan_idx,
-                               int32_t d_keep, int32_t concurrent_calls, kvc::WsPlan* plan) {
-  if (concurrent_calls < 0 || concurrent_calls > kvc::kMaxShare) return KVC_ERR_SHAPE;
+                               int32_t d_keep, int32_t cu_budget, kvc::WsPlan* plan) {
+  if (cu_budget < 0 || cu_budget > kvc::kNumCUs) return KVC_ERR_SHAPE;
   if (dt != KVC_F32 && dt != KVC_BF16) return KVC_ERR_DTYPE;
   if (reduce != KVC_REDUCE_GROUP && reduce != KVC_REDUCE_ALL_HEADS) return KVC_ERR_DTYPE;
   kvc_status st = check_shape(sh, true);
   if (st != KVC_OK) return st;
   if (chan_idx && (d_keep < 1 || d_keep > sh->D)) return KVC_ERR_SHAPE;
-  if (!kvc::ws_make_plan(sh->B, sh->H, sh->Hkv, sh->S, sh->w, concurrent_calls < 1 ? 1 : concurrent_calls,
+  if (!kvc::ws_make_plan(sh->B, sh->H, sh->Hkv, sh->S, sh->w, cu_budget == 0 ? kvc::kNumCUs : cu_budget,
                          kvc::ws_max_waves(dt == KVC_F32, sh->D), plan))
     return KVC_ERR_UNSUPPORTED;
   return KVC_OK;
@@ -101,17 +101,17 @@ extern "C" {
 kvc_status kvc_window_scores(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
                              const uint8_t* valid, const int32_t* chan_idx, int32_t d_keep, kvc_reduce reduce,
                              int32_t causal, float* scores, void* ws, size_t* ws_bytes, hipStream_t stream) {
-  return kvc_window_scores_ex(sh, dt, q_win, k, valid, chan_idx, d_keep, reduce, causal, 1, scores, ws, ws_bytes,
+  return kvc_window_scores_ex(sh, dt, q_win, k, valid, chan_idx, d_keep, reduce, causal, 0, scores, ws, ws_bytes,
                               stream);
 }
 
 kvc_status kvc_window_scores_ex(const kvc_shape* sh, kvc_dtype dt, const void* q_win, const void* k,
                                 const uint8_t* valid, const int32_t* chan_idx, int32_t d_keep, kvc_reduce reduce,
-                                int32_t causal, int32_t concurrent_calls, float* scores, void* ws,
+                                int32_t causal, int32_t cu_budget, float* scores, void* ws,
                                 size_t* ws_bytes, hipStream_t stream) {
   if (!sh || !ws_bytes) return KVC_ERR_NULL;
   kvc::WsPlan plan;
-  const kvc_status st = window_scores_check(sh, dt, reduce, chan_idx, d_keep, concurrent_calls, &plan);
+  const kvc_status st = window_scores_check(sh, dt, reduce, chan_idx, d_keep, cu_budget, &plan);
   if (st != KVC_OK) return st;
   if (!ws) {
     *ws_bytes = plan.bytes;
@@ -128,7 +128,7 @@ kvc_status kvc_window_scores_noalloc(const kvc_shape* sh, kvc_dtype dt, const vo
                                      kvc_reduce reduce, int32_t causal, float* scores, hipStream_t stream) {
   if (!sh) return KVC_ERR_NULL;
   kvc::WsPlan plan;
-  const kvc_status st = window_scores_check(sh, dt, reduce, chan_idx, d_keep, 1, &plan);
+  const kvc_status st = window_scores_check(sh, dt, reduce, chan_idx, d_keep, 0, &plan);
   if (st != KVC_OK) return st;
   if (plan.bytes > kvc::kNoAllocScratchBytes) return KVC_ERR_WORKSPACE;
   if (!q_win || !k || !scores) return KVC_ERR_NULL;

@@ -36,11 +36,12 @@ constexpr int kMaxRows = 1024;  // G*w limit per KV head
 constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
 constexpr int kMergeLanes = 8;  // lanes of the merge kernel per (b, g, row)
 
-// `share` (>= 1): the number of score calls the caller runs at the same time;
-// each call then aims at 1/share of the workgroups that fill the GPU, so that the
-// calls run side by side with longer key chunks instead of queueing for the
-// whole chip.
-constexpr int kMaxShare = 64;
+// Compute units of an MI355X.  A score call is planned for a budget of them
+// (`cu_budget`, 1..kNumCUs): the whole GPU by default; callers that keep several
+// calls and other kernels running at once on different streams give each call a
+// part, so that the calls run side by side with longer key chunks instead of
+// queueing for the whole chip.
+constexpr int kNumCUs = 256;
 
 // Most waves per workgroup for a storage type and head size: eight-wave
 // workgroups run two waves per SIMD, which leaves each wave 256 registers; fp32
@@ -49,7 +50,7 @@ constexpr int kMaxShare = 64;
 // registers each).
 inline int ws_max_waves(bool fp32, int D) { return fp32 && D == 128 ? 4 : 8; }
 
-inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, int share, int max_nw, WsPlan* p) {
+inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, int cu_budget, int max_nw, WsPlan* p) {
   const int G = H / Hkv;
   const long long R = (long long)G * w;
   if (R > kMaxRows) return false;
@@ -65,11 +66,11 @@ inline bool ws_make_plan(int B, int H, int Hkv, int S, int w, int share, int max
   p->Rpad = p->nrch * p->NW * 32;
   // the merge kernel indexes rows and lanes in 32-bit integers
   if (bg * p->Rpad * kMergeLanes > 0x7fffffffLL) return false;
-  // workgroups to aim for: about eight waves per CU on the two-pass path, two
-  // four-wave streaming workgroups per CU on the (HBM-bound) stored-logits path
-  long long target = p->store ? 512 : 256LL * 8 / p->NW;
-  target = target / (share < 1 ? 1 : share);
-  if (target < 1) target = 1;
+  // workgroups to aim for: about eight waves per budgeted CU on the two-pass
+  // path, two four-wave streaming workgroups per budgeted CU on the (HBM-bound)
+  // stored-logits path
+  const int cus = cu_budget < 1 || cu_budget > kNumCUs ? kNumCUs : cu_budget;
+  long long target = (p->store ? 2LL : 8LL / p->NW) * cus;
   long long nch = (target + bg - 1) / bg;
   if (p->store) {
     // stored-logits chunks of at least 1024 keys (a quarter of the row when that

@@ -43,6 +43,8 @@ int main() {
   expect("ws D", ws(&bad_d, 1, fake, fake, 0, fake, &big), KVC_ERR_UNSUPPORTED);
   expect("ws rows", ws(&big_rows, 1, fake, fake, 0, fake, &big), KVC_ERR_UNSUPPORTED);
   expect("ws merge overflow", ws(&overflow, 1, fake, fake, 0, fake, &big), KVC_ERR_UNSUPPORTED);
+  kvc_shape long_rows = {1, 32, 8, (1 << 30) + 1, 128, 64};
+  expect("ws S > 2^30", ws(&long_rows, 1, fake, fake, 0, fake, &big), KVC_ERR_UNSUPPORTED);
   expect("ws size query", ws(&ok, 1, nullptr, nullptr, 0, nullptr, &q), KVC_OK);
   if (q == 0) ++failures;
   expect("ws small workspace", ws(&ok, 1, fake, fake, 0, fake, &small), KVC_ERR_WORKSPACE);
@@ -52,9 +54,9 @@ int main() {
     return kvc_window_scores_ex(&ok, KVC_BF16, fake, fake, nullptr, nullptr, 0, KVC_REDUCE_GROUP, 1, conc,
                                 static_cast<float*>(fake), w, n, nullptr);
   };
-  expect("ws_ex hint < 0", wsx(-1, fake, &big), KVC_ERR_SHAPE);
-  expect("ws_ex hint > 64", wsx(65, fake, &big), KVC_ERR_SHAPE);
-  expect("ws_ex size query", wsx(2, nullptr, &q), KVC_OK);
+  expect("ws_ex budget < 0", wsx(-1, fake, &big), KVC_ERR_SHAPE);
+  expect("ws_ex budget > 256", wsx(257, fake, &big), KVC_ERR_SHAPE);
+  expect("ws_ex size query", wsx(128, nullptr, &q), KVC_OK);
   expect("ws_ex small workspace", wsx(64, fake, &small), KVC_ERR_WORKSPACE);
   expect("ws noalloc overflow",
          kvc_window_scores_noalloc(&(const kvc_shape&)kvc_shape{64, 32, 8, 8192, 128, 1}, KVC_BF16, fake, fake,

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.abi_version() == 4
+    assert lib.abi_version() == 5
     for code in range(8):
         s = lib.LIB.kvc_status_string(code).decode()
         assert s and s != "unknown status"
@@ -89,32 +89,35 @@ def test_window_scores_validation(lib):
 
 
 def test_window_scores_ex_validation(lib):
-    """The concurrency hint: 0..64 accepted (0 and 1 plan the same call), other
-    values rejected before anything else; a larger hint plans fewer, longer key
-    chunks, so the chunk statistics (and with them the workspace) shrink."""
+    """The compute-unit budget: 0..256 accepted (0 and 256 plan the same call),
+    other values rejected before anything else; a smaller budget plans fewer,
+    longer key chunks, so the chunk statistics (and with them the workspace)
+    shrink."""
     f = lib.LIB.kvc_window_scores_ex
     S = lib.KvcShape
     ok = S(1, 32, 8, 32768, 128, 64)
 
-    def size(conc, sh=ok):
+    def size(cus, sh=ok):
         n = ctypes.c_size_t(0)
-        st = f(ctypes.byref(sh), 1, None, None, None, None, 0, 0, 1, conc, None, None, ctypes.byref(n), None)
+        st = f(ctypes.byref(sh), 1, None, None, None, None, 0, 0, 1, cus, None, None, ctypes.byref(n), None)
         return st, n.value
     assert size(-1)[0] == 2
-    assert size(65)[0] == 2
+    assert size(257)[0] == 2
     st0, n0 = size(0)
-    st1, n1 = size(1)
-    assert st0 == st1 == 0 and n0 == n1 == lib.window_scores_ws_bytes(1, 32, 8, 32768, 128, 64)
-    st2, n2 = size(2)
-    assert st2 == 0 and n2 < n1
-    assert lib.window_scores_ws_bytes(1, 32, 8, 32768, 128, 64, concurrent_calls=2) == n2
-    assert size(64)[0] == 0
-    assert size(64, S(1, 4, 2, 512, 64, 1))[0] == 0  # the stored-logits path
+    st256, n256 = size(256)
+    assert st0 == st256 == 0 and n0 == n256 == lib.window_scores_ws_bytes(1, 32, 8, 32768, 128, 64)
+    st128, n128 = size(128)
+    assert st128 == 0 and n128 < n256
+    st96, n96 = size(96)
+    assert st96 == 0 and n96 < n128
+    assert lib.window_scores_ws_bytes(1, 32, 8, 32768, 128, 64, cu_budget=128) == n128
+    assert size(1)[0] == 0
+    assert size(1, S(1, 4, 2, 512, 64, 1))[0] == 0  # the stored-logits path
     n = ctypes.c_size_t(1 << 40)
-    assert f(ctypes.byref(ok), 1, FAKE, FAKE, None, None, 0, 0, 1, 2, FAKE, FAKE, ctypes.byref(ctypes.c_size_t(16)),
-             None) == 5
-    assert f(ctypes.byref(ok), 1, ODD, FAKE, None, None, 0, 0, 1, 2, FAKE, FAKE, ctypes.byref(n), None) == 4
-    assert f(ctypes.byref(S(1, 30, 8, 4096, 128, 64)), 1, FAKE, FAKE, None, None, 0, 0, 1, 2, FAKE, FAKE,
+    assert f(ctypes.byref(ok), 1, FAKE, FAKE, None, None, 0, 0, 1, 128, FAKE, FAKE,
+             ctypes.byref(ctypes.c_size_t(16)), None) == 5
+    assert f(ctypes.byref(ok), 1, ODD, FAKE, None, None, 0, 0, 1, 128, FAKE, FAKE, ctypes.byref(n), None) == 4
+    assert f(ctypes.byref(S(1, 30, 8, 4096, 128, 64)), 1, FAKE, FAKE, None, None, 0, 0, 1, 128, FAKE, FAKE,
              ctypes.byref(n), None) == 2
 
 

@@ -2,7 +2,7 @@
 
 Each test runs the workload's whole path through the C-ABI at its real shape.
 The launch configuration is the one bench.py times (the kernels and tilings
-depend only on the shape and the concurrency hint).  Results are compared with the fp64
+depend only on the shape and the compute-unit budget).  Results are compared with the fp64
 oracle on the same seeded inputs:
   * scores elementwise (1e-3 relative);
   * kept sets bit-exact against the oracle's selection on the GPU's own scores,
@@ -28,10 +28,10 @@ from tests.gpu_util import (check_gather, check_kept, check_scores, dev, host_bi
 
 pytestmark = pytest.mark.gpu
 
-# The score calls of the 32K and 128K prefill layers run two at a time in the
-# timed loop (one per stream) and take the concurrency hint 2 there; the tests
-# use the same grid split.
-CONC = 2
+# The compute-unit budgets the timed loop gives the score calls of the 32K and
+# 128K prefill layers (they run side by side on several streams there); the
+# tests use the same grid splits.
+CUS_SNAPKV_32K, CUS_SNAPKV_THEN_THINK, CUS_THINK_128K = 96, 112, 128
 
 
 def lib():
@@ -70,11 +70,12 @@ def test_c2_snapkv_32k_full():
     idx = torch.empty((p.B, p.Hkv, cfg.keep), dtype=torch.int32, device="cuda")
     ko = torch.empty((p.B, p.Hkv, cfg.keep, p.D), dtype=torch.bfloat16, device="cuda")
     vo = torch.empty_like(ko)
-    ws = torch.empty(L.window_scores_ws_bytes(p.B, p.H, p.Hkv, p.S, p.D, p.w, concurrent_calls=CONC),
+    ws = torch.empty(L.window_scores_ws_bytes(p.B, p.H, p.Hkv, p.S, p.D, p.w, cu_budget=CUS_SNAPKV_32K),
                      dtype=torch.uint8, device="cuda")
     tk_ws = torch.empty(L.topk_ws_bytes(p.B * p.Hkv, p.S), dtype=torch.uint8, device="cuda")
     # the same pre-bound calls as the timed loop
-    L.bind_window_scores(q, k, scores, ws, st, reduce=L.KVC_REDUCE_GROUP, causal=True, concurrent_calls=CONC)()
+    L.bind_window_scores(q, k, scores, ws, st, reduce=L.KVC_REDUCE_GROUP, causal=True,
+                         cu_budget=CUS_SNAPKV_32K)()
     L.bind_topk_select(scores, cfg.keep, cfg.n_tail, idx, tk_ws, st)()
     L.bind_gather_compact(k, v, idx, ko, vo, st)()
     torch.cuda.synchronize()
@@ -232,7 +233,7 @@ def test_c5_think_snapkv_128k_full():
     chg = ch.cpu().numpy()
     check_kept(chg, csg, ref_cs, cfg.d_keep, 0)
     # the oracle continues with the GPU's channel set
-    s = L.kvc_window_scores(q, k, chan_idx=ch, reduce=L.KVC_REDUCE_GROUP, causal=True, concurrent_calls=CONC)
+    s = L.kvc_window_scores(q, k, chan_idx=ch, reduce=L.KVC_REDUCE_GROUP, causal=True, cu_budget=CUS_THINK_128K)
     idx = L.kvc_topk_select(s.view(-1, p.S), cfg.keep, cfg.n_tail).view(p.B, p.Hkv, cfg.keep)
     ko, vo = L.kvc_gather_compact(k, v, idx, chan_idx=ch)
     torch.cuda.synchronize()
@@ -254,7 +255,7 @@ def test_c5_kept_keys_compressed_full():
     q, k, v = dev(p.q, "bf16"), dev(p.k, "bf16"), dev(p.v, "bf16")
     cs = L.kvc_channel_scores(q, k)
     ch = L.kvc_topk_select(cs.view(-1, p.D), cfg.d_keep).view(p.B, p.Hkv, cfg.d_keep)
-    s = L.kvc_window_scores(q, k, chan_idx=ch, reduce=L.KVC_REDUCE_GROUP, causal=True, concurrent_calls=CONC)
+    s = L.kvc_window_scores(q, k, chan_idx=ch, reduce=L.KVC_REDUCE_GROUP, causal=True, cu_budget=CUS_THINK_128K)
     idx = L.kvc_topk_select(s.view(-1, p.S), cfg.keep, cfg.n_tail).view(p.B, p.Hkv, cfg.keep)
     kc, vc = L.kvc_gather_compress(k, v, idx, ch)
     qc = L.kvc_query_channels(q, ch)
@@ -279,7 +280,7 @@ def test_c2_then_think_full():
     L = lib()
     dk = 64
     q, k, v = dev(p.q, "bf16"), dev(p.k, "bf16"), dev(p.v, "bf16")
-    s = L.kvc_window_scores(q, k, reduce=L.KVC_REDUCE_GROUP, causal=True, concurrent_calls=CONC)
+    s = L.kvc_window_scores(q, k, reduce=L.KVC_REDUCE_GROUP, causal=True, cu_budget=CUS_SNAPKV_THEN_THINK)
     idx = L.kvc_topk_select(s.view(-1, p.S), cfg.keep, cfg.n_tail).view(p.B, p.Hkv, cfg.keep)
     ko, vo = L.kvc_gather_compact(k, v, idx)
     cs = L.kvc_channel_scores(q, ko)

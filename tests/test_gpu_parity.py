@@ -109,28 +109,28 @@ def test_window_scores(case):
     assert torch.equal(s, s2)
 
 
-# The concurrency hint of kvc_window_scores_ex: fewer, longer key chunks per
-# call; each hint's scores are within the tolerance of the oracle and
+# The compute-unit budget of kvc_window_scores_ex: fewer, longer key chunks
+# per call; each budget's scores are within the tolerance of the oracle and
 # bit-reproducible.
-HINT_CASES = [c for n in ("two_pass_r256_snapkv", "two_pass_r256_holes", "store_group_holes",
+BUDGET_CASES = [c for n in ("two_pass_r256_snapkv", "two_pass_r256_holes", "store_group_holes",
                           "w8_long_s9000_allheads", "w8_long_chunks_s36000", "f32_d128_r256_row_chunks")
               for c in CASES if c[0] == n]
 
 
-@pytest.mark.parametrize("conc", [2, 3, 7, 64])
-@pytest.mark.parametrize("case", HINT_CASES, ids=[c[0] for c in HINT_CASES])
-def test_window_scores_concurrency_hint(case, conc):
+@pytest.mark.parametrize("cus", [128, 112, 96, 85, 36, 4])
+@pytest.mark.parametrize("case", BUDGET_CASES, ids=[c[0] for c in BUDGET_CASES])
+def test_window_scores_cu_budget(case, cus):
     name, B, H, Hkv, S, D, w, dt, reduce, causal, holes, d_keep, qs = case
-    say(f"window_scores_ex {name} concurrent_calls={conc}")
+    say(f"window_scores_ex {name} cu_budget={cus}")
     p, valid, chan = _make(case, 100 + CASES.index(case))
     ref = O.window_scores(p.q64(), p.k64(), valid=valid, chan_keep=chan, reduce=reduce, causal=causal)
     L = lib()
     args = dict(valid=None if valid is None else dev(valid), chan_idx=None if chan is None else dev(chan),
-                reduce=reduce, causal=bool(causal), concurrent_calls=conc)
+                reduce=reduce, causal=bool(causal), cu_budget=cus)
     s1 = L.kvc_window_scores(dev(p.q, dt), dev(p.k, dt), **args)
     s2 = L.kvc_window_scores(dev(p.q, dt), dev(p.k, dt), **args)
     torch.cuda.synchronize()
-    check_scores(s1.cpu().numpy(), ref, f"{name} hint {conc}")
+    check_scores(s1.cpu().numpy(), ref, f"{name} cu_budget {cus}")
     assert torch.equal(s1, s2)
 
 
