@@ -113,11 +113,11 @@ def test_window_scores(case):
 # per call; each budget's scores are within the tolerance of the oracle and
 # bit-reproducible.
 BUDGET_CASES = [c for n in ("two_pass_r256_snapkv", "two_pass_r256_holes", "store_group_holes",
-                          "w8_long_s9000_allheads", "w8_long_chunks_s36000", "f32_d128_r256_row_chunks")
-              for c in CASES if c[0] == n]
+                            "w8_long_s9000_allheads", "w8_long_chunks_s36000", "f32_d128_r256_row_chunks")
+                for c in CASES if c[0] == n]
 
 
-@pytest.mark.parametrize("cus", [128, 112, 96, 85, 36, 4])
+@pytest.mark.parametrize("cus", [256, 128, 112, 96, 85, 36, 4, 1])
 @pytest.mark.parametrize("case", BUDGET_CASES, ids=[c[0] for c in BUDGET_CASES])
 def test_window_scores_cu_budget(case, cus):
     name, B, H, Hkv, S, D, w, dt, reduce, causal, holes, d_keep, qs = case
@@ -132,6 +132,11 @@ def test_window_scores_cu_budget(case, cus):
     torch.cuda.synchronize()
     check_scores(s1.cpu().numpy(), ref, f"{name} cu_budget {cus}")
     assert torch.equal(s1, s2)
+    if cus == 256:  # the whole GPU: the plan of kvc_window_scores, bit for bit
+        args.pop("cu_budget")
+        s0 = L.kvc_window_scores(dev(p.q, dt), dev(p.k, dt), **args)
+        torch.cuda.synchronize()
+        assert torch.equal(s0, s1)
 
 
 # The same (b, g) rows under two grid splits: batch 0 alone, and batch 0 next to
