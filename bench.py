@@ -38,10 +38,11 @@ SCORE_SOURCES = ["window_scores.hip", "kvc_device.h", "kvc_plan.h"]
 WORKLOADS = ["snapkv_32k", "tova_tiny", "tova_batched", "scissor_decode", "think_128k", "think_128k_kc",
              "snapkv_think_32k", "scissor_queue_decode"]
 # (timed steps, warm-up steps).  The timed regions last 0.1-0.5 s: measured on
-# MI355X, c2 (then 8 layers per step) read 6.07e8 tokens/s after 10 warm-up steps
-# and 6.22e8 after 300 (the clocks settle), and c5 5.09e8 over 10 steps but
-# 5.84e8 over 100 (with two layers per step the streams' start and drain weigh on
-# a short run).  The decode workloads time one whole 800-step run.
+# MI355X, SnapKV 32k (then 8 layers per step) read 6.07e8 tokens/s after 10
+# warm-up steps and 6.22e8 after 300 (the clocks settle), and ThinK 128k 5.09e8
+# over 10 steps but 5.84e8 over 100 (with two layers per step the streams' start
+# and drain weigh on a short run).  The decode workloads time one whole 800-step
+# run.
 DEFAULT_STEPS = {"snapkv_32k": (250, 50), "tova_tiny": (2000, 200), "tova_batched": (100, 10),
                  "scissor_decode": (800, 0), "think_128k": (200, 20), "think_128k_kc": (200, 20),
                  "snapkv_think_32k": (250, 50), "scissor_queue_decode": (800, 0)}

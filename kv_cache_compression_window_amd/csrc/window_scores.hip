@@ -113,8 +113,9 @@ constexpr int kRawBufferFlags = 0x00020000;
 // non-temporal: the scores pass reads the same keys right after it and finds part
 // of them in the shared caches.  The scores pass is K's last use, so its loads
 // are non-temporal and leave the caches to the other streams' data.  Measured on
-// MI355X against no hints: the c2 call alone 1.6% faster and c5 +2.8% tokens/s;
-// non-temporal loads in the statistics pass cost c2 2.5%.
+// MI355X against no hints: the SnapKV 32k call alone 1.6% faster and the ThinK
+// 128k layer +2.8% tokens/s; non-temporal loads in the statistics pass cost the
+// SnapKV 32k layer 2.5%.
 constexpr int kStatsCpol = 1;
 constexpr int kScoresCpol = 2;
 

@@ -9,9 +9,10 @@ oracle on the same seeded inputs:
     and equal to the oracle's selection outside positions within a relative
     1e-5 of the row threshold;
   * gathers bit-exact.
-The oracle computes a full layer of c1, c2, c3 and c5 in seconds.  For the
-800-step Scissorhands decode (c4) it follows three sampled (batch, KV head)
-rows in teacher-forced lockstep, while the GPU runs all 64.
+The oracle computes a full layer of TOVA tiny, SnapKV 32k, TOVA batched and
+ThinK + SnapKV 128k in seconds.  For the 800-step Scissorhands decode it follows
+three sampled (batch, KV head) rows in teacher-forced lockstep, while the GPU
+runs all 64.
 """
 from __future__ import annotations
 
@@ -43,7 +44,7 @@ def say(msg):
     print(f"[gpu-full] {msg}", file=sys.stderr, flush=True)
 
 
-def test_c1_tova_tiny_full():
+def test_tova_tiny_full():
     cfg = configs.TOVA_TINY
     say(cfg.name)
     p = synth.tova_tiny(0)
@@ -54,12 +55,12 @@ def test_c1_tova_tiny_full():
     ko, vo = L.kvc_gather_compact(k, v, idx)
     torch.cuda.synchronize()
     ref_s, _ = O.tova(p.q64(), p.k64(), p.v64(), cfg.keep)
-    check_scores(s.cpu().numpy(), ref_s, "c1 scores")
+    check_scores(s.cpu().numpy(), ref_s, "TOVA tiny scores")
     check_kept(idx.cpu().numpy(), s.cpu().numpy(), ref_s, cfg.keep, 0)
     check_gather(ko, vo, p.k, p.v, idx.cpu().numpy())
 
 
-def test_c2_snapkv_32k_full():
+def test_snapkv_32k_full():
     cfg = configs.SNAPKV_32K
     say(cfg.name)
     p = synth.snapkv(0)
@@ -81,14 +82,14 @@ def test_c2_snapkv_32k_full():
     torch.cuda.synchronize()
     ref_s, _ = O.snapkv(p.q64(), p.k64(), cfg.keep)
     sg = scores.cpu().numpy()
-    check_scores(sg, ref_s, "c2 scores")
+    check_scores(sg, ref_s, "SnapKV 32k scores")
     # every row of scores sums to 1 (the window mean of softmax rows)
     assert np.allclose(sg.sum(axis=-1, dtype=np.float64), 1.0, rtol=0, atol=1e-4)
     check_kept(idx.cpu().numpy(), sg, ref_s, cfg.keep, cfg.n_tail)
     check_gather(ko, vo, p.k, p.v, idx.cpu().numpy())
 
 
-def test_c3_tova_batched_full():
+def test_tova_batched_full():
     cfg = configs.TOVA_BATCHED
     say(cfg.name)
     p = synth.tova_batched(0)
@@ -100,7 +101,7 @@ def test_c3_tova_batched_full():
     torch.cuda.synchronize()
     ref_s, _ = O.tova(p.q64(), p.k64(), None, cfg.keep)
     sg = s.cpu().numpy()
-    check_scores(sg, ref_s, "c3 scores")
+    check_scores(sg, ref_s, "TOVA batched scores")
     # TOVA repeats one row per KV head, so the kept sets of a sequence agree
     ig = idx.cpu().numpy()
     assert (ig == ig[:, :1]).all()
@@ -108,8 +109,8 @@ def test_c3_tova_batched_full():
     check_gather(ko, vo, p.k, p.v, ig)
 
 
-def test_c4_scissorhands_decode_full_sampled():
-    """c4 at full size: all 800 steps on all 64 (b, g) rows.  Three rows are
+def test_scissorhands_decode_full_sampled():
+    """Scissorhands decode at full size: all 800 steps on all 64 (b, g) rows.  Three rows are
     followed in teacher-forced lockstep at every step (probabilities, low bits,
     counts); at each of the 12 eviction steps every row is checked:
     probabilities, low bits, counts, fractions, the eviction set and the
@@ -147,7 +148,7 @@ def test_c4_scissorhands_decode_full_sampled():
         for si, (b, g) in enumerate(sample):
             ref_p = O.window_scores(q64[b:b + 1, g * G:(g + 1) * G], k64[b:b + 1, g:g + 1],
                                     valid=v_before[b:b + 1, g:g + 1], reduce=O.REDUCE_GROUP, causal=False)[0, 0]
-            check_scores(pg[b, g], ref_p, f"c4 step {t} ({b},{g}) probs")
+            check_scores(pg[b, g], ref_p, f"decode step {t} ({b},{g}) probs")
             planes = unpack_planes(h_now, si, C)
             # the oracle takes the step on the GPU's state: the low test needs only validity and probabilities
             low = oracle_state(v_before[b, g], planes, t, hl).record(ref_p[None, None])[0, 0]
@@ -157,7 +158,7 @@ def test_c4_scissorhands_decode_full_sampled():
         if evict:
             # every row at the eviction steps
             ref_all = O.window_scores(q64, k64, valid=v_before, reduce=O.REDUCE_GROUP, causal=False)
-            check_scores(pg, ref_all, f"c4 step {t} probs (all rows)")
+            check_scores(pg, ref_all, f"decode step {t} probs (all rows)")
             planes_all = unpack_all_planes(hist.cpu().numpy(), C).reshape(B, Hkv, C, hl)
             low_all = O.LowAttentionState.from_recordings(v_before, np.zeros((B, Hkv, C), np.int64), {}, t,
                                                           hl).record(ref_all)
@@ -175,13 +176,13 @@ def test_c4_scissorhands_decode_full_sampled():
     assert int(valid.sum().item()) == B * Hkv * (C - (cfg.steps // cfg.evict_every) * cfg.n_evict)
 
 
-def test_c4_scissorhands_resume():
+def test_scissorhands_decode_resume():
     """Checkpoint and resume of the decode state: 400 steps, a copy of the state
     buffers (validity, bit-planes, counts) through host memory into fresh
     buffers, 400 more steps; the result is bit-identical to 800 uninterrupted
     steps."""
     cfg = configs.SCISSOR_DECODE
-    say("c4 resume")
+    say("Scissorhands decode resume")
     B, Hkv, C, hl = cfg.B, cfg.Hkv, cfg.S, cfg.hist_len
     L = lib()
     kd = dev(synth.scissor_cache(0), "bf16")
@@ -217,7 +218,7 @@ def test_c4_scissorhands_resume():
         assert torch.equal(a.cpu(), b.cpu()), name
 
 
-def test_c5_think_snapkv_128k_full():
+def test_think_snapkv_128k_full():
     cfg = configs.THINK_128K
     say(cfg.name)
     p = synth.think_snapkv(0)
@@ -229,7 +230,7 @@ def test_c5_think_snapkv_128k_full():
     q64, k64 = p.q64(), p.k64()
     ref_cs = O.channel_scores(q64, k64)
     csg = cs.cpu().numpy()
-    check_scores(csg, ref_cs, "c5 channel scores")
+    check_scores(csg, ref_cs, "ThinK 128k channel scores")
     chg = ch.cpu().numpy()
     check_kept(chg, csg, ref_cs, cfg.d_keep, 0)
     # the oracle continues with the GPU's channel set
@@ -239,13 +240,13 @@ def test_c5_think_snapkv_128k_full():
     torch.cuda.synchronize()
     ref_s, _ = O.snapkv(q64, k64, cfg.keep, chan_keep=chg)
     sg = s.cpu().numpy()
-    check_scores(sg, ref_s, "c5 scores")
+    check_scores(sg, ref_s, "ThinK 128k scores")
     check_kept(idx.cpu().numpy(), sg, ref_s, cfg.keep, cfg.n_tail)
     check_gather(ko, vo, p.k, p.v, idx.cpu().numpy(), chg)
 
 
-def test_c5_kept_keys_compressed_full():
-    """The c5 layer with the kept keys stored with their 64 channels (bench
+def test_think_128k_kept_keys_compressed_full():
+    """The ThinK + SnapKV 128k layer with the kept keys stored with their 64 channels (bench
     workload think_128k_kc): compressed K, V rows and pruned window queries,
     bit-exact against the oracle on the GPU's kept positions and channels."""
     cfg = configs.THINK_128K
@@ -271,8 +272,8 @@ def test_c5_kept_keys_compressed_full():
     assert torch.equal(full.view(torch.int16), k0.view(torch.int16))
 
 
-def test_c2_then_think_full():
-    """The c2 layer followed by ThinK on its 4096 kept keys (bench workload
+def test_snapkv_32k_then_think_full():
+    """The SnapKV 32k layer followed by ThinK on its 4096 kept keys (bench workload
     snapkv_think_32k); the oracle follows the GPU's kept positions."""
     cfg = configs.SNAPKV_32K
     say(cfg.name + " then think")
@@ -291,7 +292,7 @@ def test_c2_then_think_full():
     q64, k64 = p.q64(), p.k64()
     ref_s, _ = O.snapkv(q64, k64, cfg.keep)
     sg, ig = s.cpu().numpy(), idx.cpu().numpy()
-    check_scores(sg, ref_s, "c2 scores")
+    check_scores(sg, ref_s, "SnapKV 32k scores")
     check_kept(ig, sg, ref_s, cfg.keep, cfg.n_tail)
     ref_cs = O.channel_scores(q64, np.take_along_axis(k64, ig.astype(np.int64)[..., None], axis=2))
     csg, chg = cs.cpu().numpy(), ch.cpu().numpy()
