@@ -33,8 +33,9 @@ sys.path.insert(0, ROOT)
 METRIC = "KV tokens scored+pruned/s per layer (32k ctx, GQA 32/8) + % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK = 2.5e15  # dense bf16 MFMA, FLOP/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_window_scores_snapkv_32k.json")
+# sources whose code the recorded HBM counters of a kernel belong to
 SCORE_SOURCES = ["window_scores.hip", "kvc_device.h", "kvc_plan.h"]
+GATHER_SOURCES = ["gather.hip", "kvc_device.h", "kvc_launch.h"]
 WORKLOADS = ["snapkv_32k", "tova_tiny", "tova_batched", "scissor_decode", "think_128k", "think_128k_kc",
              "snapkv_think_32k", "scissor_queue_decode"]
 # (timed steps, warm-up steps).  The timed regions last 0.1-0.5 s: measured on
@@ -60,15 +61,33 @@ DEFAULT_STEPS = {"snapkv_32k": (250, 50), "tova_tiny": (2000, 200), "tova_batche
 DEFAULT_CU_BUDGET = {"snapkv_32k": 96, "snapkv_think_32k": 112, "think_128k": 128, "think_128k_kc": 128}
 
 
-def score_kernel_hash() -> str:
-    """Hash of the score kernels' code: the sources without their // comments and
-    blank lines, so that a comment edit does not void the recorded counters."""
+def kernel_hash(sources=SCORE_SOURCES) -> str:
+    """Hash of a kernel's code: its sources without their // comments and blank
+    lines, so that a comment edit does not void the recorded counters."""
     h = hashlib.sha256()
-    for f in SCORE_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "kv_cache_compression_window_amd", "csrc", f), encoding="utf-8") as fh:
             lines = (line.split("//", 1)[0].rstrip() for line in fh.read().splitlines())
             h.update("\n".join(line for line in lines if line).encode())
     return h.hexdigest()[:16]
+
+
+def score_kernel_hash() -> str:
+    return kernel_hash(SCORE_SOURCES)
+
+
+def recorded_traffic(name: str, sources, cu_budget: int = 0):
+    """HBM bytes per launch of the dominant kernel from profiles/traffic_<name>.json
+    (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated), or None when there is no such
+    record or it was taken on other kernel code or another compute-unit budget."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("kernel_hash") != kernel_hash(sources) or tr.get("cu_budget", 0) != cu_budget:
+        return None
+    return tr.get("bytes_per_launch")
 
 
 def parse():
@@ -287,12 +306,7 @@ def wl_snapkv_32k(c: Ctx, then_think: bool = False) -> dict:
                 "kind": "oracle", "sample": f"{n} KV heads (of {Hkv} per layer) of layer 0, S={S}, fp64 numpy "
                                             f"oracle (scores, top-k, gather), {el:.1f} s"}
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_hash") == score_kernel_hash() and tr.get("cu_budget", 0) == cub:
-            traffic = tr.get("bytes_per_launch")
+    traffic = recorded_traffic("window_scores_snapkv_32k" + ("_then_think" if then_think else ""), SCORE_SOURCES, cub)
     # the score call's contraction and exps: one contraction is 2*R*S*D flops per
     # (b, g), R = G*w rows; the two passes compute it twice, with one exp2 per
     # logit in each
@@ -354,9 +368,11 @@ def wl_tova(c: Ctx, cfg, gen, dtype, tdtype) -> dict:
     layer_bytes = k_bytes + q_bytes + 2 * s_bytes + 2 * i_bytes + g_bytes
     # the dominant kernel: the gather when it moves more bytes than the scoring reads
     if g_bytes > k_bytes:
-        kernel = ("kvc_gather_compact", [ly["kgather"] for ly in layers], g_bytes + i_bytes, None)
+        kernel = ("kvc_gather_compact", [ly["kgather"] for ly in layers], g_bytes + i_bytes,
+                  recorded_traffic("gather_compact_" + cfg.name, GATHER_SOURCES))
     else:
-        kernel = ("kvc_window_scores", [ly["kscore"] for ly in layers], k_bytes + q_bytes + s_bytes, None)
+        kernel = ("kvc_window_scores", [ly["kscore"] for ly in layers], k_bytes + q_bytes + s_bytes,
+                  recorded_traffic("window_scores_" + cfg.name, SCORE_SOURCES, cub))
 
     def cpu(budget):
         from oracle import kvc_oracle as O
@@ -463,7 +479,8 @@ def wl_think_128k(c: Ctx, compress: bool = False) -> dict:
     return dict(step=step, units_per_step=B * S * nl, layers=nl, layer_bytes=layer_bytes,
                 check_outputs=check_outputs,
                 kernel=("kvc_window_scores with 64 of 128 key channels (pass 1 + pass 2)",
-                        [ly["kcall"] for ly in layers], k_bytes + q_bytes + s_bytes, None),
+                        [ly["kcall"] for ly in layers], k_bytes + q_bytes + s_bytes,
+                        recorded_traffic("window_scores_think_128k", SCORE_SOURCES, cub)),
                 kernel_alone=[ly["kcall1"] for ly in layers] if cub != 0 else None,
                 cpu=cpu, metric=f"KV tokens scored+pruned/s per layer ({cfg.name}{'_kc' if compress else ''})",
                 unit="tokens/s", dtype="bf16", workload=cfg.name + ("_kc" if compress else ""),
@@ -567,7 +584,8 @@ def wl_scissor_decode(c: Ctx) -> dict:
 
     return dict(step=step, reset=reset, units_per_step=units * nl / nsteps, layers=nl, layer_bytes=step_bytes,
                 kernel=("kvc_window_scores (w=1, stored logits)", [ly["kcall"] for ly in layers],
-                        k_bytes + B * H * D * 2 + B * Hkv * C * 4, None),
+                        k_bytes + B * H * D * 2 + B * Hkv * C * 4,
+                        recorded_traffic("window_scores_scissorhands_decode", SCORE_SOURCES, cub)),
                 final_state=final_state, graph_block=cfg.evict_every,
                 cpu=cpu, metric=f"KV token-steps scored+recorded/s per layer ({cfg.name})", unit="token-steps/s",
                 dtype="bf16", workload=cfg.name,
@@ -694,7 +712,8 @@ def wl_scissor_queue_decode(c: Ctx) -> dict:
 
     return dict(step=step, reset=reset, units_per_step=units * nl / nsteps, layers=nl, layer_bytes=step_bytes,
                 kernel=("kvc_window_scores (w=1, stored logits)", [ly["kcall"] for ly in layers],
-                        k_bytes + B * H * D * 2 + B * Hkv * C * 4, None),
+                        k_bytes + B * H * D * 2 + B * Hkv * C * 4,
+                        recorded_traffic("window_scores_scissorhands_decode", SCORE_SOURCES, cub)),
                 final_state=final_state, graph_block=m,
                 cpu=cpu, metric=f"KV token-steps scored+recorded/s per layer ({cfg.name})", unit="token-steps/s",
                 dtype="bf16", workload=cfg.name,
